@@ -1,0 +1,242 @@
+"""Decode-step benchmark of query-aware block-sparse attention on one MI355X.
+
+A step is one decode layer-step of the whole path over one batch: rebuild
+the newest block's summary of every sequence, score every block and select
+the top-k, attend over the selected blocks (split partials + merge).  The
+default workload is 8 sequences x 32 query / 4 KV heads, head dim 128, 32768
+tokens of bf16 K/V in 64-token pages, k = 128 of 512 blocks, over 32 layer
+instances with their own buffers (step i uses instance i mod 32, so no step
+re-reads data an earlier step left in the 256 MB last-level cache).  Every
+layer-step is captured once into a HIP graph and the timed loop replays them.
+
+Prints one JSON line.  Metric: decode query-tokens/s/layer = B / t(step),
+with the achieved HBM GB/s of the step and a roofline entry for the dominant
+kernel (the sparse attention) timed with HIP events on its own stream, plus
+the CPU oracle's rate on a bounded sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu] [--cpu-steps N]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode query-tokens/s/layer + achieved HBM GB/s (% peak), top-25% @32K ctx"
+PEAK_HBM_GBPS = 8000.0
+
+
+def algorithmic_bytes(w, summ_elem: int, kv_elem: int, q_elem: int) -> dict:
+    """Bytes one layer-step must move: the summaries of every block, the
+    selected K/V tiles (and fp8 scales), q, the fp32 output, and the newest
+    block's K tile read plus its summary written."""
+    units = w.B * w.Hkv
+    summ = units * w.nb * 2 * w.D * summ_elem
+    tile = w.S * w.D * kv_elem
+    kv = units * w.k * 2 * tile
+    scales = units * w.k * 2 * w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0
+    q = w.B * w.Hq * w.D * q_elem
+    out = w.B * w.Hq * w.D * 4
+    append = units * (tile + (w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0) + 2 * w.D * summ_elem)
+    return {"summaries": summ, "kv": kv, "scales": scales, "q": q, "out": out, "append": append,
+            "attention": kv + scales + q + out,
+            "step": summ + kv + scales + q + out + append}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=640)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-steps", type=int, default=2, help="layer-steps in the CPU oracle sample")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              "multi-GPU path: (sequence, KV head) units are independent, so several GPUs would "
+              "each run this same step on their share of the sequences.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from query_aware_sparse_kvs_amd import kvs, synth
+    from query_aware_sparse_kvs_amd.step import SparseDecodeStep
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    if w.hot_slots:
+        raise SystemExit("the hot-buffer workload is measured by bench_hot in tests; pick another")
+    code = kvs.DTYPE_CODE
+    L = kvs.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code[w.q_dtype], code[w.kv_dtype],
+                   w.quant_group)
+    n_layers = w.layers
+    print(f"[bench] workload {w.name}: building {n_layers} layer instance(s)", file=sys.stderr, flush=True)
+
+    layers = []
+    steps = []
+    for li in range(n_layers):
+        inp = synth.make_inputs(w, dev, layer=li)
+        st = SparseDecodeStep(L, w.k, dev)
+        summ = st.new_summaries(dev)
+        st.prefill_summaries(inp["k_pool"], inp["k_scales"], inp["block_table"], inp["seq_lens"], summ)
+        newest = ((inp["seq_lens"] + w.S - 1) // w.S - 1).to(torch.int32)
+        layers.append(dict(inp=inp, summ=summ, newest=newest))
+        steps.append(st)
+    torch.cuda.synchronize()
+    assert kvs.kvs_device_errors() == 0
+
+    def run_step(i):
+        d = layers[i]
+        inp = d["inp"]
+        steps[i].run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"],
+                     inp["block_table"], inp["seq_lens"], d["summ"], d["newest"])
+
+    def run_attn(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, inp["q"], inp["k_pool"], inp["v_pool"],
+                                   inp["k_scales"], inp["v_scales"], inp["block_table"], inp["seq_lens"],
+                                   st.sel, w.k, st.sm_scale, st.out, st.attn_ws)
+
+    def capture(fn):
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(n_layers):
+                fn(i)  # eager warm-up (also initialises the library's per-device state)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(n_layers):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn(i)
+            graphs.append(g)
+        return graphs
+
+    step_graphs = capture(run_step)
+    attn_graphs = capture(run_attn)
+    torch.cuda.synchronize()
+
+    def timed(graphs, K, W):
+        for i in range(W):
+            graphs[i % n_layers].replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for i in range(K):
+            graphs[i % n_layers].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) / 1e3, wall
+
+    print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
+    t_attn, _ = timed(attn_graphs, args.steps, args.warmup)
+    torch.cuda.synchronize()
+    assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
+
+    summ_elem = 2 if w.kv_dtype == "bf16" else 4
+    kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    q_elem = 4 if w.q_dtype == "f32" else 2
+    by = algorithmic_bytes(w, summ_elem, kv_elem, q_elem)
+    sec_per_step = t_step / args.steps
+    attn_sec = t_attn / args.steps
+    value = w.B / sec_per_step
+    step_gbps = by["step"] / sec_per_step / 1e9
+    attn_gbps = by["attention"] / attn_sec / 1e9
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, layers, args.cpu_steps)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec_per_step * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                   "head_dim": w.D, "context": w.L, "block": w.S, "top_k_blocks": w.k,
+                   "kv_storage": w.kv_dtype, "q_storage": w.q_dtype, "layer_instances": n_layers,
+                   "graph_replay": True},
+        "step_bytes": by["step"],
+        "step_GBps": round(step_gbps, 1),
+        "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": {"bound": "hbm", "kernel": "sparse decode attention (split + merge)",
+                     "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": by["attention"], "us_per_launch": round(attn_sec * 1e6, 3)},
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": round(wall_step, 4),
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(w, layers, n_steps):
+    """The oracle (single thread, fp64, as written) on `n_steps` whole
+    layer-steps of the same workload: newest-block summaries, bounds,
+    selection, sparse attention."""
+    import numpy as np
+    import torch
+
+    import oracle
+    code = {"f32": oracle.KV_F32, "bf16": oracle.KV_BF16, "e4m3": oracle.KV_E4M3}[w.kv_dtype]
+    OL = oracle.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code, w.quant_group)
+    n_steps = max(1, min(n_steps, len(layers)))
+    host = []
+    for li in range(n_steps):
+        inp = layers[li]["inp"]
+        h = {}
+        for n in ("k_pool", "v_pool"):
+            t = inp[n].cpu()
+            h[n] = t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        for n in ("k_scales", "v_scales"):
+            h[n] = None if inp[n] is None else inp[n].cpu().numpy()
+        h["table"] = inp["block_table"].cpu().numpy()
+        h["lens"] = inp["seq_lens"].cpu().numpy()
+        h["q"] = inp["q"].double().cpu().numpy()
+        h["newest"] = layers[li]["newest"].cpu().numpy()
+        # prefill-time summaries of every block, built by the oracle (untimed)
+        h["summ"] = oracle.summaries(OL, h["k_pool"], h["k_scales"], h["table"], h["lens"])
+        host.append(h)
+    print(f"[bench] CPU oracle on {n_steps} layer-step(s)", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for h in host:
+        oracle.summaries(OL, h["k_pool"], h["k_scales"], h["table"], h["lens"], h["newest"], 1, out=h["summ"])
+        W = oracle.bounds(OL, h["q"], h["summ"], h["lens"])
+        sel = oracle.select(OL, W, h["lens"], w.k)
+        oracle.sparse_attn(OL, h["q"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["table"],
+                           h["lens"], sel, 1.0 / math.sqrt(w.D))
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B * n_steps / dt, 3), "unit": "query-tokens/s/layer", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_steps} full layer-step(s) of {w.name} (all {w.B} sequences, {w.B * w.Hkv} "
+                      f"units), single-threaded fp64, {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

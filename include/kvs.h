@@ -1,0 +1,289 @@
+/*
+ * kvs.h -- C ABI of libkvs: query-aware block-sparse decode attention over a
+ * paged KV cache, with a hot-buffer / host-tier variant, for AMD MI355X
+ * (gfx950).
+ *
+ * The method (page "KV 稀疏化", §5 "Quest"): at every decode step, split the
+ * KV of a sequence into blocks, keep a compact summary of each block (here
+ * the channel-wise min and max of K), use the query and the summaries to
+ * pick the top-k blocks, and run exact attention on those blocks only, so a
+ * step reads k blocks of K/V instead of all of them.  The attention sink
+ * (same page, §2, StreamingLLM) and the newest block (recent window; page
+ * "SparDA：把KV選擇提前一層…", §4.2) are always kept.  The hot-buffer variant
+ * follows the same wiki page, §7 "HiSparse": a hot buffer in HBM holds the
+ * blocks the top-k set is likely to touch, inactive KV lives in host memory,
+ * and a swap-in step finds misses, updates the page table and copies the
+ * missed KV in before attention.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  B  = layout.num_seqs       Hq = layout.num_q_heads   Hkv = num_kv_heads
+ *  G  = Hq / Hkv (query heads per KV head; query head h reads KV head h / G)
+ *  D  = head_dim  (64 or 128)                S = block_size (16, 32 or 64)
+ *  MB = max_blocks (entries per block-table row)   P = num_pages
+ *  nb(b) = ceil(seq_lens[b] / S): blocks of sequence b, the last one may be
+ *          partial; only token positions t < seq_lens[b] are ever used.
+ *
+ *  All tensors are dense, row-major (C order), in DEVICE memory unless the
+ *  argument says "host"; the library never allocates, frees or keeps any of
+ *  them.  Workspaces are caller-owned device buffers of at least the size the
+ *  matching *_workspace_size call returns; they need no initial contents.
+ *
+ *  K/V pool (paged):  [P][Hkv][S][D] of kv_dtype; page p holds S consecutive
+ *                     tokens of one sequence for every KV head.
+ *  fp8 scales:        [P][Hkv][S][D/quant_group] fp32, one per token and
+ *                     group of quant_group adjacent channels ("分块稀疏注意力
+ *                     与KV Cache量化…", §2.4; symmetric, no zero point).  The
+ *                     value of an fp8 element is fp32(decode(code) * scale),
+ *                     code in OCP E4M3FN.
+ *  block_table:       [B][MB] int32 page ids (the paged layout's "block
+ *                     table", page "SparDA…", §4.3).
+ *  seq_lens:          [B] int32, tokens per sequence INCLUDING the token being
+ *                     decoded (its K/V already written and its block's summary
+ *                     rebuilt).  Must lie in [0, MB*S].
+ *  sel:               [B][Hkv][k] int32 block ids per (sequence, KV head):
+ *                     strictly ascending valid ids, then -1 padding ("SparDA…",
+ *                     §6.3: pad ragged masks to one length with invalid values).
+ *
+ *  Every call only enqueues work on `stream` (a hipStream_t, NULL = the
+ *  default stream) and never waits for the device.  Host-visible argument
+ *  errors return a non-zero kvs_status before anything is enqueued, with a
+ *  message in kvs_last_error().  Data that only the device sees (seq_lens,
+ *  table entries, sel entries) is range-checked by the kernels: an offending
+ *  item is skipped (a sequence length is clamped to [0, MB*S]) and a bit is
+ *  set in the device error word read by kvs_device_errors(); no kernel ever
+ *  reads or writes out of bounds.  No call falls back to another code path:
+ *  an unsupported shape or dtype returns KVS_ERR_UNSUPPORTED.
+ *
+ *  Calls on one stream run in order; calls that overlap on different streams
+ *  must not share output or workspace buffers.
+ */
+#ifndef KVS_H
+#define KVS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVS_ABI_VERSION 1
+
+typedef enum kvs_status {
+  KVS_OK = 0,
+  KVS_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent layout */
+  KVS_ERR_UNSUPPORTED = 2,   /* valid but not implemented (dtype, D, S, G)   */
+  KVS_ERR_CAPACITY = 3,      /* more blocks requested than hot slots         */
+  KVS_ERR_HIP = 4            /* the HIP runtime reported an error            */
+} kvs_status;
+
+typedef enum kvs_dtype {
+  KVS_F32 = 0,
+  KVS_BF16 = 1,
+  KVS_FP8_E4M3 = 2           /* OCP E4M3FN, 1 byte per element */
+} kvs_dtype;
+
+typedef enum kvs_table_kind {
+  /* table = block_table [B][MB] of page ids in [0, P); pools [P][Hkv][S][D] */
+  KVS_TABLE_PAGED = 0,
+  /* table = hot page table [B][Hkv][MB] of global hot-slot ids in [0, P)
+   * (-1 = not resident); pools [P][S][D], one KV head per slot; scales
+   * [P][S][D/quant_group]. P is then the total number of hot slots. */
+  KVS_TABLE_HOT = 1
+} kvs_table_kind;
+
+typedef struct kvs_layout {
+  int32_t num_seqs;      /* B,   >= 0                                   */
+  int32_t num_q_heads;   /* Hq,  multiple of num_kv_heads, G <= 16       */
+  int32_t num_kv_heads;  /* Hkv, >= 1                                   */
+  int32_t head_dim;      /* D:   64 or 128                              */
+  int32_t block_size;    /* S:   16, 32 or 64 tokens per page and block */
+  int32_t max_blocks;    /* MB:  block-table row length, 1..8192        */
+  int32_t num_pages;     /* P:   pages (or hot slots) in the pool, >= 1 */
+  int32_t q_dtype;       /* kvs_dtype of q: KVS_F32 or KVS_BF16          */
+  int32_t kv_dtype;      /* kvs_dtype of the K/V pools                  */
+  int32_t quant_group;   /* channels per fp8 scale (16, 32, 64 or 128,
+                            dividing D); 0 unless kv_dtype is fp8       */
+} kvs_layout;
+
+/* Supported dtype pairs (q, kv): (F32, F32), (BF16, BF16), (BF16, FP8_E4M3). */
+
+/* ------------------------------------------------------------------------
+ * kvs_build_summaries -- per-block channel-wise min/max of K
+ *
+ * Page "KV 稀疏化", §5 "Quest" (first step: a compact summary per block);
+ * run at prefill for every block and at each decode append for the block
+ * that received the new token.  For b in [0,B), every KV head g and every
+ * block j in [first, first + num_rebuild) ∩ [0, nb(b)), where first =
+ * first_block[b] (0 when first_block is NULL):
+ *     summaries[b][g][j][0][c] = min_t K[b,g,t,c],
+ *     summaries[b][g][j][1][c] = max_t K[b,g,t,c],
+ * over the valid tokens t in [j*S, min((j+1)*S, seq_lens[b])), K read through
+ * block_table (fp8 elements dequantised first).  Other entries are left
+ * untouched.
+ *
+ *  k_pool       [P][Hkv][S][D] kv_dtype
+ *  k_scales     fp8 only: [P][Hkv][S][D/quant_group] fp32, else NULL
+ *  block_table  [B][MB] int32;   seq_lens [B] int32
+ *  first_block  [B] int32 device array or NULL
+ *  num_rebuild  blocks rebuilt per sequence, 0..MB (MB with a NULL
+ *               first_block = full prefill build; 1 with first_block[b] =
+ *               nb(b)-1 = decode append)
+ *  summaries    [B][Hkv][MB][2][D]: bf16 when kv_dtype is bf16 (min/max of
+ *               bf16 values is exact in bf16), fp32 otherwise.
+ * Errors: INVALID_ARG (null pointer, bad layout, num_rebuild out of range),
+ * UNSUPPORTED (dtype/D/S), HIP.  Device flags: KVS_DEVERR_SEQLEN,
+ * KVS_DEVERR_TABLE.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_build_summaries(const kvs_layout* layout, const void* k_pool,
+                               const float* k_scales, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* first_block,
+                               int32_t num_rebuild, void* summaries, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_select_topk -- query-aware block scores and top-k selection
+ *
+ * Page "KV 稀疏化", §5 "Quest" (second step: coarse-filter the blocks with the
+ * query and the summaries, keep the top-k); §2 and "SparDA…" §4.2 (sink and
+ * recent blocks always kept).  The pages do not print the score; the one used
+ * is the box upper bound of q.K over the block:
+ *     U[b,h,j] = sum_{c=0}^{D-1} max(q[b,h,c]*mn[c], q[b,h,c]*mx[c])
+ * accumulated in fp64 in ascending c (every product is exact in fp64, so the
+ * result is the correctly ordered fp64 sum), and per KV head the group score
+ *     W[b,g,j] = max over the G query heads h of group g of U[b,h,j].
+ * Selection per (b,g): if nb(b) <= k every block; otherwise block 0, block
+ * nb(b)-1 and the k-2 best of blocks 1..nb(b)-2 under (W descending, block id
+ * ascending).  Written to sel ascending, padded with -1.
+ *
+ *  q            [B][Hq][D] q_dtype
+ *  summaries    as written by kvs_build_summaries (same layout)
+ *  seq_lens     [B] int32
+ *  k            2 <= k <= MB
+ *  sel          [B][Hkv][k] int32 output
+ *  bounds_out   optional [B][Hkv][MB] fp64 output: W, -inf for j >= nb(b)
+ *  workspace    >= kvs_select_workspace_size(layout, k) bytes
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Device flags: KVS_DEVERR_SEQLEN.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_select_topk(const kvs_layout* layout, const void* q, const void* summaries,
+                           const int32_t* seq_lens, int32_t k, int32_t* sel,
+                           double* bounds_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_sparse_decode_attn -- attention over the selected blocks only
+ *
+ * Page "KV 稀疏化", §5 "Quest" (third step: full attention on the selected
+ * blocks); computed tile by tile with a running max and normaliser that are
+ * merged across tiles ("分块稀疏注意力与KV Cache量化…", §2.2), fp8 K/V
+ * dequantised inside the read (same page, §1.3).  For every query head h of
+ * KV head g = h / G, over the token set T = ∪_{j in sel[b][g]} {t : j*S <= t <
+ * min((j+1)S, seq_lens[b])}:
+ *     s_t = sm_scale * q_h . K_t,  out[b][h] = sum_t softmax(s)_t V_t
+ * in fp32 arithmetic; an empty T gives a zero row.
+ *
+ *  table_kind   KVS_TABLE_PAGED or KVS_TABLE_HOT (see kvs_table_kind)
+ *  q            [B][Hq][D] q_dtype
+ *  k_pool/v_pool, k_scales/v_scales   per table_kind
+ *  table        [B][MB] (paged) or [B][Hkv][MB] (hot) int32
+ *  seq_lens     [B] int32
+ *  sel          [B][Hkv][k] int32, k >= 1
+ *  sm_scale     softmax scale (1/sqrt(D) for standard attention)
+ *  out          [B][Hq][D] fp32 output
+ *  workspace    >= kvs_attn_workspace_size(layout, k) bytes
+ * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Device flags: KVS_DEVERR_SEQLEN,
+ * KVS_DEVERR_TABLE (entry out of range or -1: block skipped),
+ * KVS_DEVERR_SEL (id >= nb(b), < -1, not ascending or after padding).
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_sparse_decode_attn(const kvs_layout* layout, int32_t table_kind,
+                                  const void* q, const void* k_pool, const void* v_pool,
+                                  const float* k_scales, const float* v_scales,
+                                  const int32_t* table, const int32_t* seq_lens,
+                                  const int32_t* sel, int32_t k, float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_hot_lookup_swapin -- hot-buffer page-table step and swap-in copy
+ *
+ * Page "KV 稀疏化", §7 "HiSparse" table: the hot device buffer keeps the KV
+ * the current top-k set is likely to touch, inactive KV sits in host memory,
+ * and the swap-in step finds the misses on the decode path, updates the page
+ * table and copies the KV back; what is resident follows the sparse access
+ * set (the selection), not idleness or LRU alone.  Per unit u = b*Hkv + g,
+ * with ns = num_slots slots of global ids u*ns + s:
+ *   1. every selected block j with page_table[u][j] >= 0 is a hit: its slot's
+ *      stamp becomes `step`;
+ *   2. the misses are the other selected blocks, ascending -> miss_list[u],
+ *      padded with -1, count -> miss_count[u];
+ *   3. victims are the slots whose owner is not selected (free slots have
+ *      owner -1 and stamp -1), ordered by (stamp ascending, slot ascending);
+ *      the r-th miss takes the r-th victim: the old owner's page-table entry
+ *      becomes -1, the miss's entry the slot id, owner = miss, stamp = step;
+ *   4. each miss's K and V block (and fp8 scales) is copied from the host
+ *      tier into its slot.
+ * Blocks in the host tier are immutable once written, so eviction needs no
+ * write-back.
+ *
+ *  layout       num_seqs, num_kv_heads, head_dim, block_size, max_blocks
+ *               (page-table row length), kv_dtype, quant_group are used
+ *  sel          [B][Hkv][k] int32 (ids < MB), 1 <= k <= num_slots
+ *  num_slots    hot slots per unit, 1..4096
+ *  step         decode step number, >= 0, larger than any previous step
+ *  page_table   [B][Hkv][MB] int32 in/out (global slot id or -1)
+ *  slot_owner   [B][Hkv][num_slots] int32 in/out (block id or -1)
+ *  slot_stamp   [B][Hkv][num_slots] int64 in/out (-1 when free)
+ *  host_k/host_v  HOST [B][Hkv][MB][S][D] kv_dtype, allocated with
+ *               hipHostMalloc (pinned and mapped; the kernels read it over
+ *               the host link)
+ *  host_k_scales/host_v_scales  HOST [B][Hkv][MB][S][D/qg] fp32 (fp8 only)
+ *  hot_k/hot_v  [B*Hkv*num_slots][S][D] kv_dtype (the KVS_TABLE_HOT pools)
+ *  hot_k_scales/hot_v_scales  [B*Hkv*num_slots][S][D/qg] fp32 (fp8 only)
+ *  miss_list    [B][Hkv][k] int32 output;  miss_count [B][Hkv] int32 output
+ * Initial state of a fresh buffer: page_table, slot_owner, slot_stamp all -1.
+ * Errors: INVALID_ARG (also when a host pool is not pinned), CAPACITY
+ * (k > num_slots), UNSUPPORTED, HIP.  Device flags: KVS_DEVERR_SEL,
+ * KVS_DEVERR_TABLE (inconsistent page table / owner state: unit skipped).
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, int32_t k,
+                                 int32_t num_slots, int64_t step, int32_t* page_table,
+                                 int32_t* slot_owner, int64_t* slot_stamp, const void* host_k,
+                                 const void* host_v, const float* host_k_scales,
+                                 const float* host_v_scales, void* hot_k, void* hot_v,
+                                 float* hot_k_scales, float* hot_v_scales, int32_t* miss_list,
+                                 int32_t* miss_count, void* stream);
+
+/* Workspace bytes needed by kvs_select_topk / kvs_sparse_decode_attn for this
+ * layout and k; 0 when the layout or k is invalid. */
+size_t kvs_select_workspace_size(const kvs_layout* layout, int32_t k);
+size_t kvs_attn_workspace_size(const kvs_layout* layout, int32_t k);
+
+/* Number of key splits the attention kernel uses for this layout and k
+ * (each (sequence, KV head) unit's k blocks are spread over that many
+ * workgroups whose partial results are merged); 0 when invalid. */
+int32_t kvs_attn_num_splits(const kvs_layout* layout, int32_t k);
+
+/* Device error word bits (see each call). */
+#define KVS_DEVERR_SEQLEN 0x1u  /* a seq_lens entry outside [0, MB*S]        */
+#define KVS_DEVERR_TABLE  0x2u  /* a table entry out of range or inconsistent */
+#define KVS_DEVERR_SEL    0x4u  /* a selection entry out of range / order     */
+
+/* Reads the current device's error word (OR of KVS_DEVERR_* bits raised by
+ * kernels since the last clear) into *flags after waiting for `stream`; when
+ * clear != 0 the word is reset to 0.  Errors: INVALID_ARG, HIP. */
+kvs_status kvs_device_errors(uint32_t* flags, int32_t clear, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* kvs_status_string(kvs_status status);
+
+/* Detail message of the last error returned on the calling thread ("" if
+ * none); valid until the next call on that thread. */
+const char* kvs_last_error(void);
+
+/* KVS_ABI_VERSION of the library. */
+int32_t kvs_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVS_H */

@@ -1,0 +1,383 @@
+// kvs_api.hip -- the extern "C" entry points declared in include/kvs.h:
+// host-side argument validation, dtype/shape dispatch, workspace sizing,
+// status strings and the device error word.  No allocation happens here;
+// every buffer belongs to the caller.
+#include <mutex>
+#include <string>
+
+#include "../../include/kvs.h"
+#include "kvs_internal.h"
+
+// OR of KVS_DEVERR_* bits raised by kernels on this device.
+__device__ unsigned int kvs_device_error_word = 0u;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kvs_status fail(kvs_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+kvs_status ok() {
+  g_last_error.clear();
+  return KVS_OK;
+}
+
+// device address of kvs_device_error_word, looked up once per device
+constexpr int kMaxDevices = 64;
+unsigned int* g_err_word[kMaxDevices] = {};
+std::mutex g_err_mu;
+
+kvs_status error_word(unsigned int** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_err_mu);
+  if (!g_err_word[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(kvs_device_error_word));
+    if (e != hipSuccess || !p)
+      return fail(KVS_ERR_HIP, std::string("hipGetSymbolAddress: ") + hipGetErrorString(e));
+    g_err_word[dev] = static_cast<unsigned int*>(p);
+  }
+  *out = g_err_word[dev];
+  return KVS_OK;
+}
+
+kvs_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(KVS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int kind_of(int32_t dt) {
+  switch (dt) {
+    case KVS_F32: return kvs::K_F32;
+    case KVS_BF16: return kvs::K_BF16;
+    default: return kvs::K_FP8;
+  }
+}
+
+size_t elem_size(int32_t dt) { return dt == KVS_F32 ? 4 : (dt == KVS_BF16 ? 2 : 1); }
+
+// Checks the layout fields every call needs.  `need_q` adds the query-side
+// checks (heads, q dtype pairing).
+kvs_status check_layout(const kvs_layout* L, bool need_q) {
+  if (!L) return fail(KVS_ERR_INVALID_ARG, "layout is NULL");
+  if (L->num_seqs < 0) return fail(KVS_ERR_INVALID_ARG, "num_seqs < 0");
+  if (L->num_kv_heads < 1) return fail(KVS_ERR_INVALID_ARG, "num_kv_heads < 1");
+  if (L->max_blocks < 1 || L->max_blocks > 8192)
+    return fail(L->max_blocks < 1 ? KVS_ERR_INVALID_ARG : KVS_ERR_UNSUPPORTED,
+                "max_blocks must be in [1, 8192]");
+  if (L->num_pages < 1) return fail(KVS_ERR_INVALID_ARG, "num_pages < 1");
+  if (L->head_dim != 64 && L->head_dim != 128)
+    return fail(L->head_dim <= 0 ? KVS_ERR_INVALID_ARG : KVS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (L->block_size != 16 && L->block_size != 32 && L->block_size != 64)
+    return fail(L->block_size <= 0 ? KVS_ERR_INVALID_ARG : KVS_ERR_UNSUPPORTED,
+                "block_size must be 16, 32 or 64");
+  if (L->kv_dtype < KVS_F32 || L->kv_dtype > KVS_FP8_E4M3)
+    return fail(KVS_ERR_INVALID_ARG, "unknown kv_dtype");
+  if (L->kv_dtype == KVS_FP8_E4M3) {
+    const int qg = L->quant_group;
+    if (qg != 16 && qg != 32 && qg != 64 && qg != 128)
+      return fail(KVS_ERR_UNSUPPORTED, "fp8 quant_group must be 16, 32, 64 or 128");
+    if (L->head_dim % qg != 0) return fail(KVS_ERR_INVALID_ARG, "quant_group must divide head_dim");
+  } else if (L->quant_group != 0) {
+    return fail(KVS_ERR_INVALID_ARG, "quant_group must be 0 unless kv_dtype is fp8");
+  }
+  if ((long long)L->max_blocks * L->block_size > 0x7FFFFFFFll)
+    return fail(KVS_ERR_INVALID_ARG, "max_blocks * block_size overflows int32");
+  if (need_q) {
+    if (L->num_q_heads < 1 || L->num_q_heads % L->num_kv_heads != 0)
+      return fail(KVS_ERR_INVALID_ARG, "num_q_heads must be a positive multiple of num_kv_heads");
+    const int G = L->num_q_heads / L->num_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+      return fail(KVS_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4, 8 or 16");
+    if (L->q_dtype != KVS_F32 && L->q_dtype != KVS_BF16) return fail(KVS_ERR_UNSUPPORTED, "q_dtype must be fp32 or bf16");
+    const bool pair_ok = (L->q_dtype == KVS_F32 && L->kv_dtype == KVS_F32) ||
+                         (L->q_dtype == KVS_BF16 && L->kv_dtype == KVS_BF16) ||
+                         (L->q_dtype == KVS_BF16 && L->kv_dtype == KVS_FP8_E4M3);
+    if (!pair_ok) return fail(KVS_ERR_UNSUPPORTED, "unsupported (q_dtype, kv_dtype) pair");
+  }
+  if ((long long)L->num_seqs * L->num_kv_heads > 0x7FFFFFFFll)
+    return fail(KVS_ERR_INVALID_ARG, "num_seqs * num_kv_heads overflows int32");
+  return KVS_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t select_ws(const kvs_layout* L) {
+  return round_up(sizeof(double) * (size_t)L->num_seqs * L->num_kv_heads * L->max_blocks, 256);
+}
+
+int attn_splits(const kvs_layout* L, int32_t k) {
+  return kvs::attn_num_splits(L->num_seqs * L->num_kv_heads, k);
+}
+
+size_t attn_ws(const kvs_layout* L, int32_t k) {
+  const size_t units = (size_t)L->num_seqs * L->num_q_heads * attn_splits(L, k);
+  return round_up(sizeof(float) * units * 2, 256) + round_up(sizeof(float) * units * L->head_dim, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvs_abi_version(void) { return KVS_ABI_VERSION; }
+
+const char* kvs_status_string(kvs_status st) {
+  switch (st) {
+    case KVS_OK: return "KVS_OK";
+    case KVS_ERR_INVALID_ARG: return "KVS_ERR_INVALID_ARG: invalid argument";
+    case KVS_ERR_UNSUPPORTED: return "KVS_ERR_UNSUPPORTED: shape or dtype not supported";
+    case KVS_ERR_CAPACITY: return "KVS_ERR_CAPACITY: more blocks than hot slots";
+    case KVS_ERR_HIP: return "KVS_ERR_HIP: HIP runtime error";
+  }
+  return "unknown kvs_status";
+}
+
+const char* kvs_last_error(void) { return g_last_error.c_str(); }
+
+size_t kvs_select_workspace_size(const kvs_layout* L, int32_t k) {
+  if (check_layout(L, true) != KVS_OK || k < 2 || k > L->max_blocks) return 0;
+  return select_ws(L);
+}
+
+size_t kvs_attn_workspace_size(const kvs_layout* L, int32_t k) {
+  if (check_layout(L, true) != KVS_OK || k < 1 || k > L->max_blocks) return 0;
+  return attn_ws(L, k);
+}
+
+int32_t kvs_attn_num_splits(const kvs_layout* L, int32_t k) {
+  if (check_layout(L, true) != KVS_OK || k < 1 || k > L->max_blocks) return 0;
+  return attn_splits(L, k);
+}
+
+kvs_status kvs_device_errors(uint32_t* flags, int32_t clear, void* stream) {
+  if (!flags) return fail(KVS_ERR_INVALID_ARG, "flags is NULL");
+  unsigned int* w = nullptr;
+  kvs_status st = error_word(&w);
+  if (st != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned int host = 0;
+  hipError_t e = hipMemcpyAsync(&host, w, sizeof host, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e, "reading the device error word");
+  *flags = host;
+  if (clear) {
+    const unsigned int zero = 0;
+    e = hipMemcpyAsync(w, &zero, sizeof zero, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e, "clearing the device error word");
+  }
+  return ok();
+}
+
+kvs_status kvs_build_summaries(const kvs_layout* L, const void* k_pool, const float* k_scales,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const int32_t* first_block, int32_t num_rebuild, void* summaries,
+                               void* stream) {
+  kvs_status st = check_layout(L, false);
+  if (st != KVS_OK) return st;
+  if (!k_pool || !block_table || !seq_lens || !summaries)
+    return fail(KVS_ERR_INVALID_ARG, "k_pool, block_table, seq_lens and summaries must be non-NULL");
+  if (L->kv_dtype == KVS_FP8_E4M3 && !k_scales) return fail(KVS_ERR_INVALID_ARG, "fp8 K needs k_scales");
+  if (num_rebuild < 0 || num_rebuild > L->max_blocks)
+    return fail(KVS_ERR_INVALID_ARG, "num_rebuild must be in [0, max_blocks]");
+  if (!aligned(k_pool, 16) || !aligned(summaries, 16))
+    return fail(KVS_ERR_INVALID_ARG, "k_pool and summaries must be 16-byte aligned");
+  unsigned int* err = nullptr;
+  if ((st = error_word(&err)) != KVS_OK) return st;
+  kvs::SummArgs a{};
+  a.k_pool = k_pool;
+  a.k_scales = k_scales;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.first_block = first_block;
+  a.out = summaries;
+  a.err = err;
+  a.B = L->num_seqs;
+  a.Hkv = L->num_kv_heads;
+  a.D = L->head_dim;
+  a.S = L->block_size;
+  a.MB = L->max_blocks;
+  a.P = L->num_pages;
+  a.qg = L->quant_group;
+  a.num_rebuild = num_rebuild;
+  return hip_status(kvs::launch_summaries(a, kind_of(L->kv_dtype), static_cast<hipStream_t>(stream)),
+                    "summaries launch");
+}
+
+kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summaries,
+                           const int32_t* seq_lens, int32_t k, int32_t* sel, double* bounds_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  kvs_status st = check_layout(L, true);
+  if (st != KVS_OK) return st;
+  if (!q || !summaries || !seq_lens || !sel)
+    return fail(KVS_ERR_INVALID_ARG, "q, summaries, seq_lens and sel must be non-NULL");
+  if (k < 2 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [2, max_blocks]");
+  if (!workspace || workspace_bytes < select_ws(L))
+    return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_select_workspace_size()");
+  if (!aligned(summaries, 16) || !aligned(workspace, 16) || (bounds_out && !aligned(bounds_out, 8)))
+    return fail(KVS_ERR_INVALID_ARG, "summaries/workspace must be 16-byte aligned, bounds_out 8-byte");
+  unsigned int* err = nullptr;
+  if ((st = error_word(&err)) != KVS_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  kvs::BoundArgs ba{};
+  ba.q = q;
+  ba.summ = summaries;
+  ba.seq_lens = seq_lens;
+  ba.W = static_cast<double*>(workspace);
+  ba.bounds_out = bounds_out;
+  ba.err = err;
+  ba.B = L->num_seqs;
+  ba.Hq = L->num_q_heads;
+  ba.Hkv = L->num_kv_heads;
+  ba.D = L->head_dim;
+  ba.S = L->block_size;
+  ba.MB = L->max_blocks;
+  const int summ_kind = L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32;
+  hipError_t e = kvs::launch_bounds(ba, kind_of(L->q_dtype), summ_kind, s);
+  if (e != hipSuccess) return hip_status(e, "bounds launch");
+  kvs::TopkArgs ta{};
+  ta.W = ba.W;
+  ta.seq_lens = seq_lens;
+  ta.sel = sel;
+  ta.B = L->num_seqs;
+  ta.Hkv = L->num_kv_heads;
+  ta.S = L->block_size;
+  ta.MB = L->max_blocks;
+  ta.k = k;
+  return hip_status(kvs::launch_topk(ta, s), "top-k launch");
+}
+
+kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const void* q,
+                                  const void* k_pool, const void* v_pool, const float* k_scales,
+                                  const float* v_scales, const int32_t* table, const int32_t* seq_lens,
+                                  const int32_t* sel, int32_t k, float sm_scale, float* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  kvs_status st = check_layout(L, true);
+  if (st != KVS_OK) return st;
+  if (table_kind != KVS_TABLE_PAGED && table_kind != KVS_TABLE_HOT)
+    return fail(KVS_ERR_INVALID_ARG, "unknown table_kind");
+  if (!q || !k_pool || !v_pool || !table || !seq_lens || !sel || !out)
+    return fail(KVS_ERR_INVALID_ARG, "q, pools, table, seq_lens, sel and out must be non-NULL");
+  if (L->kv_dtype == KVS_FP8_E4M3 && (!k_scales || !v_scales))
+    return fail(KVS_ERR_INVALID_ARG, "fp8 K/V need k_scales and v_scales");
+  if (k < 1 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [1, max_blocks]");
+  if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
+    return fail(KVS_ERR_INVALID_ARG, "sm_scale must be finite");
+  if (!workspace || workspace_bytes < attn_ws(L, k))
+    return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_attn_workspace_size()");
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 16) || !aligned(q, 4) ||
+      !aligned(out, 4))
+    return fail(KVS_ERR_INVALID_ARG, "pools and workspace must be 16-byte aligned");
+  unsigned int* err = nullptr;
+  if ((st = error_word(&err)) != KVS_OK) return st;
+  kvs::AttnArgs a{};
+  const int G = L->num_q_heads / L->num_kv_heads;
+  const int nsplit = attn_splits(L, k);
+  const size_t units = (size_t)L->num_seqs * L->num_q_heads * nsplit;
+  char* ws = static_cast<char*>(workspace);
+  a.part_m = reinterpret_cast<float*>(ws);
+  a.part_l = a.part_m + units;
+  a.part_acc = reinterpret_cast<float*>(ws + round_up(sizeof(float) * units * 2, 256));
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scales = k_scales;
+  a.v_scales = v_scales;
+  a.table = table;
+  a.seq_lens = seq_lens;
+  a.sel = sel;
+  a.out = out;
+  a.err = err;
+  a.q_scale = sm_scale * 1.4426950408889634f;
+  a.B = L->num_seqs;
+  a.Hq = L->num_q_heads;
+  a.Hkv = L->num_kv_heads;
+  a.G = G;
+  a.D = L->head_dim;
+  a.S = L->block_size;
+  a.MB = L->max_blocks;
+  a.P = L->num_pages;
+  a.qg = L->quant_group;
+  a.k = k;
+  a.nsplit = nsplit;
+  a.bps = (k + nsplit - 1) / nsplit;
+  a.hot = table_kind == KVS_TABLE_HOT ? 1 : 0;
+  return hip_status(kvs::launch_attn(a, kind_of(L->q_dtype), kind_of(L->kv_dtype), static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots,
+                                 int64_t step, int32_t* page_table, int32_t* slot_owner,
+                                 int64_t* slot_stamp, const void* host_k, const void* host_v,
+                                 const float* host_k_scales, const float* host_v_scales, void* hot_k,
+                                 void* hot_v, float* hot_k_scales, float* hot_v_scales,
+                                 int32_t* miss_list, int32_t* miss_count, void* stream) {
+  kvs_status st = check_layout(L, false);
+  if (st != KVS_OK) return st;
+  if (!sel || !page_table || !slot_owner || !slot_stamp || !host_k || !host_v || !hot_k || !hot_v ||
+      !miss_list || !miss_count)
+    return fail(KVS_ERR_INVALID_ARG, "a required pointer is NULL");
+  const bool fp8 = L->kv_dtype == KVS_FP8_E4M3;
+  if (fp8 && (!host_k_scales || !host_v_scales || !hot_k_scales || !hot_v_scales))
+    return fail(KVS_ERR_INVALID_ARG, "fp8 pools need host and hot scales");
+  if (num_slots < 1 || num_slots > 4096) return fail(KVS_ERR_UNSUPPORTED, "num_slots must be in [1, 4096]");
+  if (k < 1 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [1, max_blocks]");
+  if (k > num_slots) return fail(KVS_ERR_CAPACITY, "k selected blocks cannot fit in num_slots hot slots");
+  if (step < 0 || step >= (1ll << 50)) return fail(KVS_ERR_INVALID_ARG, "step must be in [0, 2^50)");
+  if ((long long)L->num_seqs * L->num_kv_heads * num_slots > 0x7FFFFFFFll)
+    return fail(KVS_ERR_INVALID_ARG, "total hot slots overflow int32");
+  if (!aligned(host_k, 16) || !aligned(host_v, 16) || !aligned(hot_k, 16) || !aligned(hot_v, 16))
+    return fail(KVS_ERR_INVALID_ARG, "host and hot pools must be 16-byte aligned");
+  // device aliases of the pinned host tier (hipHostMalloc memory is mapped)
+  const void* host_ptrs[4] = {host_k, host_v, host_k_scales, host_v_scales};
+  void* dev_ptrs[4] = {nullptr, nullptr, nullptr, nullptr};
+  for (int i = 0; i < (fp8 ? 4 : 2); ++i) {
+    hipError_t e = hipHostGetDevicePointer(&dev_ptrs[i], const_cast<void*>(host_ptrs[i]), 0);
+    if (e != hipSuccess || !dev_ptrs[i]) {
+      (void)hipGetLastError();
+      return fail(KVS_ERR_INVALID_ARG, "host pools must be pinned host memory (hipHostMalloc)");
+    }
+  }
+  unsigned int* err = nullptr;
+  if ((st = error_word(&err)) != KVS_OK) return st;
+  kvs::HotArgs a{};
+  a.sel = sel;
+  a.pt = page_table;
+  a.owner = slot_owner;
+  a.stamp = slot_stamp;
+  a.miss_list = miss_list;
+  a.miss_count = miss_count;
+  a.host_k = dev_ptrs[0];
+  a.host_v = dev_ptrs[1];
+  a.host_ks = static_cast<const float*>(dev_ptrs[2]);
+  a.host_vs = static_cast<const float*>(dev_ptrs[3]);
+  a.hot_k = hot_k;
+  a.hot_v = hot_v;
+  a.hot_ks = hot_k_scales;
+  a.hot_vs = hot_v_scales;
+  a.err = err;
+  a.step = step;
+  a.B = L->num_seqs;
+  a.Hkv = L->num_kv_heads;
+  a.D = L->head_dim;
+  a.S = L->block_size;
+  a.MB = L->max_blocks;
+  a.k = k;
+  a.ns = num_slots;
+  int n2 = 1;
+  while (n2 < num_slots) n2 <<= 1;
+  a.n2 = n2 < 2 ? 2 : n2;
+  a.qg = fp8 ? L->quant_group : 0;
+  a.elem_bytes = (int)elem_size(L->kv_dtype);
+  return hip_status(kvs::launch_hot(a, static_cast<hipStream_t>(stream)), "hot-buffer launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+"""Decode-step drivers: chain the C entry points of libkvs for one layer and
+own the device buffers they need (selection, workspaces, output, hot-buffer
+state).  All arithmetic runs in the library's kernels; torch only allocates.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import kvs
+
+
+class SparseDecodeStep:
+    """One layer's decode step over a paged KV cache (page "KV 稀疏化", §5
+    "Quest"): rebuild the summary of each sequence's newest block (its K row
+    was just appended), score and select the top-k blocks, attend over them.
+    """
+
+    def __init__(self, layout: kvs.Layout, k: int, device="cuda"):
+        L = self.layout = layout
+        self.k = k
+        dev = torch.device(device)
+        self.sel = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
+        self.select_ws = torch.empty(max(kvs.kvs_select_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(L.head_dim)
+
+    def new_summaries(self, device="cuda") -> torch.Tensor:
+        L = self.layout
+        return torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks, 2, L.head_dim),
+                           dtype=L.summary_dtype, device=device)
+
+    def prefill_summaries(self, k_pool, k_scales, block_table, seq_lens, summaries, stream=None):
+        kvs.kvs_build_summaries(self.layout, k_pool, k_scales, block_table, seq_lens, None,
+                                self.layout.max_blocks, summaries, stream)
+
+    def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,
+            newest_block, bounds_out=None, stream=None) -> torch.Tensor:
+        """newest_block: [B] int32 device tensor, ceil(seq_len/S) - 1."""
+        L, k = self.layout, self.k
+        kvs.kvs_build_summaries(L, k_pool, k_scales, block_table, seq_lens, newest_block, 1,
+                                summaries, stream)
+        kvs.kvs_select_topk(L, q, summaries, seq_lens, k, self.sel, bounds_out, self.select_ws, stream)
+        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, k_pool, v_pool, k_scales, v_scales,
+                                   block_table, seq_lens, self.sel, k, self.sm_scale, self.out,
+                                   self.attn_ws, stream)
+        return self.out
+
+
+class HotBufferStep:
+    """One layer's decode step with a hot device buffer over a pinned host
+    tier (page "KV 稀疏化", §7 "HiSparse"): page-table lookup, LRU slot
+    assignment and swap-in of the missed blocks, then attention through the
+    hot page table.  State starts empty (every entry -1)."""
+
+    def __init__(self, layout: kvs.Layout, k: int, num_slots: int, device="cuda"):
+        L = layout
+        self.k, self.ns = k, num_slots
+        dev = torch.device(device)
+        units = L.num_seqs * L.num_kv_heads
+        self.host_layout = layout
+        self.hot_layout = kvs.Layout(L.num_seqs, L.num_q_heads, L.num_kv_heads, L.head_dim,
+                                     L.block_size, L.max_blocks, units * num_slots, L.q_dtype,
+                                     L.kv_dtype, L.quant_group)
+        self.page_table = torch.full((L.num_seqs, L.num_kv_heads, L.max_blocks), -1, dtype=torch.int32, device=dev)
+        self.slot_owner = torch.full((L.num_seqs, L.num_kv_heads, num_slots), -1, dtype=torch.int32, device=dev)
+        self.slot_stamp = torch.full((L.num_seqs, L.num_kv_heads, num_slots), -1, dtype=torch.int64, device=dev)
+        pool_dt = {kvs.KVS_F32: torch.float32, kvs.KVS_BF16: torch.bfloat16, kvs.KVS_FP8_E4M3: torch.uint8}[L.kv_dtype]
+        shape = (units * num_slots, L.block_size, L.head_dim)
+        self.hot_k = torch.zeros(shape, dtype=pool_dt, device=dev)
+        self.hot_v = torch.zeros(shape, dtype=pool_dt, device=dev)
+        if L.quant_group:
+            sshape = (units * num_slots, L.block_size, L.head_dim // L.quant_group)
+            self.hot_ks = torch.ones(sshape, dtype=torch.float32, device=dev)
+            self.hot_vs = torch.ones(sshape, dtype=torch.float32, device=dev)
+        else:
+            self.hot_ks = self.hot_vs = None
+        self.miss_list = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
+        self.miss_count = torch.empty((L.num_seqs, L.num_kv_heads), dtype=torch.int32, device=dev)
+        self.out = torch.empty((L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
+        self.attn_ws = torch.empty(max(kvs.kvs_attn_workspace_size(self.hot_layout, k), 1), dtype=torch.uint8, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(L.head_dim)
+
+    def swap_in(self, step, sel, host_k, host_v, host_ks=None, host_vs=None, stream=None):
+        kvs.kvs_hot_lookup_swapin(self.host_layout, sel, self.k, self.ns, step, self.page_table,
+                                  self.slot_owner, self.slot_stamp, host_k, host_v, host_ks, host_vs,
+                                  self.hot_k, self.hot_v, self.hot_ks, self.hot_vs, self.miss_list,
+                                  self.miss_count, stream)
+
+    def attend(self, q, sel, seq_lens, stream=None) -> torch.Tensor:
+        kvs.kvs_sparse_decode_attn(self.hot_layout, kvs.KVS_TABLE_HOT, q, self.hot_k, self.hot_v,
+                                   self.hot_ks, self.hot_vs, self.page_table, seq_lens, sel, self.k,
+                                   self.sm_scale, self.out, self.attn_ws, stream)
+        return self.out
+
+    def run(self, step, sel, q, seq_lens, host_k, host_v, host_ks=None, host_vs=None, stream=None):
+        self.swap_in(step, sel, host_k, host_v, host_ks, host_vs, stream)
+        return self.attend(q, sel, seq_lens, stream)

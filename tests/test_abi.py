@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports every entry point include/kvs.h declares,
+and rejects bad host-visible arguments before touching the GPU (these calls
+return during validation, so they run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvs.h")
+
+
+@pytest.fixture(scope="module")
+def kvs():
+    lib = os.path.join(ROOT, "query_aware_sparse_kvs_amd", "libkvs.so")
+    if not os.path.exists(lib):
+        from query_aware_sparse_kvs_amd import build
+        build.build()
+    from query_aware_sparse_kvs_amd import kvs as mod
+    return mod
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ("kvs_build_summaries", "kvs_select_topk", "kvs_sparse_decode_attn",
+              "kvs_hot_lookup_swapin", "kvs_select_workspace_size", "kvs_attn_workspace_size",
+              "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(kvs):
+    lib = kvs.library()
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kvs.h but not exported"
+    assert set(kvs.EXPORTED) == set(declared_functions())
+
+
+def test_abi_version_and_status_strings(kvs):
+    assert kvs.kvs_abi_version() == 1
+    for st in range(5):
+        assert kvs.kvs_status_string(st).startswith("KVS_")
+    assert "unknown" in kvs.kvs_status_string(99)
+
+
+def _layout(kvs, **kw):
+    base = dict(num_seqs=2, num_q_heads=8, num_kv_heads=2, head_dim=128, block_size=64,
+                max_blocks=16, num_pages=32, q_dtype=kvs.KVS_BF16, kv_dtype=kvs.KVS_BF16,
+                quant_group=0)
+    base.update(kw)
+    return kvs.Layout(**base)
+
+
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+def _select(kvs, L, k=4, ws_bytes=1 << 20, q=FAKE, summ=FAKE):
+    lib = kvs.library()
+    return lib.kvs_select_topk(ctypes.byref(L.c()), q, summ, FAKE, k, FAKE, None, FAKE, ws_bytes, None)
+
+
+def _attn(kvs, L, k=4, kind=0, ws_bytes=1 << 24, scale=0.1):
+    lib = kvs.library()
+    return lib.kvs_sparse_decode_attn(ctypes.byref(L.c()), kind, FAKE, FAKE, FAKE, None, None, FAKE,
+                                      FAKE, FAKE, k, scale, FAKE, FAKE, ws_bytes, None)
+
+
+def test_workspace_sizes(kvs):
+    L = _layout(kvs)
+    assert kvs.kvs_select_workspace_size(L, 4) >= 8 * 2 * 2 * 16
+    assert kvs.kvs_select_workspace_size(L, 1) == 0  # k < 2
+    n = kvs.kvs_attn_num_splits(L, 8)
+    assert 1 <= n <= 8
+    assert kvs.kvs_attn_workspace_size(L, 8) >= 4 * 2 * 8 * n * (128 + 2)
+    assert kvs.kvs_attn_workspace_size(L, 17) == 0  # k > max_blocks
+    assert kvs.kvs_attn_workspace_size(_layout(kvs, head_dim=96), 4) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 96, 2), ("head_dim", 0, 1), ("block_size", 128, 2), ("block_size", 0, 1),
+    ("num_q_heads", 7, 1), ("num_q_heads", 2 * 32, 2), ("num_kv_heads", 0, 1),
+    ("max_blocks", 0, 1), ("max_blocks", 9000, 2), ("num_pages", 0, 1), ("num_seqs", -1, 1),
+    ("q_dtype", 2, 2), ("kv_dtype", 7, 1), ("quant_group", 32, 1),
+])
+def test_select_rejects_bad_layouts(kvs, field, value, status):
+    L = _layout(kvs, **{field: value})
+    assert _select(kvs, L) == status
+    assert kvs.kvs_last_error() != ""
+
+
+def test_fp8_layout_rules(kvs):
+    ok = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=48)
+    assert _attn(kvs, ok) == kvs.KVS_ERR_UNSUPPORTED
+    bad_pair = _layout(kvs, q_dtype=kvs.KVS_F32, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
+    assert _attn(kvs, bad_pair) == kvs.KVS_ERR_UNSUPPORTED  # (fp32 q, fp8 kv) pair
+    good = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
+    assert _attn(kvs, good) == kvs.KVS_ERR_INVALID_ARG  # fp8 without scales
+
+
+def test_select_argument_checks(kvs):
+    L = _layout(kvs)
+    assert _select(kvs, L, k=1) == kvs.KVS_ERR_INVALID_ARG
+    assert _select(kvs, L, k=17) == kvs.KVS_ERR_INVALID_ARG
+    assert _select(kvs, L, ws_bytes=8) == kvs.KVS_ERR_INVALID_ARG
+    assert _select(kvs, L, q=None) == kvs.KVS_ERR_INVALID_ARG
+    assert _select(kvs, L, summ=ctypes.c_void_p(0x100004)) == kvs.KVS_ERR_INVALID_ARG  # misaligned
+
+
+def test_attention_argument_checks(kvs):
+    L = _layout(kvs)
+    assert _attn(kvs, L, k=0) == kvs.KVS_ERR_INVALID_ARG
+    assert _attn(kvs, L, kind=2) == kvs.KVS_ERR_INVALID_ARG
+    assert _attn(kvs, L, ws_bytes=16) == kvs.KVS_ERR_INVALID_ARG
+    assert _attn(kvs, L, scale=float("nan")) == kvs.KVS_ERR_INVALID_ARG
+    assert _attn(kvs, L, scale=float("inf")) == kvs.KVS_ERR_INVALID_ARG
+
+
+def test_summaries_and_hot_argument_checks(kvs):
+    lib = kvs.library()
+    L = _layout(kvs)
+    c = ctypes.byref(L.c())
+    assert lib.kvs_build_summaries(c, FAKE, None, FAKE, FAKE, None, 17, FAKE, None) == 1
+    assert lib.kvs_build_summaries(c, None, None, FAKE, FAKE, None, 1, FAKE, None) == 1
+    fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
+    assert lib.kvs_build_summaries(ctypes.byref(fp8.c()), FAKE, None, FAKE, FAKE, None, 1, FAKE, None) == 1
+
+    def hot(k, ns, step=0):
+        return lib.kvs_hot_lookup_swapin(c, FAKE, k, ns, step, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                         FAKE, FAKE, None, None, FAKE, FAKE, None)
+    assert hot(8, 4) == kvs.KVS_ERR_CAPACITY
+    assert hot(4, 5000) == kvs.KVS_ERR_UNSUPPORTED
+    assert hot(0, 4) == kvs.KVS_ERR_INVALID_ARG
+    assert hot(4, 4, step=-1) == kvs.KVS_ERR_INVALID_ARG
