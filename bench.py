@@ -6,8 +6,9 @@ the top-k, attend over the selected blocks (split partials + merge).  The
 default workload is 8 sequences x 32 query / 4 KV heads, head dim 128, 32768
 tokens of bf16 K/V in 64-token pages, k = 128 of 512 blocks, over 32 layer
 instances with their own buffers (step i uses instance i mod 32, so no step
-re-reads data an earlier step left in the 256 MB last-level cache).  Every
-layer-step is captured once into a HIP graph and the timed loop replays them.
+re-reads data an earlier step left in the 256 MB last-level cache).  The
+layer sweep (every instance in order, as a decoder runs its layers) is
+captured once into a HIP graph and the timed loop replays it.
 
 Prints one JSON line.  Metric: decode query-tokens/s/layer = B / t(step),
 with the achieved HBM GB/s of the step and a roofline entry for the dominant
@@ -96,11 +97,16 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0
 
-    def run_step(i):
+    def run_append(i):
         d = layers[i]
         inp = d["inp"]
-        steps[i].run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"],
-                     inp["block_table"], inp["seq_lens"], d["summ"], d["newest"])
+        kvs.kvs_build_summaries(L, inp["k_pool"], inp["k_scales"], inp["block_table"], inp["seq_lens"],
+                                d["newest"], 1, d["summ"])
+
+    def run_select(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_select_topk(L, inp["q"], d["summ"], inp["seq_lens"], w.k, st.sel, None, st.select_ws)
 
     def run_attn(i):
         d, st = layers[i], steps[i]
@@ -109,8 +115,15 @@ def main(argv=None) -> int:
                                    inp["k_scales"], inp["v_scales"], inp["block_table"], inp["seq_lens"],
                                    st.sel, w.k, st.sm_scale, st.out, st.attn_ws)
 
+    def run_step(i):
+        run_append(i)
+        run_select(i)
+        run_attn(i)
+
     def capture(fn):
-        graphs = []
+        """One graph over every layer instance in order (as a decoder runs its
+        layers), plus one graph per layer for step counts that are not a
+        multiple of the layer count."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -118,36 +131,50 @@ def main(argv=None) -> int:
                 fn(i)  # eager warm-up (also initialises the library's per-device state)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        sweep = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(sweep):
+            for i in range(n_layers):
+                fn(i)
+        single = []
         for i in range(n_layers):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 fn(i)
-            graphs.append(g)
-        return graphs
+            single.append(g)
+        return sweep, single
 
-    step_graphs = capture(run_step)
-    attn_graphs = capture(run_attn)
-    torch.cuda.synchronize()
+    def replay(graphs, K):
+        sweep, single = graphs
+        for _ in range(K // n_layers):
+            sweep.replay()
+        for i in range(K % n_layers):
+            single[i].replay()
 
     def timed(graphs, K, W):
-        for i in range(W):
-            graphs[i % n_layers].replay()
+        replay(graphs, W)
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record(stream)
-        for i in range(K):
-            graphs[i % n_layers].replay()
+        replay(graphs, K)
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         return e0.elapsed_time(e1) / 1e3, wall
 
+    step_graphs = capture(run_step)
+    torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
-    t_attn, _ = timed(attn_graphs, args.steps, args.warmup)
+    # per-phase graphs: the dominant kernel (attention) for the roofline entry,
+    # and the two selection phases for the breakdown
+    phase = {}
+    for name, fn in (("append_summary", run_append), ("select_topk", run_select), ("attention", run_attn)):
+        t, _ = timed(capture(fn), args.steps, args.warmup)
+        phase[name] = t / args.steps
+    t_attn = phase["attention"] * args.steps
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
 
@@ -182,10 +209,11 @@ def main(argv=None) -> int:
                    "head_dim": w.D, "context": w.L, "block": w.S, "top_k_blocks": w.k,
                    "kv_storage": w.kv_dtype, "q_storage": w.q_dtype, "layer_instances": n_layers,
                    "graph_replay": True},
+        "phase_us": {k: round(v * 1e6, 3) for k, v in phase.items()},
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "sparse decode attention (split + merge)",
+        "roofline": {"bound": "hbm", "kernel": "kvs_sparse_decode_attn (attn_mfma_kernel + merge_kernel)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
                      "bytes_per_launch": by["attention"], "us_per_launch": round(attn_sec * 1e6, 3)},

@@ -67,10 +67,10 @@ static int layout_ok(const or_layout* L) {
   return 1;
 }
 
-/* K or V element (page, kv head g, slot s within the page, channel c). */
-static double kv_value(const or_layout* L, const void* pool, const float* scales,
-                       int64_t page, int32_t g, int32_t s, int32_t c) {
-  int64_t idx = ((page * L->Hkv + g) * (int64_t)L->S + s) * L->D + c;
+/* Element at flat index idx of a pool, with the fp8 scale of (page, g,
+ * token s, channel c). */
+static double pool_value(const or_layout* L, const void* pool, const float* scales,
+                         int64_t idx, int64_t page, int32_t g, int32_t s, int32_t c) {
   if (L->kv_dtype == 0) return (double)((const float*)pool)[idx];
   if (L->kv_dtype == 1) return or_bf16_to_f64(((const uint16_t*)pool)[idx]);
   {
@@ -78,6 +78,22 @@ static double kv_value(const or_layout* L, const void* pool, const float* scales
     int64_t sidx = ((page * L->Hkv + g) * (int64_t)L->S + s) * groups + c / L->quant_group;
     return (double)or_e4m3_scaled(((const uint8_t*)pool)[idx], scales[sidx]);
   }
+}
+
+/* K element (page, kv head g, token s within the page, channel c):
+ * token-major tile [S][D]. */
+static double kv_value(const or_layout* L, const void* pool, const float* scales,
+                       int64_t page, int32_t g, int32_t s, int32_t c) {
+  int64_t idx = ((page * L->Hkv + g) * (int64_t)L->S + s) * L->D + c;
+  return pool_value(L, pool, scales, idx, page, g, s, c);
+}
+
+/* V element (page, kv head g, token s, channel c): channel-major tile
+ * [D][S]. */
+static double v_value(const or_layout* L, const void* pool, const float* scales,
+                      int64_t page, int32_t g, int32_t s, int32_t c) {
+  int64_t idx = ((page * L->Hkv + g) * (int64_t)L->D + c) * L->S + s;
+  return pool_value(L, pool, scales, idx, page, g, s, c);
 }
 
 static int32_t num_blocks(const or_layout* L, int32_t len) {
@@ -325,7 +341,7 @@ int or_sparse_attn(const or_layout* L, const double* q,
           double p = exp(sm_scale * dot_qk(L, qh, k_pool, k_scales, page, g, s_in) - m);
           l = l + p;
           for (int32_t c = 0; c < L->D; ++c)
-            o[c] = o[c] + p * kv_value(L, v_pool, v_scales, page, g, s_in, c);
+            o[c] = o[c] + p * v_value(L, v_pool, v_scales, page, g, s_in, c);
         }
       }
       for (int32_t c = 0; c < L->D; ++c) o[c] = o[c] / l;
@@ -384,7 +400,7 @@ int or_dense_attn(const or_layout* L, const double* q,
         double p = exp(scores[t] - m);
         l = l + p;
         for (int32_t c = 0; c < L->D; ++c)
-          o[c] = o[c] + p * kv_value(L, v_pool, v_scales, page, g, t % L->S, c);
+          o[c] = o[c] + p * v_value(L, v_pool, v_scales, page, g, t % L->S, c);
       }
       for (int32_t c = 0; c < L->D; ++c) o[c] = o[c] / l;
     }

@@ -29,10 +29,13 @@
  *            head h reads KV head h / G), head dim D, S tokens per block
  *            (= page), max_blocks entries per block-table row, num_pages
  *            pages in the pool.
- *   pools  : K and V pools are [num_pages][Hkv][S][D] of kv_dtype
- *            (0 = fp32, 1 = bf16 bit patterns, 2 = OCP E4M3FN codes).
- *            fp8 scales are [num_pages][Hkv][S][D/quant_group] fp32; the
- *            value of an fp8 element is fp32(decode(code) * scale).
+ *   pools  : the K pool is [num_pages][Hkv][S][D] (token-major tiles), the
+ *            V pool [num_pages][Hkv][D][S] (channel-major tiles), both of
+ *            kv_dtype (0 = fp32, 1 = bf16 bit patterns, 2 = OCP E4M3FN
+ *            codes).  fp8 scales of K and of V are both
+ *            [num_pages][Hkv][S][D/quant_group] fp32, one per token and
+ *            channel group; the value of an fp8 element is
+ *            fp32(decode(code) * scale).
  *   table  : block_table[B][max_blocks], page id of logical block j.
  *   lens   : seq_lens[B], tokens per sequence (0 <= len <= max_blocks*S);
  *            nb = ceil(len / S) blocks, the last one possibly partial.

@@ -5,7 +5,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/kvs.h"
+#include "kvs.h"
 #include "kvs_internal.h"
 
 // OR of KVS_DEVERR_* bits raised by kernels on this device.
@@ -118,6 +118,7 @@ int attn_splits(const kvs_layout* L, int32_t k) {
   return kvs::attn_num_splits(L->num_seqs * L->num_kv_heads, k);
 }
 
+// attention workspace: [split m, l][split acc]
 size_t attn_ws(const kvs_layout* L, int32_t k) {
   const size_t units = (size_t)L->num_seqs * L->num_q_heads * attn_splits(L, k);
   return round_up(sizeof(float) * units * 2, 256) + round_up(sizeof(float) * units * L->head_dim, 256);

@@ -3,18 +3,41 @@
 // that are merged across tiles and splits ("分块稀疏注意力与KV Cache量化…",
 // §2.2), fp8 K/V dequantised inside the read (same page, §1.3).
 //
-// Work split: a (sequence, KV head) unit's k selected blocks are cut into
-// `nsplit` runs of `bps` entries; one 256-thread workgroup (4 wavefronts)
-// handles one run, each wavefront one block at a time.  For a block:
-//   scores   lane = token (64/S lanes share a token and split its channels);
-//            the group's G query rows sit in LDS and are read as broadcasts;
-//   softmax  per head, wavefront max/sum by shuffles, base-2 exponentials
-//            (the query is pre-scaled by sm_scale*log2 e);
-//   values   lane = channel pair; the tile's probabilities go through LDS.
-// The four wavefronts' (m, l, acc) are merged in LDS and written as a
-// split partial; combine_kernel merges the splits of a query head:
+// Work split (both kernels): a (sequence, KV head) unit's k selected blocks
+// are cut into `nsplit` runs of `bps` entries; one 256-thread workgroup
+// (4 wavefronts) handles one run, each wavefront one block (tile) at a time.
+// The four wavefronts' running (max, sum, acc) are merged in LDS and written
+// as a split partial (or, with a single split, as the output row);
+// merge_kernel then merges the splits of every query head:
 //   m* = max m_i, l* = sum l_i 2^(m_i-m*), o = sum acc_i 2^(m_i-m*) / l*.
-// Roofline: HBM-bound gather of 2*S*D*elem bytes per selected block.
+// (The merge needs the partials of workgroups on other XCDs, whose L2
+// caches are not coherent within a kernel; a kernel boundary is far cheaper
+// than a device-scope release per workgroup.)
+// Scores are kept in base 2: the query is scaled by sm_scale*log2(e).
+//
+// attn_mfma_kernel (bf16, S in {32, 64}): both products run on
+// v_mfma_f32_16x16x32_bf16 with the G query heads padded to 16 columns.
+//   scores  S^T = K Q^T: the A operand is 16 token rows x 32 channels of K,
+//           loaded straight from the token-major tile with 16-byte loads;
+//           B is Q^T, loaded once.  Token rows are permuted (tau below) so
+//           that the accumulator a lane ends up holding is exactly the
+//           8-token slice it must feed to the value product.
+//   values  O^T = V^T P^T: the A operand is 16 channels x 32 tokens of the
+//           channel-major V tile (contiguous 16-byte loads); B is P^T taken
+//           from the score accumulators in registers.  P is split into
+//           hi = bf16(p) and lo = bf16(p - hi), two MFMAs, so the product
+//           keeps ~16 bits of P.  No LDS traffic inside the tile loop.
+//   A wavefront resolves its pages (selection -> table) for all of them at
+//   once into LDS, then issues every load of a page (32 KiB of K and V)
+//   before its arithmetic.  One page per wavefront and short-lived
+//   workgroups: the workgroups that start as others finish keep the memory
+//   system busy while earlier ones compute.
+// attn_valu_kernel (fp32, fp8, and bf16 with S = 16): lane = token for the
+//   scores (64/S lanes split a token's channels), lane = channel pair for the
+//   values, probabilities broadcast through LDS; every K/V load of a tile is
+//   issued before any of its arithmetic.
+// Roofline: HBM-bound gather of 2*S*D*elem bytes (+ fp8 scales) per
+// selected block.
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -22,22 +45,338 @@ namespace {
 
 constexpr int kGMax = 16;
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Reads an input that no kernel of the call writes, at a wavefront-uniform
+// address, through the constant address space: the compiler then issues a
+// scalar load, which does not wait behind vector loads in flight.
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
+// Shared entry checks of one selection slot.  Returns the tile's pool entry
+// (page or hot slot), or -1 when the slot is padding or invalid.
+__device__ __forceinline__ int tile_entry(const AttnArgs& a, const int32_t* srow, int i, int b, int g,
+                                          int nb, int lane, int* j_out) {
+  const int j = ld_uniform(srow + i);
+  if (j < 0) {
+    if (j != -1 && lane == 0) raise_flag(a.err, 0x4u);
+    return -1;
+  }
+  const int jp = i > 0 ? ld_uniform(srow + i - 1) : -1;
+  if (j >= nb || (i > 0 && (jp >= j || jp < 0))) {
+    if (lane == 0) raise_flag(a.err, 0x4u);
+    if (j >= nb) return -1;
+  }
+  const int entry = a.hot ? ld_uniform(a.table + ((long long)b * a.Hkv + g) * a.MB + j)
+                          : ld_uniform(a.table + (long long)b * a.MB + j);
+  if (entry < 0 || entry >= a.P) {
+    if (lane == 0) raise_flag(a.err, 0x2u);
+    return -1;
+  }
+  *j_out = j;
+  return entry;
+}
+
+__device__ __forceinline__ int clamp_len(const AttnArgs& a, int b, bool flag_it) {
+  int len = ld_uniform(a.seq_lens + b);
+  const int cap = a.MB * a.S;
+  if (len < 0 || len > cap) {
+    if (flag_it) raise_flag(a.err, 0x1u);
+    len = len < 0 ? 0 : cap;
+  }
+  return len;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel (bf16)
+// ---------------------------------------------------------------------------
+
+// One 32-token sub-tile of a page: its K rows and V^T columns, and how many
+// of its tokens are valid (0 = nothing to do).
+struct SubTile {
+  const uint16_t* k;  // first K row of the sub-tile, [32][D] with row stride D
+  const uint16_t* v;  // V^T tile base + token offset, [D][S] with row stride S
+  int ntok;
+};
+
+template <int D, int S>
+struct MfmaRegs {
+  static constexpr int CS = D / 32;  // k-steps of the score product
+  static constexpr int CT = D / 16;  // channel tiles of the value product
+  uint4 kr[2][CS];                   // two 16-token row groups
+  uint4 vr[CT];                      // one 32-token k-step
+};
+
+template <int D, int S>
+__device__ __forceinline__ void load_subtile(const SubTile& t, int r, int j4, MfmaRegs<D, S>& R) {
+  constexpr int CS = D / 32, CT = D / 16;
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg) {
+    // tau(tg, r): the token row lane-row r of group tg stands for
+    const int row = 8 * (r >> 2) + 4 * tg + (r & 3);
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) R.kr[tg][cs] = *reinterpret_cast<const uint4*>(t.k + row * D + cs * 32 + 8 * j4);
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) R.vr[ct] = *reinterpret_cast<const uint4*>(t.v + (ct * 16 + r) * S + 8 * j4);
+}
+
+template <int D, int S>
+__device__ __forceinline__ void compute_subtile(const SubTile& t, int j4, MfmaRegs<D, S>& R, const bf16x8_t* qf,
+                                                float q_scale, float& m_run, float& l_run, f32x4_t* o) {
+  constexpr int CS = D / 32, CT = D / 16;
+  // scores: lane (r, j4) receives tokens 8*j4 + 4*tg + e of head r
+  f32x4_t sc[2];
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg) {
+    sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs)
+      sc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.kr[tg][cs]), qf[cs], sc[tg], 0, 0, 0);
+  }
+  float s[2][4];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = 8 * j4 + 4 * tg + e;
+      const float v = tok < t.ntok ? sc[tg][e] * q_scale : -__builtin_inff();
+      s[tg][e] = v;
+      tmax = fmaxf(tmax, v);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m_run, tmax);
+  const float alpha = exp2f(m_run - m_new);
+  float psum = 0.0f;
+#pragma unroll
+  for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s[tg][e] = exp2f(s[tg][e] - m_new);
+      psum += s[tg][e];
+    }
+  psum += __shfl_xor(psum, 16);
+  psum += __shfl_xor(psum, 32);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+  // P^T operand: slots 0..3 <- row group 0, slots 4..7 <- row group 1
+  bf16x8_t ph, pl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float pv = e < 4 ? s[0][e] : s[1][e - 4];
+    const __bf16 hb = static_cast<__bf16>(pv);
+    ph[e] = hb;
+    pl[e] = static_cast<__bf16>(pv - static_cast<float>(hb));
+  }
+  if (t.ntok < 32) {  // token positions past the sequence may hold anything: zero them
+    const int t0 = 8 * j4;
+    uint32_t keep[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (t0 + 2 * w < t.ntok ? 0x0000FFFFu : 0u) | (t0 + 2 * w + 1 < t.ntok ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      R.vr[ct].x &= keep[0];
+      R.vr[ct].y &= keep[1];
+      R.vr[ct].z &= keep[2];
+      R.vr[ct].w &= keep[3];
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.vr[ct]), ph, o[ct], 0, 0, 0);
+    o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.vr[ct]), pl, o[ct], 0, 0, 0);
+  }
+}
+
+// Resolves tiles [t0, t0 + 64) of a wavefront's list (pages i0 + 4*t of the
+// selection row), one tile per lane, into LDS: pool tile index and valid
+// token count (0 = nothing to do).  Vector loads in parallel across lanes:
+// two round trips for the whole chunk instead of two per tile.
+__device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int32_t* srow, int i0, int i1, int t0,
+                                              int b, int g, int nb, int len, int S, long long* wl_tile,
+                                              int* wl_ntok) {
+  const int lane = threadIdx.x & 63;
+  const int i = i0 + 4 * (t0 + lane);
+  long long tile = a.hot ? 0 : g;  // tile (0, g): always in bounds
+  int ntok = 0;
+  if (i < i1) {
+    const int j = srow[i];
+    bool ok = j >= 0;
+    if (j < -1) raise_flag(a.err, 0x4u);
+    if (ok) {
+      const int jp = i > 0 ? srow[i - 1] : -1;
+      if (j >= nb || (i > 0 && (jp >= j || jp < 0))) raise_flag(a.err, 0x4u);
+      ok = j < nb;
+    }
+    if (ok) {
+      const int entry = a.hot ? a.table[((long long)b * a.Hkv + g) * a.MB + j] : a.table[(long long)b * a.MB + j];
+      if (entry < 0 || entry >= a.P) {
+        raise_flag(a.err, 0x2u);
+      } else {
+        tile = a.hot ? (long long)entry : (long long)entry * a.Hkv + g;
+        ntok = min(S, len - j * S);
+      }
+    }
+  }
+  wl_tile[lane] = tile;
+  wl_ntok[lane] = ntok;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int D, int S>
+__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int CS = D / 32;  // k-steps of the score product
+  constexpr int CT = D / 16;  // 16-channel tiles of the value product
+  constexpr int NSUB = S / 32;  // 32-token sub-tiles per page
+  __shared__ float mg_m[4][16], mg_l[4][16];
+  __shared__ float mg_o[3][16][D + 4];
+  __shared__ long long wl_tile[4][64];
+  __shared__ int wl_ntok[4][64];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j4 = lane >> 4;
+  const int G = a.G;
+
+  // B operand of the score product: Q^T, column r = query head g*G + r
+  bf16x8_t qf[CS];
+  {
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + r) * D;
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < G) v = *reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4);
+      qf[cs] = as_bf16x8(v);
+    }
+  }
+  const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
+  const int nb = (len + S - 1) / S;
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4_t o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
+  const int i0 = split * a.bps + wave;           // this wavefront's pages: i0, i0+4, ...
+  const int i1 = min(split * a.bps + a.bps, a.k);
+  const int ntiles = i0 < i1 ? (i1 - i0 + 3) / 4 : 0;
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
+
+  for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
+    resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
+    const int nt = min(64, ntiles - t0);
+    // whole pages, one register buffer: all loads of a page, then its math
+    for (int tt = 0; tt < nt; ++tt) {
+      const long long tile = wl_tile[wave][tt];
+      const int ntok = wl_ntok[wave][tt];
+      if (ntok <= 0) continue;
+      MfmaRegs<D, S> rr[NSUB];
+      SubTile st[NSUB];
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h) {
+        st[h].k = kpool + (tile * S + h * 32) * D;
+        st[h].v = vpool + tile * D * S + h * 32;
+        st[h].ntok = max(0, min(32, ntok - h * 32));
+        load_subtile<D, S>(st[h], r, j4, rr[h]);
+      }
+      // keep every load of the page ahead of its arithmetic
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h)
+        if (st[h].ntok > 0) compute_subtile<D, S>(st[h], j4, rr[h], qf, a.q_scale, m_run, l_run, o);
+    }
+  }
+
+  // merge the four wavefronts: lane (r, j4) holds channels ct*16 + 4*j4 + e
+  if (j4 == 0) {
+    mg_m[wave][r] = m_run;
+    mg_l[wave][r] = l_run;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mg_o[wave - 1][r][ct * 16 + 4 * j4 + e] = o[ct][e];
+  }
+  __syncthreads();
+  if (wave == 0 && r < G) {
+    float M = mg_m[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w][r]);
+    float scw[4], L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mg_m[w][r];
+      scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
+      L += mg_l[w][r] * scw[w];
+    }
+    // one split: normalise and write the output row; else store the partial
+    const bool direct = a.nsplit == 1;
+    const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+    const long long hrow = (long long)b * a.Hq + (long long)g * G + r;
+    const long long pi = hrow * a.nsplit + split;
+    if (!direct && j4 == 0) {
+      a.part_m[pi] = M;
+      a.part_l[pi] = L;
+    }
+    float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float4 v;
+      float* pv = reinterpret_cast<float*>(&v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = ct * 16 + 4 * j4 + e;
+        float x = o[ct][e] * scw[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) x += mg_o[w - 1][r][c] * scw[w];
+        pv[e] = x * inv;
+      }
+      *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = v;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// VALU kernel (fp32, fp8, bf16 with 16-token blocks)
+// ---------------------------------------------------------------------------
+
 template <int QK, int KVK, int D, int S>
-__global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
-  constexpr int LPT = kWave / S;   // lanes per token in the score phase
-  constexpr int CPL = D / LPT;     // channels per lane in the score phase
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  constexpr int LPT = kWave / S;  // lanes per token in the score phase
+  constexpr int CPL = D / LPT;    // channels per lane in the score phase
+  constexpr int EB = elem_bytes<KVK>();
   constexpr int VEC = Vec16<KVK>::N;
   static_assert(CPL % VEC == 0, "channel split must be whole 16-byte vectors");
-  constexpr int VPL = D / kWave;   // channels per lane in the value phase
-  constexpr int EB = elem_bytes<KVK>();
+  constexpr int KL = CPL / VEC;         // 16-byte K loads per lane
+  constexpr int VPL = D / kWave;        // channels per lane in the value phase
+  constexpr int VL = S * EB / 16;       // 16-byte loads per V channel row
+  static_assert(VL >= 1, "a V channel row must span at least 16 bytes");
 
   extern __shared__ float smem[];
   const int G = a.G;
   float* qs = smem;                      // [G][D]
   float* ps = qs + G * D;                // [4][G][S]
-  float* mg_m = ps + 4 * G * S;          // [4][G]
+  float* vsc = ps + 4 * G * S;           // [4][S][groups] (fp8 V scales)
+  const int groups = KVK == K_FP8 ? D / a.qg : 1;
+  float* mg_m = vsc + 4 * S * groups;    // [4][G]
   float* mg_l = mg_m + 4 * G;            // [4][G]
-  float* mg_acc = mg_l + 4 * G;          // [3][G][D] (wavefronts 1..3)
+  float* mg_acc = mg_l + 4 * G;          // [3][G][D]
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -53,13 +392,7 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     qs[i] = v * a.q_scale;
   }
   __syncthreads();
-
-  int len = a.seq_lens[b];
-  const int cap = a.MB * S;
-  if (len < 0 || len > cap) {
-    if (tid == 0 && split == 0 && g == 0) raise_flag(a.err, 0x1u);
-    len = len < 0 ? 0 : cap;
-  }
+  const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
   const int nb = (len + S - 1) / S;
 
   float m_run[kGMax], l_run[kGMax], acc[kGMax][VPL];
@@ -76,43 +409,58 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
   const int i1 = min(i0 + a.bps, a.k);
   const int t = lane % S, part = lane / S;
   float* pw = ps + wave * G * S;
+  float* vw = vsc + wave * S * groups;
   const char* kb = static_cast<const char*>(a.k_pool);
   const char* vb = static_cast<const char*>(a.v_pool);
-  const int groups = KVK == K_FP8 ? D / a.qg : 1;
+  const int c0 = lane * VPL;  // value-phase channels of this lane
 
   for (int i = i0 + wave; i < i1; i += 4) {
-    const int j = srow[i];
-    if (j < 0) {
-      if (j != -1 && lane == 0) raise_flag(a.err, 0x4u);
-      continue;
-    }
-    if (j >= nb || (i > 0 && (srow[i - 1] >= j || srow[i - 1] < 0))) {
-      if (lane == 0) raise_flag(a.err, 0x4u);
-      if (j >= nb) continue;
-    }
-    const int entry = a.hot ? a.table[((long long)b * a.Hkv + g) * a.MB + j]
-                            : a.table[(long long)b * a.MB + j];
-    if (entry < 0 || entry >= a.P) {
-      if (lane == 0) raise_flag(a.err, 0x2u);
-      continue;
-    }
-    // first token row of the tile, in elements / D
-    const long long row0 = a.hot ? (long long)entry * S : ((long long)entry * a.Hkv + g) * S;
+    int j = 0;
+    const int entry = tile_entry(a, srow, i, b, g, nb, lane, &j);
+    if (entry < 0) continue;
+    const long long tile = a.hot ? (long long)entry : (long long)entry * a.Hkv + g;
+    const long long row0 = tile * S;  // token rows of the tile
     const int ntok = min(S, len - j * S);
 
-    // ---- scores ----
+    // ---- all loads of the tile ----
+    uint4 kraw[KL], vraw[VPL][VL];
+    if (t < ntok) {
+#pragma unroll
+      for (int x = 0; x < KL; ++x)
+        kraw[x] = *reinterpret_cast<const uint4*>(kb + ((row0 + t) * D + part * CPL + x * VEC) * EB);
+    }
+#pragma unroll
+    for (int e = 0; e < VPL; ++e)
+#pragma unroll
+      for (int x = 0; x < VL; ++x)
+        vraw[e][x] = *reinterpret_cast<const uint4*>(vb + ((tile * D + c0 + e) * S) * EB + x * 16);
+    if constexpr (KVK == K_FP8) {
+      for (int x = lane; x < S * groups; x += kWave) vw[x] = a.v_scales[row0 * groups + x];
+    }
+
+    // ---- scores (lane = token) ----
     float dot[kGMax];
 #pragma unroll
     for (int h = 0; h < kGMax; ++h) dot[h] = 0.0f;
     if (t < ntok) {
-      const long long r = row0 + t;
 #pragma unroll
-      for (int cc = 0; cc < CPL; cc += VEC) {
-        const int c = part * CPL + cc;
+      for (int x = 0; x < KL; ++x) {
+        const int c = part * CPL + x * VEC;
         float kv[VEC];
-        Vec16<KVK>::load(kb + (r * D + c) * EB, kv);
-        if constexpr (KVK == K_FP8) {
-          const float sc = a.k_scales[r * groups + c / a.qg];
+        const uint32_t ws[4] = {kraw[x].x, kraw[x].y, kraw[x].z, kraw[x].w};
+        if constexpr (KVK == K_F32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) kv[e] = __uint_as_float(ws[e]);
+        } else if constexpr (KVK == K_BF16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[2 * e] = bf16_lo(ws[e]);
+            kv[2 * e + 1] = bf16_hi(ws[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fp8x4_to_f32(ws[e], kv + 4 * e);
+          const float sc = a.k_scales[(row0 + t) * groups + c / a.qg];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) kv[e] *= sc;
         }
@@ -155,48 +503,42 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // ---- values ----
-    const int c0 = lane * VPL;
-    for (int tt = 0; tt < ntok; ++tt) {
-      float v[VPL];
-      const long long r = row0 + tt;
-      if constexpr (KVK == K_F32) {
-        if constexpr (VPL == 2) {
-          const float2 w = *reinterpret_cast<const float2*>(vb + (r * D + c0) * 4);
-          v[0] = w.x;
-          v[1] = w.y;
+
+    // ---- values (lane = channel), converted four tokens at a time ----
+    constexpr int PER = 16 / EB;  // tokens per 16-byte load
+#pragma unroll
+    for (int tt = 0; tt < S; tt += 4) {
+      float v[VPL][4];
+#pragma unroll
+      for (int e = 0; e < VPL; ++e) {
+        const uint4 w4 = vraw[e][tt / PER];
+        const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
+        const int o4 = tt % PER;
+        if constexpr (KVK == K_F32) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[e][q] = __uint_as_float(ws[q]);
+        } else if constexpr (KVK == K_BF16) {
+          v[e][0] = bf16_lo(ws[o4 / 2]);
+          v[e][1] = bf16_hi(ws[o4 / 2]);
+          v[e][2] = bf16_lo(ws[o4 / 2 + 1]);
+          v[e][3] = bf16_hi(ws[o4 / 2 + 1]);
         } else {
-          v[0] = *reinterpret_cast<const float*>(vb + (r * D + c0) * 4);
+          fp8x4_to_f32(ws[o4 / 4], v[e]);
         }
-      } else if constexpr (KVK == K_BF16) {
-        if constexpr (VPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(vb + (r * D + c0) * 2);
-          v[0] = bf16_lo(w);
-          v[1] = bf16_hi(w);
-        } else {
-          v[0] = __uint_as_float((uint32_t) * reinterpret_cast<const uint16_t*>(vb + (r * D + c0) * 2) << 16);
-        }
-      } else {
-        const float sc = a.v_scales[r * groups + c0 / a.qg];
-        if constexpr (VPL == 2) {
-          const uint32_t w = *reinterpret_cast<const uint16_t*>(vb + (r * D + c0));
-          typedef __attribute__((ext_vector_type(2))) float f2;
-          const f2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-          v[0] = f.x * sc;
-          v[1] = f.y * sc;
-        } else {
-          const uint32_t w = *reinterpret_cast<const uint8_t*>(vb + (r * D + c0));
-          typedef __attribute__((ext_vector_type(2))) float f2;
-          const f2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-          v[0] = f.x * sc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float vv = v[e][q];
+          if constexpr (KVK == K_FP8) vv *= vw[(tt + q) * groups + (c0 + e) / a.qg];
+          v[e][q] = tt + q < ntok ? vv : 0.0f;
         }
       }
 #pragma unroll
       for (int h = 0; h < kGMax; ++h) {
         if (h < G) {
-          const float p = pw[h * S + tt];
+          const float4 p4 = *reinterpret_cast<const float4*>(pw + h * S + tt);
 #pragma unroll
-          for (int e = 0; e < VPL; ++e) acc[h][e] += p * v[e];
+          for (int e = 0; e < VPL; ++e)
+            acc[h][e] += p4.x * v[e][0] + p4.y * v[e][1] + p4.z * v[e][2] + p4.w * v[e][3];
         }
       }
     }
@@ -215,99 +557,189 @@ __global__ __launch_bounds__(256) void attn_split_kernel(AttnArgs a) {
     for (int h = 0; h < kGMax; ++h)
       if (h < G)
 #pragma unroll
-        for (int e = 0; e < VPL; ++e) mg_acc[((wave - 1) * G + h) * D + lane * VPL + e] = acc[h][e];
+        for (int e = 0; e < VPL; ++e) mg_acc[((wave - 1) * G + h) * D + c0 + e] = acc[h][e];
   }
   __syncthreads();
-  if (wave != 0) return;
-  const long long pbase = ((long long)b * a.Hq + (long long)g * G) * a.nsplit + split;
+  if (wave == 0) {
+    const bool direct = a.nsplit == 1;
 #pragma unroll
-  for (int h = 0; h < kGMax; ++h) {
-    if (h >= G) continue;
-    float M = mg_m[h];
+    for (int h = 0; h < kGMax; ++h) {
+      if (h >= G) continue;
+      float M = mg_m[h];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w * G + h]);
-    float sc[4];
-    float L = 0.0f;
+      for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w * G + h]);
+      float sc[4];
+      float L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mg_m[w * G + h];
-      sc[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
-      L += mg_l[w * G + h] * sc[w];
-    }
-    const long long pi = pbase + (long long)h * a.nsplit;
-    if (lane == 0) {
-      a.part_m[pi] = M;
-      a.part_l[pi] = L;
-    }
+      for (int w = 0; w < 4; ++w) {
+        const float mw = mg_m[w * G + h];
+        sc[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
+        L += mg_l[w * G + h] * sc[w];
+      }
+      const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+      const long long hrow = (long long)b * a.Hq + (long long)g * G + h;
+      const long long pi = hrow * a.nsplit + split;
+      if (!direct && lane == 0) {
+        a.part_m[pi] = M;
+        a.part_l[pi] = L;
+      }
+      float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
 #pragma unroll
-    for (int e = 0; e < VPL; ++e) {
-      float o = acc[h][e] * sc[0];
+      for (int e = 0; e < VPL; ++e) {
+        float o = acc[h][e] * sc[0];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) o += mg_acc[((w - 1) * G + h) * D + lane * VPL + e] * sc[w];
-      a.part_acc[pi * D + lane * VPL + e] = o;
+        for (int w = 1; w < 4; ++w) o += mg_acc[((w - 1) * G + h) * D + c0 + e] * sc[w];
+        dst[c0 + e] = o * inv;
+      }
     }
   }
 }
 
-// one workgroup per (sequence, query head); thread c owns output channel c
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-  if (c >= a.D) return;
-  const long long pbase = ((long long)b * a.Hq + h) * a.nsplit;
-  float M = -__builtin_inff();
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_m[pbase + s]);
-  float o = 0.0f;
-  if (M != -__builtin_inff()) {
-    float L = 0.0f, acc = 0.0f;
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float ms = a.part_m[pbase + s];
-      const float w = ms == -__builtin_inff() ? 0.0f : exp2f(ms - M);
-      L += a.part_l[pbase + s] * w;
-      acc += a.part_acc[(pbase + s) * a.D + c] * w;
+// Split merge: one 256-thread workgroup per 2 query heads.  Thread t takes
+// 4 output channels of one head and a quarter of the splits; all of its
+// partial loads (m, acc) are issued together, the quarters are summed in LDS.
+constexpr int kMergeHeads = 2;
+
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
+  constexpr int C4 = D / 4;                    // float4 chunks per head
+  constexpr int CH = kMergeHeads * C4;         // chunks per workgroup
+  constexpr int SG = 256 / CH;                 // split groups
+  constexpr int BATCH = 8;                     // partial rows in flight per thread
+  __shared__ float4 red[SG][CH];
+  __shared__ float hm[kMergeHeads], hl[kMergeHeads];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const long long h0 = (long long)blockIdx.x * kMergeHeads;  // first head row (b*Hq + h)
+  const long long nrows = (long long)a.B * a.Hq;
+  const int ns = a.nsplit;
+  const int ch = tid % CH, sg = tid / CH;
+  const int hh = ch / C4, c = (ch % C4) * 4;
+  const long long row = h0 + hh;
+  // per head: max and normaliser over the splits (one wavefront per head)
+  if (wave < kMergeHeads && h0 + wave < nrows) {
+    const float* pm = a.part_m + (h0 + wave) * ns;
+    const float* pl = a.part_l + (h0 + wave) * ns;
+    float M = -__builtin_inff();
+    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, pm[s]);
+    M = wave_max(M);
+    float L = 0.0f;
+    for (int s = lane; s < ns; s += kWave) {
+      const float ms = pm[s];
+      L += ms == -__builtin_inff() ? 0.0f : pl[s] * exp2f(ms - M);
     }
-    o = acc / L;
+    L = wave_sum(L);
+    if (lane == 0) {
+      hm[wave] = M;
+      hl[wave] = L;
+    }
   }
-  a.out[((long long)b * a.Hq + h) * a.D + c] = o;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  const bool live = row < nrows;
+  float4 v[BATCH];
+  float ms[BATCH];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int x = 0; x < BATCH; ++x) {
+      const int s = s0 + x * SG;
+      v[x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      ms[x] = -__builtin_inff();
+      if (live && s < ns) {
+        v[x] = *reinterpret_cast<const float4*>(a.part_acc + (row * ns + s) * D + c);
+        ms[x] = a.part_m[row * ns + s];
+      }
+    }
+  };
+  auto add_batch = [&](float M) {
+#pragma unroll
+    for (int x = 0; x < BATCH; ++x) {
+      const float w = ms[x] == -__builtin_inff() ? 0.0f : exp2f(ms[x] - M);
+      acc.x += w * v[x].x;
+      acc.y += w * v[x].y;
+      acc.z += w * v[x].z;
+      acc.w += w * v[x].w;
+    }
+  };
+  // the first batch is in flight while the per-head max is computed; every
+  // thread meets the same two barriers
+  load_batch(sg);
+  __syncthreads();
+  const float Mh = live ? hm[hh] : 0.0f;
+  add_batch(Mh);
+  for (int s0 = sg + SG * BATCH; s0 < ns; s0 += SG * BATCH) {
+    load_batch(s0);
+    add_batch(Mh);
+  }
+  red[sg][ch] = acc;
+  __syncthreads();
+  if (sg != 0 || !live) return;
+#pragma unroll
+  for (int q = 1; q < SG; ++q) {
+    const float4 o = red[q][ch];
+    acc.x += o.x;
+    acc.y += o.y;
+    acc.z += o.z;
+    acc.w += o.w;
+  }
+  const float M = hm[hh], L = hl[hh];
+  const float inv = (M != -__builtin_inff() && L > 0.0f) ? 1.0f / L : 0.0f;
+  *reinterpret_cast<float4*>(a.out + row * D + c) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
 template <int QK, int KVK, int D>
-hipError_t launch_s(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
-  const size_t lds = sizeof(float) * ((size_t)a.G * D + 4 * (size_t)a.G * a.S + 8 * (size_t)a.G +
-                                      3 * (size_t)a.G * D);
+  const int groups = KVK == K_FP8 ? D / a.qg : 1;
+  const size_t lds = sizeof(float) * ((size_t)a.G * D + 4 * (size_t)a.G * a.S + 4 * (size_t)a.S * groups +
+                                      8 * (size_t)a.G + 3 * (size_t)a.G * D);
   switch (a.S) {
-    case 16: hipLaunchKernelGGL((attn_split_kernel<QK, KVK, D, 16>), grid, dim3(256), lds, st, a); break;
-    case 32: hipLaunchKernelGGL((attn_split_kernel<QK, KVK, D, 32>), grid, dim3(256), lds, st, a); break;
-    default: hipLaunchKernelGGL((attn_split_kernel<QK, KVK, D, 64>), grid, dim3(256), lds, st, a); break;
+    case 16: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 16>), grid, dim3(256), lds, st, a); break;
+    case 32: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 32>), grid, dim3(256), lds, st, a); break;
+    default: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 64>), grid, dim3(256), lds, st, a); break;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)a.Hq, (unsigned)a.B), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
-template <int QK, int KVK>
-hipError_t launch_d(const AttnArgs& a, hipStream_t st) {
-  return a.D == 64 ? launch_s<QK, KVK, 64>(a, st) : launch_s<QK, KVK, 128>(a, st);
+template <int D>
+hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
+  if (a.S == 32)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 32>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 64>), grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 int attn_num_splits(int units, int k) {
-  // enough workgroups to cover the 256 compute units several times over,
-  // but at least one selected block per wavefront of a split
+  // one selected page per wavefront (4 per workgroup), while the grid stays
+  // within 8192 workgroups; beyond that a wavefront takes several pages
   const int by_k = (k + 3) / 4;
-  int want = (2048 + units - 1) / (units > 0 ? units : 1);
-  if (want < 1) want = 1;
-  int n = by_k < want ? by_k : want;
+  int cap = 8192 / (units > 0 ? units : 1);
+  if (cap < 1) cap = 1;
+  const int n = by_k < cap ? by_k : cap;
   return n < 1 ? 1 : n;
 }
 
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  if (q_kind == K_F32 && kv_kind == K_F32) return launch_d<K_F32, K_F32>(a, st);
-  if (q_kind == K_BF16 && kv_kind == K_BF16) return launch_d<K_BF16, K_BF16>(a, st);
-  return launch_d<K_BF16, K_FP8>(a, st);
+  hipError_t e;
+  if (q_kind == K_BF16 && kv_kind == K_BF16 && a.S >= 32)
+    e = a.D == 64 ? launch_mfma<64>(a, st) : launch_mfma<128>(a, st);
+  else if (q_kind == K_F32 && kv_kind == K_F32)
+    e = a.D == 64 ? launch_valu<K_F32, K_F32, 64>(a, st) : launch_valu<K_F32, K_F32, 128>(a, st);
+  else if (q_kind == K_BF16 && kv_kind == K_BF16)
+    e = a.D == 64 ? launch_valu<K_BF16, K_BF16, 64>(a, st) : launch_valu<K_BF16, K_BF16, 128>(a, st);
+  else
+    e = a.D == 64 ? launch_valu<K_BF16, K_FP8, 64>(a, st) : launch_valu<K_BF16, K_FP8, 128>(a, st);
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const long long rows = (long long)a.B * a.Hq;
+  const dim3 grid((unsigned)((rows + kMergeHeads - 1) / kMergeHeads));
+  if (a.D == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace kvs

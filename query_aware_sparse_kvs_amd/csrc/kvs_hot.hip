@@ -160,16 +160,17 @@ __global__ __launch_bounds__(256) void swapin_copy_kernel(HotArgs a) {
   const long long src_off = ((long long)u * a.MB + j) * tile_bytes;
   const long long dst_off = (long long)slot * tile_bytes;
   const int n16 = (int)(tile_bytes / 16);
-  const uint4* sk = reinterpret_cast<const uint4*>(static_cast<const char*>(a.host_k) + src_off);
-  const uint4* sv = reinterpret_cast<const uint4*>(static_cast<const char*>(a.host_v) + src_off);
-  uint4* dk = reinterpret_cast<uint4*>(static_cast<char*>(a.hot_k) + dst_off);
-  uint4* dv = reinterpret_cast<uint4*>(static_cast<char*>(a.hot_v) + dst_off);
+  const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_k) + src_off);
+  const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_v) + src_off);
+  u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_k) + dst_off);
+  u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_v) + dst_off);
   constexpr int kMaxPer = 8;  // 16-byte vectors per thread per round
   for (int x0 = 0; x0 < n16; x0 += 256 * kMaxPer) {
-    uint4 bk[kMaxPer], bv[kMaxPer];
+    u32x4 bk[kMaxPer], bv[kMaxPer];
 #pragma unroll
     for (int q = 0; q < kMaxPer; ++q) {
       const int x = x0 + q * 256 + tid;
+      bk[q] = bv[q] = u32x4{0u, 0u, 0u, 0u};
       if (x < n16) {
         bk[q] = sk[x];
         bv[q] = sv[x];

@@ -12,6 +12,10 @@ enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2 };
 
 constexpr int kWave = 64;
 
+// 16 bytes as a native vector (HIP's uint4 is a struct; copying it whole
+// keeps staging arrays out of registers)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // ---------------------------------------------------------------------------
 // element conversion
 // ---------------------------------------------------------------------------

@@ -3,7 +3,9 @@
 // summaries, keep the top-k; the sink block and the newest block are always
 // kept, same page §2 and "SparDA：把KV選擇提前一層…" §4.2).
 //
-// bounds_kernel: one thread per (block, query head).  The block score is
+// bounds_kernel: a workgroup stages 32 consecutive blocks' summaries (16 for
+// G = 16) in LDS with coalesced 16-byte loads, then runs one thread per
+// (block, query head).  The block score is
 // U = sum_c max(q_c*mn_c, q_c*mx_c); since mx_c >= mn_c the larger product is
 // q_c*mx_c when q_c >= 0 and q_c*mn_c otherwise, so each channel costs one
 // select and one fp64 fma.  Every product of a bf16/fp32 query with a
@@ -13,26 +15,56 @@
 // of the summaries (2*D*elem bytes per block and KV head).
 //
 // topk_kernel: one 256-thread workgroup per (sequence, KV head).  Scores are
-// mapped to order-preserving 64-bit keys and a most-significant-digit radix
-// select (8 passes of 8 bits, LDS histogram) finds the (k-2)-th largest key
-// among blocks 1..nb-2; ties at that key go to the lowest block ids, the
-// (W desc, id asc) order.  A block-wide prefix sum then writes the chosen
-// ids in ascending order.  Latency-bound.
+// mapped to order-preserving 64-bit keys.  A most-significant-digit radix
+// select (8-bit digits, LDS histogram) over the high 32 bits, starting at
+// the first bit where the candidates' keys differ, finds the bucket of the
+// (k-2)-th largest key among blocks 1..nb-2; only when that bucket holds
+// more keys than are needed does a second select run on the low 32 bits of
+// the tied keys.  Ties on the full key go to the lowest block ids, the
+// (W desc, id asc) order.  A block-wide prefix sum writes the chosen ids in
+// ascending order.  Latency-bound.
 #include "kvs_internal.h"
 
 namespace kvs {
 namespace {
 
+// Blocks per bounds workgroup and its thread count for G query heads per KV
+// head: one thread per (block, head).
+template <int G>
+struct BoundShape {
+  static constexpr int NBLK = G >= 16 ? 16 : 32;
+  static constexpr int THREADS = NBLK * G;
+};
+
 template <int QK, int SK, int D, int G>
-__global__ __launch_bounds__(256) void bounds_kernel(BoundArgs a) {
-  constexpr int NBLK = 256 / G;  // blocks per workgroup
-  constexpr int QPAD = 4;
+__global__ __launch_bounds__(BoundShape<G>::THREADS) void bounds_kernel(BoundArgs a) {
+  constexpr int NBLK = BoundShape<G>::NBLK;
+  constexpr int NT = BoundShape<G>::THREADS;
+  constexpr int EB = elem_bytes<SK>();
+  constexpr int ROWB = 2 * D * EB;            // bytes of one block's summary
+  constexpr int ROWP = ROWB + 16;             // padded LDS row (bank spread)
+  constexpr int NV = NBLK * ROWB / 16;        // 16-byte vectors of the chunk
+  constexpr int NPT = (NV + NT - 1) / NT;
   constexpr int SVEC = Vec16<SK>::N;
-  __shared__ float qs[G][D + QPAD];
+  __shared__ float qs[G][D + 4];
+  __shared__ __attribute__((aligned(16))) char sm[NBLK * ROWP];
   const int b = blockIdx.z, g = blockIdx.y;
   const int tid = threadIdx.x;
-  // stage the group's G query rows (exact in fp32 for bf16/fp32 queries)
-  for (int i = tid; i < G * D; i += 256) {
+  const int j0 = blockIdx.x * NBLK;
+
+  const int nmem = min(NBLK, a.MB - j0);   // blocks of this chunk inside the array
+
+  // stage the chunk's summaries: every load issued before any use, and not
+  // waiting for seq_lens (blocks past nb are read but never used)
+  const char* src = static_cast<const char*>(a.summ) + ((((long long)b * a.Hkv + g) * a.MB + j0) * 2 * D) * EB;
+  u32x4 raw[NPT];
+#pragma unroll
+  for (int x = 0; x < NPT; ++x) {
+    const int v = x * NT + tid;
+    raw[x] = u32x4{0u, 0u, 0u, 0u};
+    if (v < NV && v / (ROWB / 16) < nmem) raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)v * 16);
+  }
+  for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, c = i % D;
     const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
     float v;
@@ -42,10 +74,6 @@ __global__ __launch_bounds__(256) void bounds_kernel(BoundArgs a) {
       v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
     qs[h][c] = v;
   }
-  __syncthreads();
-
-  const int h = tid % G;
-  const int j = blockIdx.x * NBLK + tid / G;
   int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
   if (len < 0 || len > cap) {
@@ -53,19 +81,29 @@ __global__ __launch_bounds__(256) void bounds_kernel(BoundArgs a) {
     len = len < 0 ? 0 : cap;
   }
   const int nb = (len + a.S - 1) / a.S;
+  const int nvalid = min(NBLK, nb - j0);  // blocks of this chunk below nb (may be <= 0)
+#pragma unroll
+  for (int x = 0; x < NPT; ++x) {
+    const int v = x * NT + tid;
+    if (v < NV && v / (ROWB / 16) < nmem) {
+      const int blk = v / (ROWB / 16), off = (v % (ROWB / 16)) * 16;
+      *reinterpret_cast<u32x4*>(sm + blk * ROWP + off) = raw[x];
+    }
+  }
+  __syncthreads();
 
+  const int h = tid % G, blk = tid / G;
+  const int j = j0 + blk;
   double acc = -__builtin_inf();
-  if (j < nb) {
+  if (blk < nvalid) {
     acc = 0.0;
-    const char* sb = static_cast<const char*>(a.summ);
-    const long long row = (((long long)b * a.Hkv + g) * a.MB + j) * 2 * D;
-    const char* pmn = sb + row * elem_bytes<SK>();
-    const char* pmx = sb + (row + D) * elem_bytes<SK>();
-#pragma unroll 2
+    const char* pmn = sm + blk * ROWP;
+    const char* pmx = pmn + D * EB;
+#pragma unroll 4
     for (int c0 = 0; c0 < D; c0 += SVEC) {
       float mn[SVEC], mx[SVEC];
-      Vec16<SK>::load(pmn + c0 * elem_bytes<SK>(), mn);
-      Vec16<SK>::load(pmx + c0 * elem_bytes<SK>(), mx);
+      Vec16<SK>::load(pmn + c0 * EB, mn);
+      Vec16<SK>::load(pmx + c0 * EB, mx);
 #pragma unroll
       for (int e = 0; e < SVEC; ++e) {
         const float qc = qs[h][c0 + e];
@@ -94,11 +132,85 @@ __device__ __forceinline__ unsigned long long order_key(double w) {
   return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
 }
 
+// Radix select over the active 32-bit keys of a 256-thread workgroup: finds
+// the value T of the rem-th largest active key (rem is 1-based) and how many
+// keys equal to T are needed (*rem_eq).  Keys share the bits above byte
+// `start_byte` (given in `prefix`), so only bytes start_byte..0 are scanned.
+template <int PT>
+__device__ __forceinline__ void radix_select_u32(const unsigned (&key)[PT], const bool (&act)[PT], int rem,
+                                                 int start_byte, unsigned prefix, unsigned* hist,
+                                                 unsigned* sh_T, int* sh_rem, unsigned* T, int* rem_eq) {
+  const int tid = threadIdx.x;
+  unsigned mask = start_byte >= 3 ? 0u : (0xFFFFFFFFu << (8 * (start_byte + 1)));
+  prefix &= mask;
+  for (int pass = start_byte; pass >= 0; --pass) {
+    const int shift = pass * 8;
+    hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      if (act[i] && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      // lane l owns digits 255-4l .. 252-4l (highest digits first)
+      unsigned c4[4], s = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c4[e] = hist[255 - 4 * tid - e];
+        s += c4[e];
+      }
+      unsigned incl = s;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const unsigned o = __shfl_up(incl, off);
+        if (tid >= off) incl += o;
+      }
+      unsigned above = incl - s;  // keys in higher digits
+      if ((int)above < rem && rem <= (int)incl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if ((int)(above + c4[e]) >= rem) {
+            *sh_T = prefix | ((unsigned)(255 - 4 * tid - e) << shift);
+            *sh_rem = rem - (int)above;
+            break;
+          }
+          above += c4[e];
+        }
+      }
+    }
+    __syncthreads();
+    prefix = *sh_T;
+    rem = *sh_rem;
+    mask |= 0xFFu << shift;
+  }
+  *T = prefix;
+  *rem_eq = rem;
+}
+
+// block-wide min and max of v over 256 threads (tmp: 8 words of LDS)
+__device__ __forceinline__ void block_min_max_256(unsigned v_min, unsigned v_max, unsigned* tmp, unsigned* mn,
+                                                  unsigned* mx) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    v_min = min(v_min, (unsigned)__shfl_xor((int)v_min, off));
+    v_max = max(v_max, (unsigned)__shfl_xor((int)v_max, off));
+  }
+  if (lane == 0) {
+    tmp[wave] = v_min;
+    tmp[4 + wave] = v_max;
+  }
+  __syncthreads();
+  *mn = min(min(tmp[0], tmp[1]), min(tmp[2], tmp[3]));
+  *mx = max(max(tmp[4], tmp[5]), max(tmp[6], tmp[7]));
+}
+
 template <int PT>  // candidates per thread (contiguous block ids)
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  __shared__ unsigned int hist[256];
+  __shared__ unsigned hist[256];
+  __shared__ unsigned mm_tmp[8];
   __shared__ int scan_tmp[4];
-  __shared__ unsigned long long sh_prefix;
+  __shared__ unsigned sh_T;
   __shared__ int sh_rem;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int k = a.k;
@@ -108,84 +220,92 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   const int nb = (len + a.S - 1) / a.S;
   int32_t* out = a.sel + ((long long)b * a.Hkv + g) * k;
 
+  // scores of every id below MB are loaded before nb is known (ids past nb
+  // are never candidates); ids are spread as contiguous runs of `per`
+  const double* W = a.W + ((long long)b * a.Hkv + g) * a.MB;
+  const int per = (a.MB + 255) / 256;  // ids per thread, <= PT
+  const int j0 = tid * per;
+  double wv[PT];
+#pragma unroll
+  for (int i = 0; i < PT; ++i) wv[i] = (i < per && j0 + i < a.MB) ? W[j0 + i] : 0.0;
   if (nb <= k) {  // every block, then padding
     for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
     return;
   }
   const int M = k - 2;  // free picks among blocks 1..nb-2
-  const double* W = a.W + ((long long)b * a.Hkv + g) * a.MB;
-  const int per = (nb + 255) / 256;  // ids per thread, <= PT
-  const int j0 = tid * per;
 
-  unsigned long long key[PT];
+  bool cand[PT];
+  unsigned hi[PT], lo[PT];
+  unsigned hmin = 0xFFFFFFFFu, hmax = 0u;
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int j = j0 + i;
-    const bool cand = i < per && j >= 1 && j <= nb - 2;
-    key[i] = cand ? order_key(W[j]) : 0ull;
-  }
-
-  unsigned long long prefix = 0ull, mask = 0ull;
-  int rem = M;  // rank (1-based, from the top) still to locate
-  if (M > 0) {
-    for (int pass = 7; pass >= 0; --pass) {
-      const int shift = pass * 8;
-      hist[tid] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int j = j0 + i;
-        const bool cand = i < per && j >= 1 && j <= nb - 2;
-        if (cand && (key[i] & mask) == prefix)
-          atomicAdd(&hist[(unsigned)(key[i] >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns digits 255-4l .. 252-4l (highest digits first)
-        unsigned int c4[4], s = 0u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          c4[e] = hist[255 - 4 * tid - e];
-          s += c4[e];
-        }
-        unsigned int incl = s;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const unsigned int o = __shfl_up(incl, off);
-          if (tid >= off) incl += o;
-        }
-        unsigned int above = incl - s;  // count in higher digits
-        if ((int)above < rem && rem <= (int)incl) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if ((int)(above + c4[e]) >= rem) {
-              sh_prefix = prefix | ((unsigned long long)(255 - 4 * tid - e) << shift);
-              sh_rem = rem - (int)above;
-              break;
-            }
-            above += c4[e];
-          }
-        }
-      }
-      __syncthreads();
-      prefix = sh_prefix;
-      rem = sh_rem;
-      mask |= 0xFFull << shift;
-      __syncthreads();
+    cand[i] = i < per && j >= 1 && j <= nb - 2;
+    const unsigned long long key = cand[i] ? order_key(wv[i]) : 0ull;
+    hi[i] = (unsigned)(key >> 32);
+    lo[i] = (unsigned)key;
+    if (cand[i]) {
+      hmin = min(hmin, hi[i]);
+      hmax = max(hmax, hi[i]);
     }
   }
-  // prefix = the M-th largest key T; rem = how many keys equal to T to take
-  int n_eq = 0;
+  // phase 1: threshold on the high 32 bits of the key
+  unsigned T_hi = 0u, T_lo = 0u;
+  int rem_hi = 0, rem_lo = 0, n_eq = 0;
+  bool need_lo = false;
+  bool eqh[PT];
+  if (M > 0) {
+    unsigned mn, mx;
+    block_min_max_256(hmin, hmax, mm_tmp, &mn, &mx);
+    if (mn == mx) {
+      T_hi = mn;
+      rem_hi = M;
+    } else {
+      const int top_bit = 31 - __clz(mn ^ mx);
+      radix_select_u32<PT>(hi, cand, M, top_bit / 8, mn, hist, &sh_T, &sh_rem, &T_hi, &rem_hi);
+    }
+    int cnt = 0;
 #pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int j = j0 + i;
-    const bool cand = i < per && j >= 1 && j <= nb - 2;
-    n_eq += (M > 0 && cand && key[i] == prefix) ? 1 : 0;
+    for (int i = 0; i < PT; ++i) {
+      eqh[i] = cand[i] && hi[i] == T_hi;
+      cnt += eqh[i] ? 1 : 0;
+    }
+    int tot;
+    (void)block_exclusive_scan_256(cnt, scan_tmp, &tot);
+    n_eq = tot;
+    // phase 2 (only when the threshold bucket holds more keys than needed):
+    // threshold on the low 32 bits among the keys tied on the high bits
+    need_lo = rem_hi < n_eq;
+    if (need_lo) {
+      unsigned lmin = 0xFFFFFFFFu, lmax = 0u;
+#pragma unroll
+      for (int i = 0; i < PT; ++i)
+        if (eqh[i]) {
+          lmin = min(lmin, lo[i]);
+          lmax = max(lmax, lo[i]);
+        }
+      unsigned mn2, mx2;
+      block_min_max_256(lmin, lmax, mm_tmp, &mn2, &mx2);
+      if (mn2 == mx2) {
+        T_lo = mn2;
+        rem_lo = rem_hi;
+      } else {
+        const int top_bit = 31 - __clz(mn2 ^ mx2);
+        radix_select_u32<PT>(lo, eqh, rem_hi, top_bit / 8, mn2, hist, &sh_T, &sh_rem, &T_lo, &rem_lo);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PT; ++i) eqh[i] = false;
   }
+  // ties on the full key go to the lowest block ids
+  int n_tie = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) n_tie += (need_lo && eqh[i] && lo[i] == T_lo) ? 1 : 0;
   int tot;
-  int eq_before = block_exclusive_scan_256(n_eq, scan_tmp, &tot);
+  int tie_before = block_exclusive_scan_256(n_tie, scan_tmp, &tot);
   int n_sel = 0;
-  unsigned int chosen = 0u;  // bit i: id j0+i selected
+  unsigned chosen = 0u;  // bit i: id j0+i selected
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int j = j0 + i;
@@ -193,15 +313,17 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     bool take;
     if (j == 0 || j == nb - 1) {
       take = true;
-    } else if (M == 0) {
+    } else if (!cand[i] || M == 0) {
       take = false;
-    } else if (key[i] > prefix) {
-      take = true;
-    } else if (key[i] == prefix) {
-      take = eq_before < rem;
-      ++eq_before;
+    } else if (hi[i] != T_hi) {
+      take = hi[i] > T_hi;
+    } else if (!need_lo) {
+      take = true;  // the whole bucket is needed
+    } else if (lo[i] != T_lo) {
+      take = lo[i] > T_lo;
     } else {
-      take = false;
+      take = tie_before < rem_lo;
+      ++tie_before;
     }
     if (take) {
       chosen |= 1u << i;
@@ -215,16 +337,21 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
   for (int i = tot + tid; i < k; i += 256) out[i] = -1;
 }
 
+template <int QK, int SK, int D, int G>
+void launch_bounds_one(const BoundArgs& a, hipStream_t s) {
+  constexpr int nblk = BoundShape<G>::NBLK;
+  const dim3 grid((unsigned)((a.MB + nblk - 1) / nblk), (unsigned)a.Hkv, (unsigned)a.B);
+  hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(BoundShape<G>::THREADS), 0, s, a);
+}
+
 template <int QK, int SK, int D>
 hipError_t launch_bounds_g(const BoundArgs& a, int G, hipStream_t s) {
-  const int nblk = 256 / G;
-  const dim3 grid((unsigned)((a.MB + nblk - 1) / nblk), (unsigned)a.Hkv, (unsigned)a.B);
   switch (G) {
-    case 1: hipLaunchKernelGGL((bounds_kernel<QK, SK, D, 1>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((bounds_kernel<QK, SK, D, 2>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((bounds_kernel<QK, SK, D, 4>), grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL((bounds_kernel<QK, SK, D, 8>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((bounds_kernel<QK, SK, D, 16>), grid, dim3(256), 0, s, a); break;
+    case 1: launch_bounds_one<QK, SK, D, 1>(a, s); break;
+    case 2: launch_bounds_one<QK, SK, D, 2>(a, s); break;
+    case 4: launch_bounds_one<QK, SK, D, 4>(a, s); break;
+    case 8: launch_bounds_one<QK, SK, D, 8>(a, s); break;
+    default: launch_bounds_one<QK, SK, D, 16>(a, s); break;
   }
   return hipGetLastError();
 }

@@ -1,34 +1,37 @@
 // kvs_summaries.hip -- per-block channel-wise min/max of K (the block
 // summary of page "KV 稀疏化", §5 "Quest").
 //
-// One wavefront per (sequence, KV head, block).  Lanes read the block's K
-// tile in coalesced 16-byte vectors (LPR lanes cover one token row of D
-// channels, RPI rows per wave-instruction), keep a running min/max per
-// channel in registers, then fold the RPI row groups with cross-lane
-// shuffles.  fp8 codes are decoded and multiplied by their group scale in
-// fp32 before the comparison, the same value attention uses.
+// One 256-thread workgroup per (sequence, KV head, block).  The K tile
+// (S rows x D channels) is read as 16-byte vectors, every load of a thread
+// issued before any comparison; a thread always sees the same channel chunk
+// (the vectors of a row are spread over LPR threads), so it folds its rows
+// in registers, then the row groups are folded by cross-lane shuffles and
+// the four wavefronts through LDS.  fp8 codes are decoded and multiplied by
+// their group scale in fp32 first, the same value attention uses.
 //
 // Roofline: HBM-bound streaming read of S*D*elem bytes (+ fp8 scales) per
-// block and 2*D*out_elem bytes written; no arithmetic to speak of.
+// block, 2*D*out_elem bytes written; the comparisons are negligible.
 #include "kvs_internal.h"
 
 namespace kvs {
 namespace {
 
-template <int KVK, int D>
+template <int KVK, int D, int S>
 __global__ __launch_bounds__(256) void summaries_kernel(SummArgs a) {
-  constexpr int VEC = Vec16<KVK>::N;  // elements per 16-byte load
-  constexpr int LPR = D / VEC;        // lanes per token row
-  constexpr int RPI = kWave / LPR;    // rows per wave-instruction
-  static_assert(LPR >= 1 && LPR <= kWave && (kWave % LPR) == 0, "bad row split");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int S = a.S;
+  constexpr int VEC = Vec16<KVK>::N;              // elements per 16-byte vector
+  constexpr int LPR = D / VEC;                    // vectors per token row
+  constexpr int NV = S * LPR;                     // vectors per tile
+  constexpr int NPT = (NV + 255) / 256;           // vectors per thread
+  constexpr int RSTEP = 256 / LPR;                // row stride between a thread's vectors
+  static_assert(256 % LPR == 0 && LPR <= kWave, "row split must divide the workgroup");
+  __shared__ float red[4][2][LPR][VEC];
 
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int b = blockIdx.z, g = blockIdx.y;
   int len = a.seq_lens[b];
   const int cap = a.MB * S;
   if (len < 0 || len > cap) {
-    if (lane == 0 && wave == 0 && blockIdx.x == 0 && g == 0) raise_flag(a.err, 0x1u);
+    if (tid == 0 && blockIdx.x == 0 && g == 0) raise_flag(a.err, 0x1u);
     len = len < 0 ? 0 : cap;
   }
   const int nb = (len + S - 1) / S;
@@ -36,35 +39,61 @@ __global__ __launch_bounds__(256) void summaries_kernel(SummArgs a) {
   if (first < 0) first = 0;
   const long long end_ll = (long long)first + a.num_rebuild;
   const int end = end_ll < nb ? (int)end_ll : nb;
-  const long long jl = (long long)first + (long long)blockIdx.x * 4 + wave;
-  if (jl >= end) return;
+  const long long jl = (long long)first + blockIdx.x;
+  if (jl >= end) return;  // uniform over the workgroup
   const int j = (int)jl;
-
   const int page = a.block_table[(long long)b * a.MB + j];
   if (page < 0 || page >= a.P) {
-    if (lane == 0) raise_flag(a.err, 0x2u);
+    if (tid == 0) raise_flag(a.err, 0x2u);
     return;
   }
   const int ntok = min(S, len - j * S);
   const long long tile = ((long long)page * a.Hkv + g) * S;  // first token row
-  const int col = (lane % LPR) * VEC;
-  const int r0 = lane / LPR;
+  const int col = (tid % LPR) * VEC;
+  const int r0 = tid / LPR;
+  const char* base = static_cast<const char*>(a.k_pool);
 
+  uint4 raw[NPT];
+#pragma unroll
+  for (int x = 0; x < NPT; ++x) {
+    const int row = r0 + x * RSTEP;
+    if (row < ntok) raw[x] = *reinterpret_cast<const uint4*>(base + ((tile + row) * D + col) * elem_bytes<KVK>());
+  }
+  float sc[NPT];
+  if constexpr (KVK == K_FP8) {
+    const int groups = D / a.qg;
+#pragma unroll
+    for (int x = 0; x < NPT; ++x) {
+      const int row = r0 + x * RSTEP;
+      sc[x] = row < ntok ? a.k_scales[(tile + row) * groups + col / a.qg] : 1.0f;
+    }
+  }
   float mn[VEC], mx[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) {
     mn[e] = __builtin_inff();
     mx[e] = -__builtin_inff();
   }
-  const char* base = static_cast<const char*>(a.k_pool);
-  for (int t = r0; t < ntok; t += RPI) {
-    float v[VEC];
-    Vec16<KVK>::load(base + ((tile + t) * D + col) * elem_bytes<KVK>(), v);
-    if constexpr (KVK == K_FP8) {
-      const int groups = D / a.qg;
-      const float sc = a.k_scales[(tile + t) * groups + col / a.qg];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) v[e] = v[e] * sc;
+  for (int x = 0; x < NPT; ++x) {
+    const int row = r0 + x * RSTEP;
+    if (row >= ntok) continue;
+    float v[VEC];
+    const uint32_t ws[4] = {raw[x].x, raw[x].y, raw[x].z, raw[x].w};
+    if constexpr (KVK == K_F32) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(ws[e]);
+    } else if constexpr (KVK == K_BF16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[2 * e] = bf16_lo(ws[e]);
+        v[2 * e + 1] = bf16_hi(ws[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fp8x4_to_f32(ws[e], v + 4 * e);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = v[e] * sc[x];
     }
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
@@ -72,6 +101,7 @@ __global__ __launch_bounds__(256) void summaries_kernel(SummArgs a) {
       mx[e] = fmaxf(mx[e], v[e]);
     }
   }
+  // fold the row groups inside the wavefront, then across wavefronts
 #pragma unroll
   for (int off = LPR; off < kWave; off <<= 1) {
 #pragma unroll
@@ -80,7 +110,22 @@ __global__ __launch_bounds__(256) void summaries_kernel(SummArgs a) {
       mx[e] = fmaxf(mx[e], __shfl_xor(mx[e], off));
     }
   }
-  if (lane >= LPR) return;
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      red[wave][0][lane][e] = mn[e];
+      red[wave][1][lane][e] = mx[e];
+    }
+  }
+  __syncthreads();
+  if (wave != 0 || lane >= LPR) return;
+#pragma unroll
+  for (int w = 1; w < 4; ++w)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      mn[e] = fminf(mn[e], red[w][0][lane][e]);
+      mx[e] = fmaxf(mx[e], red[w][1][lane][e]);
+    }
   const long long orow = (((long long)b * a.Hkv + g) * a.MB + j) * 2 * D;
   if constexpr (KVK == K_BF16) {
     uint16_t* o = static_cast<uint16_t*>(a.out) + orow;
@@ -104,14 +149,20 @@ __global__ __launch_bounds__(256) void summaries_kernel(SummArgs a) {
   }
 }
 
+template <int KVK, int D>
+hipError_t launch_s(const SummArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.num_rebuild, (unsigned)a.Hkv, (unsigned)a.B);
+  switch (a.S) {
+    case 16: hipLaunchKernelGGL((summaries_kernel<KVK, D, 16>), grid, dim3(256), 0, s, a); break;
+    case 32: hipLaunchKernelGGL((summaries_kernel<KVK, D, 32>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((summaries_kernel<KVK, D, 64>), grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 template <int KVK>
 hipError_t launch_d(const SummArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.num_rebuild + 3) / 4), (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.D == 64)
-    hipLaunchKernelGGL((summaries_kernel<KVK, 64>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((summaries_kernel<KVK, 128>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  return a.D == 64 ? launch_s<KVK, 64>(a, s) : launch_s<KVK, 128>(a, s);
 }
 
 }  // namespace

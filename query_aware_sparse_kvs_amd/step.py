@@ -24,7 +24,7 @@ class SparseDecodeStep:
         self.sel = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
         self.out = torch.empty((L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
         self.select_ws = torch.empty(max(kvs.kvs_select_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
-        self.attn_ws = torch.empty(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
         self.sm_scale = 1.0 / math.sqrt(L.head_dim)
 
     def new_summaries(self, device="cuda") -> torch.Tensor:
@@ -68,9 +68,8 @@ class HotBufferStep:
         self.slot_owner = torch.full((L.num_seqs, L.num_kv_heads, num_slots), -1, dtype=torch.int32, device=dev)
         self.slot_stamp = torch.full((L.num_seqs, L.num_kv_heads, num_slots), -1, dtype=torch.int64, device=dev)
         pool_dt = {kvs.KVS_F32: torch.float32, kvs.KVS_BF16: torch.bfloat16, kvs.KVS_FP8_E4M3: torch.uint8}[L.kv_dtype]
-        shape = (units * num_slots, L.block_size, L.head_dim)
-        self.hot_k = torch.zeros(shape, dtype=pool_dt, device=dev)
-        self.hot_v = torch.zeros(shape, dtype=pool_dt, device=dev)
+        self.hot_k = torch.zeros((units * num_slots, L.block_size, L.head_dim), dtype=pool_dt, device=dev)
+        self.hot_v = torch.zeros((units * num_slots, L.head_dim, L.block_size), dtype=pool_dt, device=dev)
         if L.quant_group:
             sshape = (units * num_slots, L.block_size, L.head_dim // L.quant_group)
             self.hot_ks = torch.ones(sshape, dtype=torch.float32, device=dev)
@@ -80,7 +79,7 @@ class HotBufferStep:
         self.miss_list = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
         self.miss_count = torch.empty((L.num_seqs, L.num_kv_heads), dtype=torch.int32, device=dev)
         self.out = torch.empty((L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
-        self.attn_ws = torch.empty(max(kvs.kvs_attn_workspace_size(self.hot_layout, k), 1), dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(self.hot_layout, k), 1), dtype=torch.uint8, device=dev)
         self.sm_scale = 1.0 / math.sqrt(L.head_dim)
 
     def swap_in(self, step, sel, host_k, host_v, host_ks=None, host_vs=None, stream=None):

@@ -92,7 +92,7 @@ class Problem:
     def gpu_attn(self, sel, k):
         torch, kvs, L = self.env.torch, self.env.kvs, self.L
         out = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=self.env.dev)
-        ws = torch.empty(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=self.env.dev)
+        ws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=self.env.dev)
         kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, self.inp["q"], self.inp["k_pool"],
                                    self.inp["v_pool"], self.inp["k_scales"], self.inp["v_scales"],
                                    self.inp["block_table"], self.inp["seq_lens"], sel, k,
@@ -177,6 +177,8 @@ SMALL = [
     ("bf16-s16-g16", "llama8b", {"B": 2, "L": 2050, "S": 16, "Hq": 32, "Hkv": 2, "layers": 1},
      [2050, 800], 0, 20),
     ("bf16-g1", "llama8b", {"B": 2, "L": 4000, "Hq": 4, "Hkv": 4, "layers": 1}, [4000, 3333], 1, 10),
+    ("bf16-one-split", "llama8b", {"B": 2, "L": 3000, "layers": 1}, [3000, 190], 0, 4),
+    ("fp8-one-split", "longfp8", {"B": 2, "L": 3000}, [3000, 100], 0, 3),
     ("fp8-qg32", "longfp8", {"B": 2, "L": 6000}, [6000, 2049], 2, 16),
     ("fp8-qg16-d64", "longfp8", {"B": 2, "L": 3000, "D": 64, "quant_group": 16, "S": 32}, [3000, 100], 0, 9),
 ]
