@@ -16,7 +16,12 @@ kernel (the sparse attention) timed with HIP events on its own stream, plus
 the CPU oracle's rate on a bounded sample.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu] [--cpu-steps N]
+                  [--parts P] [--no-cpu] [--cpu-steps N]
+
+--parts P cuts the batch into P slices of sequences whose kernel chains run
+concurrently on their own streams inside the step (the units never interact).
+The per-phase times in "phase_us" are whole-batch, one-chain runs of each
+phase alone.
 """
 from __future__ import annotations
 
@@ -57,6 +62,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=640)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--parts", type=int, default=1,
+                    help="batch slices run as concurrent chains within a step (1 = one chain)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=2, help="layer-steps in the CPU oracle sample")
     args = ap.parse_args(argv)
@@ -88,7 +95,7 @@ def main(argv=None) -> int:
     steps = []
     for li in range(n_layers):
         inp = synth.make_inputs(w, dev, layer=li)
-        st = SparseDecodeStep(L, w.k, dev)
+        st = SparseDecodeStep(L, w.k, dev, parts=args.parts)
         summ = st.new_summaries(dev)
         st.prefill_summaries(inp["k_pool"], inp["k_scales"], inp["block_table"], inp["seq_lens"], summ)
         newest = ((inp["seq_lens"] + w.S - 1) // w.S - 1).to(torch.int32)
@@ -116,9 +123,10 @@ def main(argv=None) -> int:
                                    st.sel, w.k, st.sm_scale, st.out, st.attn_ws)
 
     def run_step(i):
-        run_append(i)
-        run_select(i)
-        run_attn(i)
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
+               inp["seq_lens"], d["summ"], d["newest"])
 
     def capture(fn):
         """One graph over every layer instance in order (as a decoder runs its
@@ -208,7 +216,7 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "context": w.L, "block": w.S, "top_k_blocks": w.k,
                    "kv_storage": w.kv_dtype, "q_storage": w.q_dtype, "layer_instances": n_layers,
-                   "graph_replay": True},
+                   "graph_replay": True, "concurrent_batch_slices": len(steps[0].slices)},
         "phase_us": {k: round(v * 1e6, 3) for k, v in phase.items()},
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),

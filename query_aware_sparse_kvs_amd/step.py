@@ -11,21 +11,43 @@ import torch
 from . import kvs
 
 
+def split_batch(num_seqs: int, parts: int):
+    """[b0, b1) ranges of `parts` near-equal slices of the batch (empty ones dropped)."""
+    parts = max(1, min(parts, num_seqs)) if num_seqs > 0 else 1
+    bounds = [num_seqs * i // parts for i in range(parts + 1)]
+    return [(bounds[i], bounds[i + 1]) for i in range(parts) if bounds[i + 1] > bounds[i]] or [(0, 0)]
+
+
 class SparseDecodeStep:
     """One layer's decode step over a paged KV cache (page "KV 稀疏化", §5
     "Quest"): rebuild the summary of each sequence's newest block (its K row
     was just appended), score and select the top-k blocks, attend over them.
+
+    (sequence, KV head) units never interact, so with parts > 1 the batch is
+    cut into that many slices of sequences whose calls run as independent
+    chains on their own streams (joined back into the caller's stream): one
+    slice's selection and short kernels overlap another slice's attention.
+    Every slice is the same computation on its rows; results are identical.
     """
 
-    def __init__(self, layout: kvs.Layout, k: int, device="cuda"):
+    def __init__(self, layout: kvs.Layout, k: int, device="cuda", parts: int = 1):
         L = self.layout = layout
         self.k = k
         dev = torch.device(device)
         self.sel = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
         self.out = torch.empty((L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(L.head_dim)
+        self.slices = []
+        for b0, b1 in split_batch(L.num_seqs, parts):
+            Lp = kvs.Layout(b1 - b0, L.num_q_heads, L.num_kv_heads, L.head_dim, L.block_size, L.max_blocks,
+                            L.num_pages, L.q_dtype, L.kv_dtype, L.quant_group)
+            sws = torch.empty(max(kvs.kvs_select_workspace_size(Lp, k), 1), dtype=torch.uint8, device=dev)
+            aws = torch.zeros(max(kvs.kvs_attn_workspace_size(Lp, k), 1), dtype=torch.uint8, device=dev)
+            self.slices.append((b0, b1, Lp, sws, aws))
+        self.streams = [torch.cuda.Stream(device=dev) for _ in self.slices[1:]]
+        # whole-batch workspaces for the single-chain path
         self.select_ws = torch.empty(max(kvs.kvs_select_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
         self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
-        self.sm_scale = 1.0 / math.sqrt(L.head_dim)
 
     def new_summaries(self, device="cuda") -> torch.Tensor:
         L = self.layout
@@ -36,16 +58,42 @@ class SparseDecodeStep:
         kvs.kvs_build_summaries(self.layout, k_pool, k_scales, block_table, seq_lens, None,
                                 self.layout.max_blocks, summaries, stream)
 
+    def _chain(self, L, sws, aws, sl, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens,
+               summaries, newest_block, bounds_out, stream):
+        k = self.k
+        kvs.kvs_build_summaries(L, k_pool, k_scales, block_table[sl], seq_lens[sl], newest_block[sl], 1,
+                                summaries[sl], stream)
+        kvs.kvs_select_topk(L, q[sl], summaries[sl], seq_lens[sl], k, self.sel[sl],
+                            None if bounds_out is None else bounds_out[sl], sws, stream)
+        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q[sl], k_pool, v_pool, k_scales, v_scales,
+                                   block_table[sl], seq_lens[sl], self.sel[sl], k, self.sm_scale,
+                                   self.out[sl], aws, stream)
+
     def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,
             newest_block, bounds_out=None, stream=None) -> torch.Tensor:
-        """newest_block: [B] int32 device tensor, ceil(seq_len/S) - 1."""
-        L, k = self.layout, self.k
-        kvs.kvs_build_summaries(L, k_pool, k_scales, block_table, seq_lens, newest_block, 1,
-                                summaries, stream)
-        kvs.kvs_select_topk(L, q, summaries, seq_lens, k, self.sel, bounds_out, self.select_ws, stream)
-        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, k_pool, v_pool, k_scales, v_scales,
-                                   block_table, seq_lens, self.sel, k, self.sm_scale, self.out,
-                                   self.attn_ws, stream)
+        """newest_block: [B] int32 device tensor, ceil(seq_len/S) - 1.
+        stream: None (torch's current stream) or a torch.cuda.Stream."""
+        args = (q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries, newest_block,
+                bounds_out)
+        if len(self.slices) == 1:
+            self._chain(self.layout, self.select_ws, self.attn_ws, slice(None), *args, stream)
+            return self.out
+        cur = torch.cuda.current_stream() if stream is None else stream
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        joins = []
+        for i, (b0, b1, Lp, sws, aws) in enumerate(self.slices):
+            s = cur if i == 0 else self.streams[i - 1]
+            if i:
+                s.wait_event(fork)
+            with torch.cuda.stream(s):
+                self._chain(Lp, sws, aws, slice(b0, b1), *args, None)
+            if i:
+                e = torch.cuda.Event()
+                e.record(s)
+                joins.append(e)
+        for e in joins:
+            cur.wait_event(e)
         return self.out
 
 

@@ -1,13 +1,16 @@
 """A decode layer-step captured into a HIP graph gives, on every replay, the
 same results as the eager calls (the path records no memset nodes; this
-checks it with replays separated by unrelated eager work)."""
+checks it with replays separated by unrelated eager work), also when the
+batch runs as concurrent slices on several streams (fork and join inside the
+graph), which must give bit-identical results to the one-chain step."""
 import numpy as np
 import pytest
 
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager(orc):
+@pytest.mark.parametrize("parts", [1, 3])
+def test_graph_replays_match_eager(orc, parts):
     import torch
     from query_aware_sparse_kvs_amd import kvs, synth
     from query_aware_sparse_kvs_amd.step import SparseDecodeStep
@@ -17,7 +20,8 @@ def test_graph_replays_match_eager(orc):
     inp = synth.make_inputs(w, dev, seq_lens=[9000, 8191, 64, 4000])
     code = kvs.DTYPE_CODE
     L = kvs.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code[w.q_dtype], code[w.kv_dtype])
-    st = SparseDecodeStep(L, w.k, dev)
+    st = SparseDecodeStep(L, w.k, dev, parts=parts)
+    assert len(st.slices) == parts
     summ = st.new_summaries(dev)
     st.prefill_summaries(inp["k_pool"], None, inp["block_table"], inp["seq_lens"], summ)
     newest = ((inp["seq_lens"] + w.S - 1) // w.S - 1).to(torch.int32)
@@ -29,6 +33,12 @@ def test_graph_replays_match_eager(orc):
     eager_out = step().clone()
     eager_sel = st.sel.clone()
     torch.cuda.synchronize()
+    if parts > 1:  # the same kernels on the same rows: bit-identical to one chain
+        one = SparseDecodeStep(L, w.k, dev, parts=1)
+        one.run(inp["q"], inp["k_pool"], inp["v_pool"], None, None, inp["block_table"], inp["seq_lens"],
+                summ, newest)
+        torch.cuda.synchronize()
+        assert torch.equal(one.sel, eager_sel) and torch.equal(one.out, eager_out)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):

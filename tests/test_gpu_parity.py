@@ -81,18 +81,23 @@ class Problem:
                                 L.max_blocks if num_rebuild is None else num_rebuild, out)
         return out
 
-    def gpu_select(self, summ, k):
+    def gpu_select(self, summ, k, with_bounds=True):
+        """Selection, and the exact bounds W when asked (without them the
+        scores stay in the workspace)."""
         torch, kvs, L = self.env.torch, self.env.kvs, self.L
         sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=self.env.dev)
-        W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=self.env.dev)
+        W = None
+        if with_bounds:
+            W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=self.env.dev)
         ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=self.env.dev)
         kvs.kvs_select_topk(L, self.inp["q"], summ, self.inp["seq_lens"], k, sel, W, ws)
         return sel, W
 
-    def gpu_attn(self, sel, k):
+    def gpu_attn(self, sel, k, ws=None):
         torch, kvs, L = self.env.torch, self.env.kvs, self.L
         out = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=self.env.dev)
-        ws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=self.env.dev)
+        if ws is None:
+            ws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=self.env.dev)
         kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, self.inp["q"], self.inp["k_pool"],
                                    self.inp["v_pool"], self.inp["k_scales"], self.inp["v_scales"],
                                    self.inp["block_table"], self.inp["seq_lens"], sel, k,
@@ -196,6 +201,9 @@ def test_step_parity_small(env, case):
     g_sel, g_W = p.gpu_select(g_summ, k)
     no_device_errors(env)
     o_sel, ties = check_selection(p, g_sel, g_W, k)
+    f_sel, _ = p.gpu_select(g_summ, k, with_bounds=False)
+    no_device_errors(env)
+    assert np.array_equal(f_sel.cpu().numpy(), o_sel), "selection without bounds_out differs"
     g_out = p.gpu_attn(g_sel, k)
     no_device_errors(env)
     err, rel = check_attn(g_out, p.or_attn(o_sel))
@@ -263,9 +271,41 @@ def test_selection_ties_and_degenerate_queries(env):
     for k in (2, 7, 13, 38, 39, 40):
         g_sel, g_W = p.gpu_select(g_summ, k)
         no_device_errors(env)
-        check_selection(p, g_sel, g_W, k)
-    g_sel, _ = p.gpu_select(g_summ, 7)
-    assert list(g_sel[1, 0].cpu().numpy()) == [0, 1, 2, 3, 4, 5, 39]
+        o_sel, _ = check_selection(p, g_sel, g_W, k)
+        f_sel, _ = p.gpu_select(g_summ, k, with_bounds=False)
+        assert np.array_equal(f_sel.cpu().numpy(), o_sel), f"selection without bounds_out differs at k={k}"
+    for wb in (True, False):
+        g_sel, _ = p.gpu_select(g_summ, 7, with_bounds=wb)
+        assert list(g_sel[1, 0].cpu().numpy()) == [0, 1, 2, 3, 4, 5, 39]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_selection_with_many_exact_ties(env, seed):
+    """K drawn from {-1, -0.5, 0, 0.5, 1} and q from {-1, 1}: many blocks share
+    a score exactly, so the top-k threshold falls inside large groups of equal
+    scores that must be ranked by block id exactly as the plain definition
+    does."""
+    torch = env.torch
+    w = env.synth.scaled(env.synth.WORKLOADS["llama8b"], B=3, L=64 * 300, k=40, layers=1, heavy="none",
+                         seed=20 + seed)
+    p = Problem(env, w, seq_lens=[64 * 300, 64 * 300 - 7, 64 * 120])
+    g = torch.Generator(device=env.dev)
+    g.manual_seed(seed)
+    vals = torch.tensor([-1.0, -0.5, 0.0, 0.5, 1.0], device=env.dev)
+    idx = torch.randint(0, 5, p.inp["k_pool"].shape, device=env.dev, generator=g)
+    p.inp["k_pool"].copy_(vals[idx].to(torch.bfloat16))
+    qs = torch.randint(0, 2, p.inp["q"].shape, device=env.dev, generator=g) * 2 - 1
+    p.inp["q"].copy_(qs.to(torch.bfloat16))
+    p.h["k_pool"] = np_pool(p.inp["k_pool"])
+    p.h["q"] = p.inp["q"].double().cpu().numpy()
+    g_summ = p.gpu_summaries()
+    for k in (5, 40, 77):
+        g_sel, g_W = p.gpu_select(g_summ, k)
+        no_device_errors(env)
+        o_sel, _ = check_selection(p, g_sel, g_W, k)
+        f_sel, _ = p.gpu_select(g_summ, k, with_bounds=False)
+        no_device_errors(env)
+        assert np.array_equal(f_sel.cpu().numpy(), o_sel), f"selection without bounds_out differs at k={k}"
 
 
 def test_attention_padding_empty_and_partial(env):
@@ -404,6 +444,11 @@ def test_full_llama8b_layer(env):
     o_sel, ties = check_selection(p, st.sel, W, w.k)
     err, rel = check_attn(out, p.or_attn(o_sel))
     print(f"[llama8b] near-tie units {ties}; attention max|err| {err:.2e} rel L2 {rel:.2e}")
+    # the benchmark's call: no bounds requested
+    st.run(p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], None, None, p.inp["block_table"],
+           p.inp["seq_lens"], summ, newest)
+    no_device_errors(env)
+    assert np.array_equal(st.sel.cpu().numpy(), o_sel), "selection without bounds_out differs"
 
 
 def _compact(p, seqs):
@@ -452,6 +497,11 @@ def test_full_highconc_sampled(env):
     assert np.array_equal(st.sel[seqs].cpu().numpy(), o_sel)
     o_out = orc.sparse_attn(OL, q, kp, vp, None, None, new_tbl, lens, o_sel, 1 / math.sqrt(w.D))
     check_attn(out[seqs], o_out)
+    exact_sel = st.sel.clone()
+    st.run(p_inp["q"], p_inp["k_pool"], p_inp["v_pool"], None, None, p_inp["block_table"],
+           p_inp["seq_lens"], summ, newest)
+    no_device_errors(env)
+    assert torch.equal(st.sel, exact_sel), "selection without bounds_out differs"
 
 
 def test_full_longfp8_sampled(env):
