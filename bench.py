@@ -64,6 +64,11 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--parts", type=int, default=1,
                     help="batch slices run as concurrent chains within a step (1 = one chain)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer instances to rotate through (default: the workload's own count)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB five times (the reference kernel "
+                         "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-steps", type=int, default=2, help="layer-steps in the CPU oracle sample")
     args = ap.parse_args(argv)
@@ -82,13 +87,22 @@ def main(argv=None) -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
     w = synth.WORKLOADS[args.workload]
     if w.hot_slots:
         raise SystemExit("the hot-buffer workload is measured by bench_hot in tests; pick another")
     code = kvs.DTYPE_CODE
     L = kvs.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code[w.q_dtype], code[w.kv_dtype],
                    w.quant_group)
-    n_layers = w.layers
+    n_layers = args.layers if args.layers > 0 else w.layers
     print(f"[bench] workload {w.name}: building {n_layers} layer instance(s)", file=sys.stderr, flush=True)
 
     layers = []
@@ -223,13 +237,47 @@ def main(argv=None) -> int:
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "hbm", "kernel": "kvs_sparse_decode_attn (attn_mfma_kernel + merge_kernel)",
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(w.name),
                      "bytes_per_launch": by["attention"], "us_per_launch": round(attn_sec * 1e6, 3)},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall_step, 4),
     }
     print(json.dumps(result), flush=True)
     return 0
+
+
+ATTN_SOURCES = ("query_aware_sparse_kvs_amd/csrc/kvs_attn.hip", "query_aware_sparse_kvs_amd/csrc/kvs_internal.h")
+
+
+def attn_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention call (both kernels) from the counter summary in
+    profiles/, scaled by the copy-kernel calibration recorded there; None when
+    there is none for this workload or the attention sources have changed
+    since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"attention_{workload}_hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("attention_sources_sha256") != attn_source_digest():
+        return None
+    try:
+        return int(rec["hbm_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, layers, n_steps):
