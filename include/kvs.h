@@ -168,6 +168,13 @@ kvs_status kvs_build_summaries(const kvs_layout* layout, const void* k_pool,
  *  sel          [B][Hkv][k] int32 output
  *  bounds_out   optional [B][Hkv][MB] fp64 output: W, -inf for j >= nb(b)
  *  workspace    >= kvs_select_workspace_size(layout, k) bytes
+ * Two implementations give identical selections.  By default every block's W
+ * is computed in exact fp64 and a second kernel selects.  When bounds_out is
+ * NULL, q and the summaries are bf16, MB <= 2048 and B*Hkv*MB >= 65536, the
+ * blocks are instead scored on the matrix cores in fp32 together with a
+ * rigorous bound on that rounding, and only the blocks whose fp32 score lies
+ * within the bound of the top-k threshold get their W recomputed in exact
+ * fp64 to settle the ranking.
  * Errors: INVALID_ARG, UNSUPPORTED, HIP.  Device flags: KVS_DEVERR_SEQLEN.
  * ---------------------------------------------------------------------- */
 kvs_status kvs_select_topk(const kvs_layout* layout, const void* q, const void* summaries,

@@ -424,10 +424,15 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
     // ---- all loads of the tile ----
     uint4 kraw[KL], vraw[VPL][VL];
+    float ksc[KL];  // fp8: the scale of each 16-channel chunk's group, loaded with the tile
     if (t < ntok) {
 #pragma unroll
       for (int x = 0; x < KL; ++x)
         kraw[x] = *reinterpret_cast<const uint4*>(kb + ((row0 + t) * D + part * CPL + x * VEC) * EB);
+      if constexpr (KVK == K_FP8) {
+#pragma unroll
+        for (int x = 0; x < KL; ++x) ksc[x] = a.k_scales[(row0 + t) * groups + (part * CPL + x * VEC) / a.qg];
+      }
     }
 #pragma unroll
     for (int e = 0; e < VPL; ++e)
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e) fp8x4_to_f32(ws[e], kv + 4 * e);
-          const float sc = a.k_scales[(row0 + t) * groups + c / a.qg];
+          const float sc = ksc[x];
 #pragma unroll
           for (int e = 0; e < VEC; ++e) kv[e] *= sc;
         }

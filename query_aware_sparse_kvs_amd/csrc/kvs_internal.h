@@ -142,6 +142,17 @@ struct TopkArgs {
   int32_t B, Hkv, S, MB, k;
 };
 
+struct SelMfmaArgs {
+  const void* q;
+  const void* summ;
+  const int32_t* seq_lens;
+  float* w32;   // workspace [B][Hkv][MB]: fp32 scores
+  float* amag;  // workspace [B][Hkv][MB]: their error magnitudes
+  int32_t* sel;
+  unsigned int* err;
+  int32_t B, Hq, Hkv, G, D, S, MB, k;
+};
+
 struct AttnArgs {
   const void* q;
   const void* k_pool;
@@ -185,6 +196,8 @@ struct HotArgs {
 hipError_t launch_summaries(const SummArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_bounds(const BoundArgs& a, int q_kind, int summ_kind, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
+bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G);
+hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s);
 hipError_t launch_hot(const HotArgs& a, hipStream_t s);
 

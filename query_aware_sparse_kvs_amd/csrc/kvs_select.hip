@@ -3,16 +3,19 @@
 // summaries, keep the top-k; the sink block and the newest block are always
 // kept, same page §2 and "SparDA：把KV選擇提前一層…" §4.2).
 //
-// bounds_kernel: a workgroup stages 32 consecutive blocks' summaries (16 for
-// G = 16) in LDS with coalesced 16-byte loads, then runs one thread per
-// (block, query head).  The block score is
+// bounds_kernel: a 256-thread workgroup stages 64 consecutive blocks'
+// summaries in LDS with coalesced 16-byte loads; lane = block, wavefront w
+// takes query heads w, w+4, ...  The block score is
 // U = sum_c max(q_c*mn_c, q_c*mx_c); since mx_c >= mn_c the larger product is
-// q_c*mx_c when q_c >= 0 and q_c*mn_c otherwise, so each channel costs one
-// select and one fp64 fma.  Every product of a bf16/fp32 query with a
-// bf16/fp32 summary is exact in fp64, and the sum runs in ascending c, so
-// the result is bit-identical to the plain ordered fp64 sum; the max over a
-// group's G heads is taken across G adjacent lanes.  Roofline: HBM-bound read
-// of the summaries (2*D*elem bytes per block and KV head).
+// q_c*mx_c when q_c >= 0 and q_c*mn_c otherwise.  That choice depends only
+// on the head, so it is uniform over a wavefront: a per-head bit mask picks
+// mn or mx for a whole 32-bit word of summaries with one bit-field insert,
+// and the head's query sits in LDS as fp64 (broadcast reads).  Every product
+// of a bf16/fp32 query with a bf16/fp32 summary is exact in fp64 and the sum
+// runs in ascending c, so the result is bit-identical to the plain ordered
+// fp64 sum.  The group max over heads goes through LDS.  Roofline: HBM read
+// of the summaries (2*D*elem bytes per block and KV head); the fp64 chain
+// costs about four vector instructions per (block, head, channel).
 //
 // topk_kernel: one 256-thread workgroup per (sequence, KV head).  Scores are
 // mapped to order-preserving 64-bit keys.  A most-significant-digit radix
@@ -28,31 +31,26 @@
 namespace kvs {
 namespace {
 
-// Blocks per bounds workgroup and its thread count for G query heads per KV
-// head: one thread per (block, head).
-template <int G>
-struct BoundShape {
-  static constexpr int NBLK = G >= 16 ? 16 : 32;
-  static constexpr int THREADS = NBLK * G;
-};
+constexpr int kBoundBlocks = 64;  // blocks per bounds workgroup (lane = block)
 
 template <int QK, int SK, int D, int G>
-__global__ __launch_bounds__(BoundShape<G>::THREADS) void bounds_kernel(BoundArgs a) {
-  constexpr int NBLK = BoundShape<G>::NBLK;
-  constexpr int NT = BoundShape<G>::THREADS;
+__global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
+  constexpr int NB = kBoundBlocks;
   constexpr int EB = elem_bytes<SK>();
-  constexpr int ROWB = 2 * D * EB;            // bytes of one block's summary
-  constexpr int ROWP = ROWB + 16;             // padded LDS row (bank spread)
-  constexpr int NV = NBLK * ROWB / 16;        // 16-byte vectors of the chunk
-  constexpr int NPT = (NV + NT - 1) / NT;
-  constexpr int SVEC = Vec16<SK>::N;
-  __shared__ float qs[G][D + 4];
-  __shared__ __attribute__((aligned(16))) char sm[NBLK * ROWP];
+  constexpr int ROWB = 2 * D * EB;           // bytes of one block's summary
+  constexpr int ROWP = ROWB + 16;            // padded LDS row (bank spread)
+  constexpr int NV = NB * ROWB / 16;         // 16-byte vectors of the chunk
+  constexpr int NPT = NV / 256;
+  constexpr int VEC = 16 / EB;               // summary elements per 16 bytes
+  constexpr int WPR = D * EB / 4;            // 32-bit words per half row
+  __shared__ __attribute__((aligned(16))) char sm[NB * ROWP];
+  __shared__ __attribute__((aligned(16))) double qd[G][D];
+  __shared__ __attribute__((aligned(16))) uint32_t qm[G][WPR];
   const int b = blockIdx.z, g = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int j0 = blockIdx.x * NBLK;
-
-  const int nmem = min(NBLK, a.MB - j0);   // blocks of this chunk inside the array
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j0 = blockIdx.x * NB;
+  const int nmem = min(NB, a.MB - j0);  // blocks of this chunk inside the array
 
   // stage the chunk's summaries: every load issued before any use, and not
   // waiting for seq_lens (blocks past nb are read but never used)
@@ -60,11 +58,12 @@ __global__ __launch_bounds__(BoundShape<G>::THREADS) void bounds_kernel(BoundArg
   u32x4 raw[NPT];
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
-    const int v = x * NT + tid;
+    const int v = x * 256 + tid;
     raw[x] = u32x4{0u, 0u, 0u, 0u};
-    if (v < NV && v / (ROWB / 16) < nmem) raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)v * 16);
+    if (v / (ROWB / 16) < nmem) raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)v * 16);
   }
-  for (int i = tid; i < G * D; i += NT) {
+  // the query as fp64, and per head the words' choice of max (mask bits set) or min
+  for (int i = tid; i < G * D; i += 256) {
     const int h = i / D, c = i % D;
     const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
     float v;
@@ -72,7 +71,7 @@ __global__ __launch_bounds__(BoundShape<G>::THREADS) void bounds_kernel(BoundArg
       v = static_cast<const float*>(a.q)[qi];
     else
       v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
-    qs[h][c] = v;
+    qd[h][c] = (double)v;
   }
   int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
@@ -81,45 +80,79 @@ __global__ __launch_bounds__(BoundShape<G>::THREADS) void bounds_kernel(BoundArg
     len = len < 0 ? 0 : cap;
   }
   const int nb = (len + a.S - 1) / a.S;
-  const int nvalid = min(NBLK, nb - j0);  // blocks of this chunk below nb (may be <= 0)
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
-    const int v = x * NT + tid;
-    if (v < NV && v / (ROWB / 16) < nmem) {
+    const int v = x * 256 + tid;
+    if (v / (ROWB / 16) < nmem) {
       const int blk = v / (ROWB / 16), off = (v % (ROWB / 16)) * 16;
       *reinterpret_cast<u32x4*>(sm + blk * ROWP + off) = raw[x];
     }
   }
   __syncthreads();
+  for (int i = tid; i < G * WPR; i += 256) {
+    const int h = i / WPR, w = i % WPR;
+    uint32_t m;
+    if constexpr (EB == 2)
+      m = (qd[h][2 * w] >= 0.0 ? 0x0000FFFFu : 0u) | (qd[h][2 * w + 1] >= 0.0 ? 0xFFFF0000u : 0u);
+    else
+      m = qd[h][w] >= 0.0 ? 0xFFFFFFFFu : 0u;
+    qm[h][w] = m;
+  }
+  __syncthreads();
 
-  const int h = tid % G, blk = tid / G;
-  const int j = j0 + blk;
-  double acc = -__builtin_inf();
-  if (blk < nvalid) {
-    acc = 0.0;
-    const char* pmn = sm + blk * ROWP;
-    const char* pmx = pmn + D * EB;
-#pragma unroll 4
-    for (int c0 = 0; c0 < D; c0 += SVEC) {
-      float mn[SVEC], mx[SVEC];
-      Vec16<SK>::load(pmn + c0 * EB, mn);
-      Vec16<SK>::load(pmx + c0 * EB, mx);
+  constexpr int HPW = (G + 3) / 4;  // heads per wavefront
+  const bool valid = j0 + lane < nb;
+  double acc[HPW];
 #pragma unroll
-      for (int e = 0; e < SVEC; ++e) {
-        const float qc = qs[h][c0 + e];
-        const float x = qc >= 0.0f ? mx[e] : mn[e];
-        acc = __builtin_fma((double)qc, (double)x, acc);
+  for (int i = 0; i < HPW; ++i) acc[i] = 0.0;
+  const char* pmn = sm + lane * ROWP;
+  const char* pmx = pmn + D * EB;
+  if (wave < G) {
+#pragma unroll 1
+    for (int c0 = 0; c0 < D; c0 += VEC) {
+      const u32x4 vmn = *reinterpret_cast<const u32x4*>(pmn + c0 * EB);
+      const u32x4 vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
+#pragma unroll
+      for (int i = 0; i < HPW; ++i) {
+        const int h = wave + 4 * i;
+        if (h >= G) break;
+        const u32x4 m = *reinterpret_cast<const u32x4*>(&qm[h][c0 * EB / 4]);
+        const u32x4 x = (vmx & m) | (vmn & ~m);
+        float xf[VEC];
+        if constexpr (EB == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            xf[2 * e] = bf16_lo(x[e]);
+            xf[2 * e + 1] = bf16_hi(x[e]);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(x[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[i] = __builtin_fma(qd[h][c0 + e], (double)xf[e], acc[i]);
       }
     }
   }
-  double w = acc;
+  __syncthreads();  // the staged rows are no longer needed: reuse them for the group max
+  double* ured = reinterpret_cast<double*>(sm);  // [G][NB]
 #pragma unroll
-  for (int off = 1; off < G; off <<= 1) {
-    const double o = __shfl_xor(w, off);
-    w = o > w ? o : w;
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + 4 * i;
+    if (h < G) ured[h * NB + lane] = acc[i];
   }
-  if (h == 0 && j < a.MB) {
-    const long long wi = ((long long)b * a.Hkv + g) * a.MB + j;
+  __syncthreads();
+  if (wave == 0 && lane < nmem) {
+    double w = -__builtin_inf();
+    if (valid) {
+      w = ured[lane];
+#pragma unroll
+      for (int h = 1; h < G; ++h) {
+        const double o = ured[h * NB + lane];
+        w = o > w ? o : w;
+      }
+    }
+    const long long wi = ((long long)b * a.Hkv + g) * a.MB + j0 + lane;
     a.W[wi] = w;
     if (a.bounds_out) a.bounds_out[wi] = w;
   }
@@ -339,9 +372,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 template <int QK, int SK, int D, int G>
 void launch_bounds_one(const BoundArgs& a, hipStream_t s) {
-  constexpr int nblk = BoundShape<G>::NBLK;
-  const dim3 grid((unsigned)((a.MB + nblk - 1) / nblk), (unsigned)a.Hkv, (unsigned)a.B);
-  hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(BoundShape<G>::THREADS), 0, s, a);
+  const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks), (unsigned)a.Hkv, (unsigned)a.B);
+  hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(256), 0, s, a);
 }
 
 template <int QK, int SK, int D>

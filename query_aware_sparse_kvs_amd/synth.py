@@ -25,7 +25,9 @@ Shapes of the five workloads, with the reading of each recipe:
                 N(0,1) with one outlier channel per KV head (ceil(0.5 % of
                 128)) scaled x8, then stored as OCP E4M3FN codes with one fp32
                 scale per 32 channels of a token (scale = absmax / 448, 1 for
-                an all-zero group; round to nearest even, saturated); bf16 q.
+                an all-zero group; round to nearest even, saturated); bf16 q;
+                16 layer instances (a step reads only 48 MiB, so fewer would
+                fit in the 256 MB last-level cache).
 
 The pages speak of large models (an 8B model with 32 layers, 4 KV heads and
 head dim 128; GLM-5.1-FP8 at 32K+8K tokens and 256 requests).  Their weights
@@ -87,7 +89,7 @@ WORKLOADS = {
                        q_dtype="bf16", kv_dtype="bf16", layers=32, heavy="scattered",
                        heavy_frac=0.02, heavy_scale=4.0, hot_slots=128, drift=13, seed=4),
     "longfp8": Workload("longfp8", B=4, Hq=32, Hkv=4, D=128, S=64, L=131072, k=64,
-                        q_dtype="bf16", kv_dtype="e4m3", quant_group=32,
+                        q_dtype="bf16", kv_dtype="e4m3", quant_group=32, layers=16,
                         outlier_channels=1, outlier_mult=8.0, seed=5),
 }
 

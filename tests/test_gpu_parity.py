@@ -308,6 +308,41 @@ def test_selection_with_many_exact_ties(env, seed):
         assert np.array_equal(f_sel.cpu().numpy(), o_sel), f"selection without bounds_out differs at k={k}"
 
 
+@pytest.mark.parametrize("kind", ["heavy", "ties", "zero_q"])
+def test_matrix_core_selection_matches_oracle(env, kind):
+    """At 8 x 4 x 2048 blocks, kvs_select_topk without bounds_out scores on the
+    matrix cores in fp32 and refines near the threshold in exact fp64; its
+    selection must equal the plain definition's, also for large groups of
+    exactly equal scores and for all-zero queries."""
+    torch, orc = env.torch, env.orc
+    heavy = "scattered" if kind == "heavy" else "none"
+    w = env.synth.scaled(env.synth.WORKLOADS["llama8b"], B=8, L=64 * 300, k=40, layers=1, heavy=heavy,
+                         seed=31)
+    lens = [64 * 300, 64 * 300 - 7, 64 * 120, 64 * 41 + 5, 64 * 300, 64 * 2, 64 * 40, 64 * 299 + 1]
+    p = Problem(env, w, seq_lens=lens, max_blocks=2048)
+    assert p.L.num_seqs * p.L.num_kv_heads * p.L.max_blocks >= 65536
+    if kind == "ties":
+        g = torch.Generator(device=env.dev)
+        g.manual_seed(7)
+        vals = torch.tensor([-1.0, -0.5, 0.0, 0.5, 1.0], device=env.dev)
+        idx = torch.randint(0, 5, p.inp["k_pool"].shape, device=env.dev, generator=g)
+        p.inp["k_pool"].copy_(vals[idx].to(torch.bfloat16))
+        qs = torch.randint(0, 2, p.inp["q"].shape, device=env.dev, generator=g) * 2 - 1
+        p.inp["q"].copy_(qs.to(torch.bfloat16))
+        p.h["k_pool"] = np_pool(p.inp["k_pool"])
+    if kind == "zero_q":
+        p.inp["q"][1].zero_()
+        p.inp["q"][4, : 2 * w.G].zero_()  # two KV heads' groups of sequence 4
+    p.h["q"] = p.inp["q"].double().cpu().numpy()
+    g_summ = p.gpu_summaries()
+    W = p.or_bounds(p.or_summaries())
+    for k in (2, 5, 40, 77):
+        f_sel, _ = p.gpu_select(g_summ, k, with_bounds=False)
+        no_device_errors(env)
+        o_sel = orc.select(p.OL, W, p.h["lens"], k)
+        assert np.array_equal(f_sel.cpu().numpy(), o_sel), f"selection differs at k={k}"
+
+
 def test_attention_padding_empty_and_partial(env):
     torch = env.torch
     w = env.synth.scaled(env.synth.WORKLOADS["llama8b"], B=4, L=1000, layers=1)
