@@ -28,10 +28,11 @@
 //           hi = bf16(p) and lo = bf16(p - hi), two MFMAs, so the product
 //           keeps ~16 bits of P.  No LDS traffic inside the tile loop.
 //   A wavefront resolves its pages (selection -> table) for all of them at
-//   once into LDS, then issues every load of a page (32 KiB of K and V)
-//   before its arithmetic.  One page per wavefront and short-lived
-//   workgroups: the workgroups that start as others finish keep the memory
-//   system busy while earlier ones compute.
+//   once into LDS, then streams them through a two-stage software pipeline:
+//   the next page's K is requested as soon as the current page's scores are
+//   computed, its V as soon as the current value product is, so about one
+//   page (32 KiB of K and V at S = 64, d = 128) stays in flight per
+//   wavefront.
 // attn_valu_kernel (fp32, fp8, and bf16 with S = 16): lane = token for the
 //   scores (64/S lanes split a token's channels), lane = channel pair for the
 //   values, probabilities broadcast through LDS; every K/V load of a tile is
@@ -44,11 +45,20 @@ namespace kvs {
 namespace {
 
 constexpr int kGMax = 16;
+constexpr int kComputeUnits = 256;  // MI355X
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// A wavefront-uniform 64-bit value held in scalar registers.
+__device__ __forceinline__ long long uniform64(long long v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)v);
+  const int hi = __builtin_amdgcn_readfirstlane((int)((unsigned long long)v >> 32));
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
 
 // Reads an input that no kernel of the call writes, at a wavefront-uniform
 // address, through the constant address space: the compiler then issues a
@@ -96,105 +106,128 @@ __device__ __forceinline__ int clamp_len(const AttnArgs& a, int b, bool flag_it)
 // MFMA kernel (bf16)
 // ---------------------------------------------------------------------------
 
-// One 32-token sub-tile of a page: its K rows and V^T columns, and how many
-// of its tokens are valid (0 = nothing to do).
-struct SubTile {
-  const uint16_t* k;  // first K row of the sub-tile, [32][D] with row stride D
-  const uint16_t* v;  // V^T tile base + token offset, [D][S] with row stride S
-  int ntok;
+// The K and V registers of one page in the MFMA layouts.  K: for each
+// 32-token sub-tile h and row group tg, 16 token rows x 32 channels per
+// k-step (A operand of the score product).  V: for each sub-tile, 16
+// channels x 32 tokens per channel tile (A operand of the value product).
+template <int D, int S>
+struct PageK {
+  u32x4 r[S / 32][2][D / 32];
+};
+template <int D, int S>
+struct PageV {
+  u32x4 r[S / 32][D / 16];
 };
 
+// kt: the page's K tile [S][D]; vt: its V tile [D][S].
 template <int D, int S>
-struct MfmaRegs {
-  static constexpr int CS = D / 32;  // k-steps of the score product
-  static constexpr int CT = D / 16;  // channel tiles of the value product
-  uint4 kr[2][CS];                   // two 16-token row groups
-  uint4 vr[CT];                      // one 32-token k-step
-};
-
+__device__ __forceinline__ void load_page_k(const uint16_t* kt, int r, int j4, PageK<D, S>& K) {
+#pragma unroll
+  for (int h = 0; h < S / 32; ++h)
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      // tau(tg, r): the token row lane-row r of group tg stands for
+      const int row = h * 32 + 8 * (r >> 2) + 4 * tg + (r & 3);
+#pragma unroll
+      for (int cs = 0; cs < D / 32; ++cs)
+        K.r[h][tg][cs] = *reinterpret_cast<const u32x4*>(kt + row * D + cs * 32 + 8 * j4);
+    }
+}
 template <int D, int S>
-__device__ __forceinline__ void load_subtile(const SubTile& t, int r, int j4, MfmaRegs<D, S>& R) {
-  constexpr int CS = D / 32, CT = D / 16;
+__device__ __forceinline__ void load_page_v(const uint16_t* vt, int r, int j4, PageV<D, S>& V) {
 #pragma unroll
-  for (int tg = 0; tg < 2; ++tg) {
-    // tau(tg, r): the token row lane-row r of group tg stands for
-    const int row = 8 * (r >> 2) + 4 * tg + (r & 3);
+  for (int h = 0; h < S / 32; ++h)
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) R.kr[tg][cs] = *reinterpret_cast<const uint4*>(t.k + row * D + cs * 32 + 8 * j4);
-  }
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) R.vr[ct] = *reinterpret_cast<const uint4*>(t.v + (ct * 16 + r) * S + 8 * j4);
+    for (int ct = 0; ct < D / 16; ++ct)
+      V.r[h][ct] = *reinterpret_cast<const u32x4*>(vt + (ct * 16 + r) * S + h * 32 + 8 * j4);
 }
 
+// Scores of one page (ntok valid tokens, possibly 0), the online-softmax
+// update of (m_run, l_run, o), and the P^T operands of the value product:
+// lane (r, j4) holds tokens h*32 + 8*j4 + 4*tg + e of head r, which are
+// exactly the 8 tokens it supplies to the value product of sub-tile h
+// (slots 0..3 <- tg 0, 4..7 <- tg 1).  P = hi + lo, both bf16.
 template <int D, int S>
-__device__ __forceinline__ void compute_subtile(const SubTile& t, int j4, MfmaRegs<D, S>& R, const bf16x8_t* qf,
-                                                float q_scale, float& m_run, float& l_run, f32x4_t* o) {
-  constexpr int CS = D / 32, CT = D / 16;
-  // scores: lane (r, j4) receives tokens 8*j4 + 4*tg + e of head r
-  f32x4_t sc[2];
-#pragma unroll
-  for (int tg = 0; tg < 2; ++tg) {
-    sc[tg] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int cs = 0; cs < CS; ++cs)
-      sc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.kr[tg][cs]), qf[cs], sc[tg], 0, 0, 0);
-  }
-  float s[2][4];
+__device__ __forceinline__ void page_scores(const PageK<D, S>& K, const bf16x8_t* qf, float q_scale, int ntok, int j4,
+                                            float& m_run, float& l_run, f32x4_t* o, bf16x8_t* ph, bf16x8_t* pl) {
+  constexpr int NSUB = S / 32, CS = D / 32, CT = D / 16;
+  float s[NSUB][2][4];
   float tmax = -__builtin_inff();
 #pragma unroll
-  for (int tg = 0; tg < 2; ++tg)
+  for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int tok = 8 * j4 + 4 * tg + e;
-      const float v = tok < t.ntok ? sc[tg][e] * q_scale : -__builtin_inff();
-      s[tg][e] = v;
-      tmax = fmaxf(tmax, v);
+    for (int tg = 0; tg < 2; ++tg) {
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(K.r[h][tg][cs]), qf[cs], sc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = h * 32 + 8 * j4 + 4 * tg + e;
+        const float v = tok < ntok ? sc[e] * q_scale : -__builtin_inff();
+        s[h][tg][e] = v;
+        tmax = fmaxf(tmax, v);
+      }
     }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const float m_new = fmaxf(m_run, tmax);
-  const float alpha = exp2f(m_run - m_new);
+  // nothing valid so far (m_new = -inf): leave everything as it is
+  const float alpha = m_new == -__builtin_inff() ? 1.0f : exp2f(m_run - m_new);
   float psum = 0.0f;
 #pragma unroll
-  for (int tg = 0; tg < 2; ++tg)
+  for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      s[tg][e] = exp2f(s[tg][e] - m_new);
-      psum += s[tg][e];
-    }
+    for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = s[h][tg][e];
+        const float p = v == -__builtin_inff() ? 0.0f : exp2f(v - m_new);
+        s[h][tg][e] = p;
+        psum += p;
+      }
   psum += __shfl_xor(psum, 16);
   psum += __shfl_xor(psum, 32);
   l_run = l_run * alpha + psum;
   m_run = m_new;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
-  // P^T operand: slots 0..3 <- row group 0, slots 4..7 <- row group 1
-  bf16x8_t ph, pl;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float pv = e < 4 ? s[0][e] : s[1][e - 4];
-    const __bf16 hb = static_cast<__bf16>(pv);
-    ph[e] = hb;
-    pl[e] = static_cast<__bf16>(pv - static_cast<float>(hb));
-  }
-  if (t.ntok < 32) {  // token positions past the sequence may hold anything: zero them
-    const int t0 = 8 * j4;
-    uint32_t keep[4];
+  for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      keep[w] = (t0 + 2 * w < t.ntok ? 0x0000FFFFu : 0u) | (t0 + 2 * w + 1 < t.ntok ? 0xFFFF0000u : 0u);
+    for (int e = 0; e < 8; ++e) {
+      const float pv = e < 4 ? s[h][0][e] : s[h][1][e - 4];
+      const __bf16 hb = static_cast<__bf16>(pv);
+      ph[h][e] = hb;
+      pl[h][e] = static_cast<__bf16>(pv - static_cast<float>(hb));
+    }
+}
+
+// The value product of one page: o += V^T P^T, with V zeroed at token
+// positions >= ntok (they may hold anything).
+template <int D, int S>
+__device__ __forceinline__ void page_values(PageV<D, S>& V, int ntok, int j4, const bf16x8_t* ph, const bf16x8_t* pl,
+                                            f32x4_t* o) {
+  constexpr int NSUB = S / 32, CT = D / 16;
+#pragma unroll
+  for (int h = 0; h < NSUB; ++h) {
+    const int nt = ntok - h * 32;
+    if (nt < 32) {
+      const int t0 = 8 * j4;
+      uint32_t keep[4];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        keep[w] = (t0 + 2 * w < nt ? 0x0000FFFFu : 0u) | (t0 + 2 * w + 1 < nt ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) V.r[h][ct][w] &= keep[w];
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      R.vr[ct].x &= keep[0];
-      R.vr[ct].y &= keep[1];
-      R.vr[ct].z &= keep[2];
-      R.vr[ct].w &= keep[3];
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(V.r[h][ct]), ph[h], o[ct], 0, 0, 0);
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(V.r[h][ct]), pl[h], o[ct], 0, 0, 0);
     }
-  }
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) {
-    o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.vr[ct]), ph, o[ct], 0, 0, 0);
-    o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(R.vr[ct]), pl, o[ct], 0, 0, 0);
   }
 }
 
@@ -277,28 +310,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
 
+  // a software pipeline over the wavefront's pages: K of the next page is
+  // requested as soon as this page's scores are done, V as soon as its
+  // value product is; the last page requests itself again (cache hits), so
+  // every iteration issues the same loads and the waits stay exact
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
     resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
-    // whole pages, one register buffer: all loads of a page, then its math
+    PageK<D, S> K;
+    PageV<D, S> V;
+    {
+      const long long tile = uniform64(wl_tile[wave][0]);
+      load_page_k<D, S>(kpool + tile * S * D, r, j4, K);
+      load_page_v<D, S>(vpool + tile * D * S, r, j4, V);
+    }
     for (int tt = 0; tt < nt; ++tt) {
-      const long long tile = wl_tile[wave][tt];
-      const int ntok = wl_ntok[wave][tt];
-      if (ntok <= 0) continue;
-      MfmaRegs<D, S> rr[NSUB];
-      SubTile st[NSUB];
-#pragma unroll
-      for (int h = 0; h < NSUB; ++h) {
-        st[h].k = kpool + (tile * S + h * 32) * D;
-        st[h].v = vpool + tile * D * S + h * 32;
-        st[h].ntok = max(0, min(32, ntok - h * 32));
-        load_subtile<D, S>(st[h], r, j4, rr[h]);
-      }
-      // keep every load of the page ahead of its arithmetic
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int h = 0; h < NSUB; ++h)
-        if (st[h].ntok > 0) compute_subtile<D, S>(st[h], j4, rr[h], qf, a.q_scale, m_run, l_run, o);
+      const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
+      const long long tnext = uniform64(wl_tile[wave][min(tt + 1, nt - 1)]);
+      bf16x8_t ph[NSUB], pl[NSUB];
+      page_scores<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, ph, pl);
+      load_page_k<D, S>(kpool + tnext * S * D, r, j4, K);
+      page_values<D, S>(V, ntok, j4, ph, pl, o);
+      load_page_v<D, S>(vpool + tnext * D * S, r, j4, V);
     }
   }
 
@@ -717,12 +750,16 @@ hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 int attn_num_splits(int units, int k) {
-  // one selected page per wavefront (4 per workgroup), while the grid stays
-  // within 8192 workgroups; beyond that a wavefront takes several pages
-  const int by_k = (k + 3) / 4;
-  int cap = 8192 / (units > 0 ? units : 1);
-  if (cap < 1) cap = 1;
-  const int n = by_k < cap ? by_k : cap;
+  // As few splits as still give about one workgroup per compute unit: each
+  // wavefront then streams the most pages through its pipeline, and the
+  // split partials to merge are fewest (one split writes the output).
+  // Measured on the 8 x 4 unit, k = 128 shape: 2/4/6/8 pages per wavefront
+  // take 37.0/33.5/36.2/44.4 us; on 256 x 4, k = 32: 4 pages 221 us, 8 pages
+  // (one split) 199 us.
+  if (units < 1) units = 1;
+  const int by_k = (k + 3) / 4;  // at least one page per wavefront
+  const int want = (kComputeUnits + units - 1) / units;
+  const int n = by_k < want ? by_k : want;
   return n < 1 ? 1 : n;
 }
 
