@@ -312,8 +312,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
 
   // a software pipeline over the wavefront's pages: K of the next page is
   // requested as soon as this page's scores are done, V as soon as its
-  // value product is; the last page requests itself again (cache hits), so
-  // every iteration issues the same loads and the waits stay exact
+  // value product is.  Every iteration issues the same loads, so the waits
+  // stay exact; after the last page the request goes to the pool's first
+  // tile of this KV head, which every workgroup of the head shares and the
+  // caches keep (no HBM traffic)
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
     resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
     for (int tt = 0; tt < nt; ++tt) {
       const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
-      const long long tnext = uniform64(wl_tile[wave][min(tt + 1, nt - 1)]);
+      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : g));
       bf16x8_t ph[NSUB], pl[NSUB];
       page_scores<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, ph, pl);
       load_page_k<D, S>(kpool + tnext * S * D, r, j4, K);
