@@ -268,6 +268,65 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int32_t* 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The end of an MFMA-kernel workgroup: merges the four wavefronts' running
+// (max, sum, acc) in LDS; lane (r, j4) holds channels ct*16 + 4*j4 + e of
+// head r.  One split: the normalised output row is written; otherwise the
+// split partial.
+template <int D>
+__device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, int split, int wave, int r, int j4,
+                                               float m_run, float l_run, const f32x4_t* o, float (*mg_m)[16],
+                                               float (*mg_l)[16], float (*mg_o)[16][D + 4]) {
+  constexpr int CT = D / 16;
+  const int G = a.G;
+  if (j4 == 0) {
+    mg_m[wave][r] = m_run;
+    mg_l[wave][r] = l_run;
+  }
+  if (wave > 0) {
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mg_o[wave - 1][r][ct * 16 + 4 * j4 + e] = o[ct][e];
+  }
+  __syncthreads();
+  if (wave == 0 && r < G) {
+    float M = mg_m[0][r];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w][r]);
+    float scw[4], L = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float mw = mg_m[w][r];
+      scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
+      L += mg_l[w][r] * scw[w];
+    }
+    // one split: normalise and write the output row; else store the partial
+    const bool direct = a.nsplit == 1;
+    const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+    const long long hrow = (long long)b * a.Hq + (long long)g * G + r;
+    const long long pi = hrow * a.nsplit + split;
+    if (!direct && j4 == 0) {
+      a.part_m[pi] = M;
+      a.part_l[pi] = L;
+    }
+    float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      float4 v;
+      float* pv = reinterpret_cast<float*>(&v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = ct * 16 + 4 * j4 + e;
+        float x = o[ct][e] * scw[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) x += mg_o[w - 1][r][c] * scw[w];
+        pv[e] = x * inv;
+      }
+      *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = v;
+    }
+  }
+}
+
 template <int D, int S>
 __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CS = D / 32;  // k-steps of the score product
@@ -337,61 +396,277 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // merge the four wavefronts: lane (r, j4) holds channels ct*16 + 4*j4 + e
-  if (j4 == 0) {
-    mg_m[wave][r] = m_run;
-    mg_l[wave][r] = l_run;
+  wg_merge_write<D>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel for fp8 K/V (bf16 q)
+// ---------------------------------------------------------------------------
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// Eight fp8 codes -> eight floats (exact).
+__device__ __forceinline__ void fp8x8_to_f32(u32x2 w, float* out) {
+  fp8x4_to_f32(w.x, out);
+  fp8x4_to_f32(w.y, out + 4);
+}
+// Eight floats that are bf16 values (low 16 bits zero) -> bf16x8.
+__device__ __forceinline__ bf16x8_t pack_bf16_exact(const float* f) {
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (__float_as_uint(f[2 * i + 1]) & 0xFFFF0000u) | (__float_as_uint(f[2 * i]) >> 16);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+// Eight floats -> hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
+__device__ __forceinline__ void split_bf16(const float* f, bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = static_cast<__bf16>(f[e]);
+    hi[e] = h;
+    lo[e] = static_cast<__bf16>(f[e] - static_cast<float>(h));
   }
-  if (wave > 0) {
+}
+
+// K of one page: 8 codes of one token row per (sub-tile h, row group tg,
+// k-step cs), in the A layout of the score product, and each one's scale.
+template <int D, int S>
+struct PageK8 {
+  u32x2 k[S / 32][2][D / 32];
+  float ks[S / 32][2][D / 32];
+};
+// V of one page: 8 codes (8 tokens of one channel) per (h, channel tile ct),
+// in the A layout of the value product, and this lane's share of the page's
+// V scales [S][groups] (at most 8 groups).
+template <int D, int S>
+struct PageV8 {
+  u32x2 v[S / 32][D / 16];
+  float vs[S * 8 / kWave];
+};
+
+template <int D, int S>
+__device__ __forceinline__ void load_page_k8(const uint8_t* kt, const float* kst, int groups, const int* kgrp, int r,
+                                             int j4, PageK8<D, S>& K) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+  for (int h = 0; h < S / 32; ++h)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) mg_o[wave - 1][r][ct * 16 + 4 * j4 + e] = o[ct][e];
+    for (int tg = 0; tg < 2; ++tg) {
+      const int row = h * 32 + 8 * (r >> 2) + 4 * tg + (r & 3);  // tau(tg, r)
+#pragma unroll
+      for (int cs = 0; cs < D / 32; ++cs) {
+        K.k[h][tg][cs] = *reinterpret_cast<const u32x2*>(kt + row * D + cs * 32 + 8 * j4);
+        K.ks[h][tg][cs] = kst[row * groups + kgrp[cs]];
+      }
+    }
+}
+template <int D, int S>
+__device__ __forceinline__ void load_page_v8(const uint8_t* vt, const float* vst, int groups, int r, int j4,
+                                             int lane, PageV8<D, S>& V) {
+#pragma unroll
+  for (int h = 0; h < S / 32; ++h)
+#pragma unroll
+    for (int ct = 0; ct < D / 16; ++ct)
+      V.v[h][ct] = *reinterpret_cast<const u32x2*>(vt + (ct * 16 + r) * S + h * 32 + 8 * j4);
+#pragma unroll
+  for (int y = 0; y < S * 8 / kWave; ++y) {
+    const int x = y * kWave + lane;
+    V.vs[y] = x < S * groups ? vst[x] : 0.0f;
   }
-  __syncthreads();
-  if (wave == 0 && r < G) {
-    float M = mg_m[0][r];
+}
+
+// Scores of one page.  K = fp32(decode(code) * scale) is split into two bf16
+// (hi + lo) for the matrix product, so the scores keep ~16 bits of K.
+// Returns the probabilities of this lane's 8 tokens per sub-tile (tokens
+// h*32 + 8*j4 + e, the slots it supplies to the value product).
+template <int D, int S>
+__device__ __forceinline__ void page_scores8(const PageK8<D, S>& K, const bf16x8_t* qf, float q_scale, int ntok,
+                                             int j4, float& m_run, float& l_run, f32x4_t* o, float (*pf)[8]) {
+  constexpr int NSUB = S / 32, CS = D / 32, CT = D / 16;
+  float s[NSUB][2][4];
+  float tmax = -__builtin_inff();
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w][r]);
-    float scw[4], L = 0.0f;
+  for (int h = 0; h < NSUB; ++h)
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float mw = mg_m[w][r];
-      scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
-      L += mg_l[w][r] * scw[w];
-    }
-    // one split: normalise and write the output row; else store the partial
-    const bool direct = a.nsplit == 1;
-    const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
-    const long long hrow = (long long)b * a.Hq + (long long)g * G + r;
-    const long long pi = hrow * a.nsplit + split;
-    if (!direct && j4 == 0) {
-      a.part_m[pi] = M;
-      a.part_l[pi] = L;
-    }
-    float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
+    for (int tg = 0; tg < 2; ++tg) {
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      float4 v;
-      float* pv = reinterpret_cast<float*>(&v);
+      for (int cs = 0; cs < CS; ++cs) {
+        float x[8];
+        fp8x8_to_f32(K.k[h][tg][cs], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] *= K.ks[h][tg][cs];
+        bf16x8_t hi, lo;
+        split_bf16(x, hi, lo);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, qf[cs], sc, 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, qf[cs], sc, 0, 0, 0);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int c = ct * 16 + 4 * j4 + e;
-        float x = o[ct][e] * scw[0];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) x += mg_o[w - 1][r][c] * scw[w];
-        pv[e] = x * inv;
+        const int tok = h * 32 + 8 * j4 + 4 * tg + e;
+        const float v = tok < ntok ? sc[e] * q_scale : -__builtin_inff();
+        s[h][tg][e] = v;
+        tmax = fmaxf(tmax, v);
       }
-      *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = v;
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(m_run, tmax);
+  const float alpha = m_new == -__builtin_inff() ? 1.0f : exp2f(m_run - m_new);
+  float psum = 0.0f;
+#pragma unroll
+  for (int h = 0; h < NSUB; ++h)
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = s[h][tg][e];
+        const float p = v == -__builtin_inff() ? 0.0f : exp2f(v - m_new);
+        pf[h][4 * tg + e] = p;
+        psum += p;
+      }
+  psum += __shfl_xor(psum, 16);
+  psum += __shfl_xor(psum, 32);
+  l_run = l_run * alpha + psum;
+  m_run = m_new;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+}
+
+// The value product of one page: V codes decode exactly to bf16; the V scale
+// of (token, channel group) is folded into P per group (P' = p * scale,
+// split hi + lo).  vsl: this page's V scales in LDS as [group][S].
+template <int D, int S>
+__device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, int j4, const float (*pf)[8],
+                                             const float* vsl, const int* ctgrp, f32x4_t* o) {
+  constexpr int NSUB = S / 32, CT = D / 16;
+#pragma unroll
+  for (int h = 0; h < NSUB; ++h) {
+    const int nt = ntok - h * 32;
+    const int t0 = 8 * j4;
+    uint32_t keep[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      keep[w] = (t0 + 2 * w < nt ? 0x0000FFFFu : 0u) | (t0 + 2 * w + 1 < nt ? 0xFFFF0000u : 0u);
+    bf16x8_t phi, plo;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      if (ct == 0 || ctgrp[ct] != ctgrp[ct - 1]) {  // uniform: a new channel group
+        const float* vg = vsl + ctgrp[ct] * S + h * 32 + t0;
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(vg);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(vg + 4);
+        float pp[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pp[e] = pf[h][e] * s0[e];
+          pp[4 + e] = pf[h][4 + e] * s1[e];
+        }
+        split_bf16(pp, phi, plo);
+      }
+      float x[8];
+      fp8x8_to_f32(V.v[h][ct], x);
+      bf16x8_t a = pack_bf16_exact(x);
+      u32x4 aw = __builtin_bit_cast(u32x4, a);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) aw[w] &= keep[w];  // positions past the sequence may hold anything
+      a = __builtin_bit_cast(bf16x8_t, aw);
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, o[ct], 0, 0, 0);
+      o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, o[ct], 0, 0, 0);
     }
   }
+}
+
+template <int D, int S>
+__global__ __launch_bounds__(256, 2) void attn_mfma8_kernel(AttnArgs a) {
+  constexpr int CS = D / 32;
+  constexpr int CT = D / 16;
+  constexpr int NSUB = S / 32;
+  __shared__ float mg_m[4][16], mg_l[4][16];
+  __shared__ float mg_o[3][16][D + 4];
+  __shared__ long long wl_tile[4][64];
+  __shared__ int wl_ntok[4][64];
+  __shared__ __attribute__((aligned(16))) float vsl[4][S * 8];  // per wavefront: [group][S]
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r = lane & 15, j4 = lane >> 4;
+  const int G = a.G;
+  const int groups = D / a.qg;  // 1, 2, 4 or 8 (qg >= 16)
+  const int gshift = __builtin_ctz(groups);
+  int kgrp[CS], ctgrp[CT];
+#pragma unroll
+  for (int cs = 0; cs < CS; ++cs) kgrp[cs] = (cs * 32 + 8 * j4) / a.qg;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) ctgrp[ct] = __builtin_amdgcn_readfirstlane((ct * 16) / a.qg);
+
+  bf16x8_t qf[CS];  // B operand of the score product: Q^T, column r = query head g*G + r
+  {
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + r) * D;
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (r < G) v = *reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4);
+      qf[cs] = as_bf16x8(v);
+    }
+  }
+  const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
+  const int nb = (len + S - 1) / S;
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4_t o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
+  const int i0 = split * a.bps + wave;
+  const int i1 = min(split * a.bps + a.bps, a.k);
+  const int ntiles = i0 < i1 ? (i1 - i0 + 3) / 4 : 0;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
+  float* vw = vsl[wave];
+
+  // the same two-stage page pipeline as the bf16 kernel
+  for (int t0 = 0; t0 < ntiles; t0 += 64) {
+    resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
+    const int nt = min(64, ntiles - t0);
+    PageK8<D, S> K;
+    PageV8<D, S> V;
+    {
+      const long long tile = uniform64(wl_tile[wave][0]);
+      load_page_k8<D, S>(kpool + tile * S * D, a.k_scales + tile * S * groups, groups, kgrp, r, j4, K);
+      load_page_v8<D, S>(vpool + tile * D * S, a.v_scales + tile * S * groups, groups, r, j4, lane, V);
+    }
+    for (int tt = 0; tt < nt; ++tt) {
+      const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
+      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : g));
+      float pf[NSUB][8];
+      page_scores8<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, pf);
+      load_page_k8<D, S>(kpool + tnext * S * D, a.k_scales + tnext * S * groups, groups, kgrp, r, j4, K);
+      // this page's V scales -> LDS as [group][S]
+#pragma unroll
+      for (int y = 0; y < S * 8 / kWave; ++y) {
+        const int x = y * kWave + lane;
+        if (x < S * groups) vw[(x & (groups - 1)) * S + (x >> gshift)] = V.vs[y];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      page_values8<D, S>(V, ntok, j4, pf, vw, ctgrp, o);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      load_page_v8<D, S>(vpool + tnext * D * S, a.v_scales + tnext * S * groups, groups, r, j4, lane, V);
+    }
+  }
+  wg_merge_write<D>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
 }
 
 // ---------------------------------------------------------------------------
 // VALU kernel (fp32, fp8, bf16 with 16-token blocks)
 // ---------------------------------------------------------------------------
 
-template <int QK, int KVK, int D, int S>
+// GM: an upper bound on G (8 or 16) that sizes the per-head register arrays.
+template <int QK, int KVK, int D, int S, int GM>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   constexpr int LPT = kWave / S;  // lanes per token in the score phase
   constexpr int CPL = D / LPT;    // channels per lane in the score phase
@@ -416,23 +691,35 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
 
-  for (int i = tid; i < G * D; i += 256) {
-    const int h = i / D, c = i % D;
-    const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
-    float v;
-    if constexpr (QK == K_F32)
-      v = static_cast<const float*>(a.q)[qi];
-    else
-      v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
-    qs[i] = v * a.q_scale;
+  // the group's query rows (G*D contiguous values): a fixed-trip loop, so
+  // every load is issued before the first one is waited for
+  {
+    const long long q0 = ((long long)b * a.Hq + (long long)g * G) * D;
+    float qv[(GM * D + 255) / 256];
+#pragma unroll
+    for (int x = 0; x < (GM * D + 255) / 256; ++x) {
+      const int i = x * 256 + tid;
+      qv[x] = 0.0f;
+      if (i < G * D) {
+        if constexpr (QK == K_F32)
+          qv[x] = static_cast<const float*>(a.q)[q0 + i];
+        else
+          qv[x] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[q0 + i] << 16);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < (GM * D + 255) / 256; ++x) {
+      const int i = x * 256 + tid;
+      if (i < G * D) qs[i] = qv[x] * a.q_scale;
+    }
   }
   __syncthreads();
   const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
   const int nb = (len + S - 1) / S;
 
-  float m_run[kGMax], l_run[kGMax], acc[kGMax][VPL];
+  float m_run[GM], l_run[GM], acc[GM][VPL];
 #pragma unroll
-  for (int h = 0; h < kGMax; ++h) {
+  for (int h = 0; h < GM; ++h) {
     m_run[h] = -__builtin_inff();
     l_run[h] = 0.0f;
 #pragma unroll
@@ -448,6 +735,12 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   const char* kb = static_cast<const char*>(a.k_pool);
   const char* vb = static_cast<const char*>(a.v_pool);
   const int c0 = lane * VPL;  // value-phase channels of this lane
+  // the scale groups of this lane's channels, computed once (no division in the loops)
+  int vgrp[VPL], kgrp[KL];
+#pragma unroll
+  for (int e = 0; e < VPL; ++e) vgrp[e] = KVK == K_FP8 ? (c0 + e) / a.qg : 0;
+#pragma unroll
+  for (int x = 0; x < KL; ++x) kgrp[x] = KVK == K_FP8 ? (part * CPL + x * VEC) / a.qg : 0;
 
   for (int i = i0 + wave; i < i1; i += 4) {
     int j = 0;
@@ -466,7 +759,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
         kraw[x] = *reinterpret_cast<const uint4*>(kb + ((row0 + t) * D + part * CPL + x * VEC) * EB);
       if constexpr (KVK == K_FP8) {
 #pragma unroll
-        for (int x = 0; x < KL; ++x) ksc[x] = a.k_scales[(row0 + t) * groups + (part * CPL + x * VEC) / a.qg];
+        for (int x = 0; x < KL; ++x) ksc[x] = a.k_scales[(row0 + t) * groups + kgrp[x]];
       }
     }
 #pragma unroll
@@ -475,13 +768,24 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
       for (int x = 0; x < VL; ++x)
         vraw[e][x] = *reinterpret_cast<const uint4*>(vb + ((tile * D + c0 + e) * S) * EB + x * 16);
     if constexpr (KVK == K_FP8) {
-      for (int x = lane; x < S * groups; x += kWave) vw[x] = a.v_scales[row0 * groups + x];
+      // at most 8 groups per token: a fixed-trip loop, all loads in flight together
+      float vsv[S * 8 / kWave];
+#pragma unroll
+      for (int y = 0; y < S * 8 / kWave; ++y) {
+        const int x = y * kWave + lane;
+        vsv[y] = x < S * groups ? a.v_scales[row0 * groups + x] : 0.0f;
+      }
+#pragma unroll
+      for (int y = 0; y < S * 8 / kWave; ++y) {
+        const int x = y * kWave + lane;
+        if (x < S * groups) vw[x] = vsv[y];
+      }
     }
 
     // ---- scores (lane = token) ----
-    float dot[kGMax];
+    float dot[GM];
 #pragma unroll
-    for (int h = 0; h < kGMax; ++h) dot[h] = 0.0f;
+    for (int h = 0; h < GM; ++h) dot[h] = 0.0f;
     if (t < ntok) {
 #pragma unroll
       for (int x = 0; x < KL; ++x) {
@@ -505,7 +809,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
           for (int e = 0; e < VEC; ++e) kv[e] *= sc;
         }
 #pragma unroll
-        for (int h = 0; h < kGMax; ++h) {
+        for (int h = 0; h < GM; ++h) {
           if (h < G) {
 #pragma unroll
             for (int e = 0; e < VEC; e += 4) {
@@ -517,7 +821,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int h = 0; h < kGMax; ++h) {
+    for (int h = 0; h < GM; ++h) {
       if (h < G) {
 #pragma unroll
         for (int off = S; off < kWave; off <<= 1) dot[h] += __shfl_xor(dot[h], off);
@@ -525,7 +829,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     }
     // ---- online softmax (base 2) ----
 #pragma unroll
-    for (int h = 0; h < kGMax; ++h) {
+    for (int h = 0; h < GM; ++h) {
       if (h < G) {
         const float s = t < ntok ? dot[h] : -__builtin_inff();
         const float mt = wave_max(s);
@@ -568,12 +872,12 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           float vv = v[e][q];
-          if constexpr (KVK == K_FP8) vv *= vw[(tt + q) * groups + (c0 + e) / a.qg];
+          if constexpr (KVK == K_FP8) vv *= vw[(tt + q) * groups + vgrp[e]];
           v[e][q] = tt + q < ntok ? vv : 0.0f;
         }
       }
 #pragma unroll
-      for (int h = 0; h < kGMax; ++h) {
+      for (int h = 0; h < GM; ++h) {
         if (h < G) {
           const float4 p4 = *reinterpret_cast<const float4*>(pw + h * S + tt);
 #pragma unroll
@@ -594,7 +898,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   }
   if (wave > 0) {
 #pragma unroll
-    for (int h = 0; h < kGMax; ++h)
+    for (int h = 0; h < GM; ++h)
       if (h < G)
 #pragma unroll
         for (int e = 0; e < VPL; ++e) mg_acc[((wave - 1) * G + h) * D + c0 + e] = acc[h][e];
@@ -603,7 +907,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   if (wave == 0) {
     const bool direct = a.nsplit == 1;
 #pragma unroll
-    for (int h = 0; h < kGMax; ++h) {
+    for (int h = 0; h < GM; ++h) {
       if (h >= G) continue;
       float M = mg_m[h];
 #pragma unroll
@@ -725,17 +1029,35 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   *reinterpret_cast<float4*>(a.out + row * D + c) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
+template <int QK, int KVK, int D, int GM>
+void launch_valu_s(const AttnArgs& a, size_t lds, hipStream_t st) {
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
+  switch (a.S) {
+    case 16: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 16, GM>), grid, dim3(256), lds, st, a); break;
+    case 32: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 32, GM>), grid, dim3(256), lds, st, a); break;
+    default: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 64, GM>), grid, dim3(256), lds, st, a); break;
+  }
+}
+
 template <int QK, int KVK, int D>
 hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
-  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
   const int groups = KVK == K_FP8 ? D / a.qg : 1;
   const size_t lds = sizeof(float) * ((size_t)a.G * D + 4 * (size_t)a.G * a.S + 4 * (size_t)a.S * groups +
                                       8 * (size_t)a.G + 3 * (size_t)a.G * D);
-  switch (a.S) {
-    case 16: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 16>), grid, dim3(256), lds, st, a); break;
-    case 32: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 32>), grid, dim3(256), lds, st, a); break;
-    default: hipLaunchKernelGGL((attn_valu_kernel<QK, KVK, D, 64>), grid, dim3(256), lds, st, a); break;
-  }
+  if (a.G <= 8)
+    launch_valu_s<QK, KVK, D, 8>(a, lds, st);
+  else
+    launch_valu_s<QK, KVK, D, kGMax>(a, lds, st);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma8(const AttnArgs& a, hipStream_t st) {
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
+  if (a.S == 32)
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -772,6 +1094,8 @@ hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s
     e = a.D == 64 ? launch_mfma<64>(a, st) : launch_mfma<128>(a, st);
   else if (q_kind == K_F32 && kv_kind == K_F32)
     e = a.D == 64 ? launch_valu<K_F32, K_F32, 64>(a, st) : launch_valu<K_F32, K_F32, 128>(a, st);
+  else if (q_kind == K_BF16 && kv_kind == K_FP8 && a.S >= 32)
+    e = a.D == 64 ? launch_mfma8<64>(a, st) : launch_mfma8<128>(a, st);
   else if (q_kind == K_BF16 && kv_kind == K_BF16)
     e = a.D == 64 ? launch_valu<K_BF16, K_BF16, 64>(a, st) : launch_valu<K_BF16, K_BF16, 128>(a, st);
   else
