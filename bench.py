@@ -70,7 +70,7 @@ def main(argv=None) -> int:
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-steps", type=int, default=2, help="layer-steps in the CPU oracle sample")
+    ap.add_argument("--cpu-steps", type=int, default=6, help="layer-steps in the CPU oracle sample (about 2 s each)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
