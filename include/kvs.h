@@ -183,6 +183,32 @@ kvs_status kvs_select_topk(const kvs_layout* layout, const void* q, const void* 
                            void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_select_topk_append -- kvs_select_topk for a decode step whose newest
+ * token has just been appended to the K pool: also rebuilds the summary of
+ * every sequence's newest block nb(b)-1 from K (as kvs_build_summaries with
+ * first_block = nb(b)-1 and num_rebuild = 1 would).
+ *
+ * Same computation as kvs_build_summaries followed by kvs_select_topk; the
+ * newest block is always selected, so its score never decides the
+ * selection.  With bf16 K and bounds_out NULL the rebuild runs as one more
+ * workgroup per (sequence, KV head) of the scoring launch, beside the
+ * workgroups that score the other blocks (the newest block's own score then
+ * uses its summary before or after the rebuild; it is not used).  Otherwise
+ * (fp32/fp8 K, or bounds_out requested) the summary is rebuilt first, so
+ * bounds_out matches the plain definition on the rebuilt summaries.
+ *
+ *  k_pool, k_scales, block_table   as for kvs_build_summaries
+ *  summaries    in/out, as written by kvs_build_summaries
+ *  others       as for kvs_select_topk
+ * Errors: as kvs_select_topk and kvs_build_summaries.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_select_topk_append(const kvs_layout* layout, const void* q, const void* k_pool,
+                                  const float* k_scales, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* summaries, int32_t k, int32_t* sel,
+                                  double* bounds_out, void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_sparse_decode_attn -- attention over the selected blocks only
  *
  * Page "KV 稀疏化", §5 "Quest" (third step: full attention on the selected

@@ -217,9 +217,17 @@ kvs_status kvs_build_summaries(const kvs_layout* L, const void* k_pool, const fl
                     "summaries launch");
 }
 
-kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summaries,
-                           const int32_t* seq_lens, int32_t k, int32_t* sel, double* bounds_out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// kvs_select_topk's checks and launches; with `app`, each sequence's newest
+// block summary is also rebuilt from K -- by one more workgroup per
+// (sequence, KV head) inside the scoring launch when no bounds are returned,
+// else by a summaries launch before scoring.
+kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries, const int32_t* seq_lens, int32_t k,
+                       int32_t* sel, double* bounds_out, void* workspace, size_t workspace_bytes, void* stream,
+                       const kvs::SummArgs* app) {
   kvs_status st = check_layout(L, true);
   if (st != KVS_OK) return st;
   if (!q || !summaries || !seq_lens || !sel)
@@ -234,6 +242,17 @@ kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summa
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int summ_kind = L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32;
   const int G = L->num_q_heads / L->num_kv_heads;
+  kvs::SummArgs ap{};
+  bool fuse = false;
+  if (app) {
+    ap = *app;
+    ap.err = err;
+    fuse = !bounds_out;
+    if (!fuse) {  // bounds must see the new summary: rebuild it first
+      hipError_t e = kvs::launch_summaries(ap, kind_of(L->kv_dtype), s);
+      if (e != hipSuccess) return hip_status(e, "summaries launch");
+    }
+  }
   // Two implementations with identical selections.  The exact one spends a
   // fixed amount of fp64 arithmetic per (block, head, channel); the
   // matrix-core one streams the summaries at memory speed but pays a longer
@@ -259,6 +278,8 @@ kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summa
     ma.S = L->block_size;
     ma.MB = L->max_blocks;
     ma.k = k;
+    ma.append = fuse ? 1 : 0;
+    ma.app = ap;
     return hip_status(kvs::launch_select_mfma(ma, s), "select launch");
   }
   kvs::BoundArgs ba{};
@@ -274,6 +295,9 @@ kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summa
   ba.D = L->head_dim;
   ba.S = L->block_size;
   ba.MB = L->max_blocks;
+  ba.append = fuse ? 1 : 0;
+  ba.app_kv = kind_of(L->kv_dtype);
+  ba.app = ap;
   hipError_t e = kvs::launch_bounds(ba, kind_of(L->q_dtype), summ_kind, s);
   if (e != hipSuccess) return hip_status(e, "bounds launch");
   kvs::TopkArgs ta{};
@@ -286,6 +310,44 @@ kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summa
   ta.MB = L->max_blocks;
   ta.k = k;
   return hip_status(kvs::launch_topk(ta, s), "top-k launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summaries,
+                           const int32_t* seq_lens, int32_t k, int32_t* sel, double* bounds_out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr);
+}
+
+kvs_status kvs_select_topk_append(const kvs_layout* L, const void* q, const void* k_pool, const float* k_scales,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* summaries,
+                                  int32_t k, int32_t* sel, double* bounds_out, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  kvs_status st = check_layout(L, true);
+  if (st != KVS_OK) return st;
+  if (!k_pool || !block_table) return fail(KVS_ERR_INVALID_ARG, "k_pool and block_table must be non-NULL");
+  if (L->kv_dtype == KVS_FP8_E4M3 && !k_scales) return fail(KVS_ERR_INVALID_ARG, "fp8 K needs k_scales");
+  if (!aligned(k_pool, 16)) return fail(KVS_ERR_INVALID_ARG, "k_pool must be 16-byte aligned");
+  kvs::SummArgs ap{};
+  ap.k_pool = k_pool;
+  ap.k_scales = k_scales;
+  ap.block_table = block_table;
+  ap.seq_lens = seq_lens;
+  ap.first_block = nullptr;
+  ap.out = summaries;
+  ap.B = L->num_seqs;
+  ap.Hkv = L->num_kv_heads;
+  ap.D = L->head_dim;
+  ap.S = L->block_size;
+  ap.MB = L->max_blocks;
+  ap.P = L->num_pages;
+  ap.qg = L->quant_group;
+  ap.num_rebuild = 1;
+  ap.newest = 1;
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, &ap);
 }
 
 kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const void* q,

@@ -123,6 +123,7 @@ struct SummArgs {
   void* out;
   unsigned int* err;
   int32_t B, Hkv, D, S, MB, P, qg, num_rebuild;
+  int32_t newest;  // 1: rebuild block nb(b)-1 of every sequence (first_block unused)
 };
 
 struct BoundArgs {
@@ -133,6 +134,9 @@ struct BoundArgs {
   double* bounds_out;  // optional copy
   unsigned int* err;
   int32_t B, Hq, Hkv, D, S, MB;
+  int32_t append;      // 1: one more workgroup per (b, g) rebuilds the newest block's summary
+  int32_t app_kv;      // K storage kind of that rebuild (Kind; bf16 with bf16 summaries)
+  SummArgs app;
 };
 
 struct TopkArgs {
@@ -151,6 +155,8 @@ struct SelMfmaArgs {
   int32_t* sel;
   unsigned int* err;
   int32_t B, Hq, Hkv, G, D, S, MB, k;
+  int32_t append;  // as in BoundArgs
+  SummArgs app;
 };
 
 struct AttnArgs {

@@ -26,7 +26,7 @@
 // the tied keys.  Ties on the full key go to the lowest block ids, the
 // (W desc, id asc) order.  A block-wide prefix sum writes the chosen ids in
 // ascending order.  Latency-bound.
-#include "kvs_internal.h"
+#include "kvs_summarize.h"
 
 namespace kvs {
 namespace {
@@ -47,6 +47,18 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   __shared__ __attribute__((aligned(16))) double qd[G][D];
   __shared__ __attribute__((aligned(16))) uint32_t qm[G][WPR];
   const int b = blockIdx.z, g = blockIdx.y;
+  if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
+    static_assert(sizeof(sm) >= kSummRed<D> * sizeof(float), "summary reduction fits the chunk buffer");
+    float* red = reinterpret_cast<float*>(sm);
+    if constexpr (SK == K_BF16) {
+      rebuild_newest_summary<K_BF16, D>(a.app, b, g, red);
+    } else if (a.app_kv == K_FP8) {
+      rebuild_newest_summary<K_FP8, D>(a.app, b, g, red);
+    } else {
+      rebuild_newest_summary<K_F32, D>(a.app, b, g, red);
+    }
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = blockIdx.x * NB;
@@ -372,7 +384,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 template <int QK, int SK, int D, int G>
 void launch_bounds_one(const BoundArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks), (unsigned)a.Hkv, (unsigned)a.B);
+  const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks + (a.append ? 1 : 0)), (unsigned)a.Hkv,
+                  (unsigned)a.B);
   hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(256), 0, s, a);
 }
 

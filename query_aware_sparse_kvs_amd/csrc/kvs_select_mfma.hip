@@ -25,7 +25,7 @@
 // -- fp64, ascending channels, the sum of the plain definition -- one thread
 // per (block, head), and are ranked by (W desc, id asc) for the places left.
 // The selection therefore equals the one the exact scores give.
-#include "kvs_internal.h"
+#include "kvs_summarize.h"
 
 namespace kvs {
 namespace {
@@ -92,6 +92,11 @@ __global__ __launch_bounds__(256, 4) void scores32_kernel(SelMfmaArgs a) {
   constexpr int HC = D / 32;  // 32-channel chunks per summary half
   constexpr int KC = 2 * HC;  // chunks of the [max | min] row
   const int g = blockIdx.y, b = blockIdx.z;
+  if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
+    __shared__ float red[kSummRed<D>];
+    rebuild_newest_summary<K_BF16, D>(a.app, b, g, red);
+    return;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j4 = lane >> 4;
@@ -442,7 +447,7 @@ bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G) {
 
 hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  const dim3 g1((unsigned)((a.MB + 63) / 64), (unsigned)a.Hkv, (unsigned)a.B);
+  const dim3 g1((unsigned)((a.MB + 63) / 64 + (a.append ? 1 : 0)), (unsigned)a.Hkv, (unsigned)a.B);
   const dim3 g2((unsigned)a.Hkv, (unsigned)a.B);
   if (a.D == 64) {
     hipLaunchKernelGGL(scores32_kernel<64>, g1, dim3(256), 0, s, a);

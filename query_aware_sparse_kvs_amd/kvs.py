@@ -75,6 +75,7 @@ def _load():
     sigs = {
         "kvs_build_summaries": (i32, [LP, P, P, P, P, P, i32, P, P]),
         "kvs_select_topk": (i32, [LP, P, P, P, i32, P, P, P, sz, P]),
+        "kvs_select_topk_append": (i32, [LP, P, P, P, P, P, P, i32, P, P, P, sz, P]),
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
         "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvs_select_workspace_size": (sz, [LP, i32]),
@@ -92,7 +93,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
+EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
 
@@ -172,6 +173,27 @@ def kvs_select_topk(layout: Layout, q, summaries, seq_lens, k: int, sel, bounds_
         _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
         ws, workspace.numel() if workspace is not None else 0,
         _stream(stream)), "kvs_select_topk")
+
+
+def kvs_select_topk_append(layout: Layout, q, k_pool, k_scales, block_table, seq_lens, summaries, k: int,
+                           sel, bounds_out, workspace, stream=None) -> None:
+    L = layout
+    tile = L.num_kv_heads * L.block_size * L.head_dim
+    qg = L.quant_group
+    ws = _ptr(workspace, "workspace", torch.uint8)
+    _check(_lib.kvs_select_topk_append(
+        ctypes.byref(L.c()),
+        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(k_pool, "k_pool", _pool_dtype(L), L.num_pages * tile),
+        _ptr(k_scales, "k_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(block_table, "block_table", torch.int32, L.num_seqs * L.max_blocks),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
+        int(k),
+        _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
+        _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
+        ws, workspace.numel() if workspace is not None else 0,
+        _stream(stream)), "kvs_select_topk_append")
 
 
 def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,

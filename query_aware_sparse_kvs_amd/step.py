@@ -21,7 +21,8 @@ def split_batch(num_seqs: int, parts: int):
 class SparseDecodeStep:
     """One layer's decode step over a paged KV cache (page "KV 稀疏化", §5
     "Quest"): rebuild the summary of each sequence's newest block (its K row
-    was just appended), score and select the top-k blocks, attend over them.
+    was just appended) while scoring and selecting the top-k blocks, then
+    attend over them.
 
     (sequence, KV head) units never interact, so with parts > 1 the batch is
     cut into that many slices of sequences whose calls run as independent
@@ -59,22 +60,19 @@ class SparseDecodeStep:
                                 self.layout.max_blocks, summaries, stream)
 
     def _chain(self, L, sws, aws, sl, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens,
-               summaries, newest_block, bounds_out, stream):
+               summaries, bounds_out, stream):
         k = self.k
-        kvs.kvs_build_summaries(L, k_pool, k_scales, block_table[sl], seq_lens[sl], newest_block[sl], 1,
-                                summaries[sl], stream)
-        kvs.kvs_select_topk(L, q[sl], summaries[sl], seq_lens[sl], k, self.sel[sl],
-                            None if bounds_out is None else bounds_out[sl], sws, stream)
+        kvs.kvs_select_topk_append(L, q[sl], k_pool, k_scales, block_table[sl], seq_lens[sl], summaries[sl], k,
+                                   self.sel[sl], None if bounds_out is None else bounds_out[sl], sws, stream)
         kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q[sl], k_pool, v_pool, k_scales, v_scales,
                                    block_table[sl], seq_lens[sl], self.sel[sl], k, self.sm_scale,
                                    self.out[sl], aws, stream)
 
     def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,
-            newest_block, bounds_out=None, stream=None) -> torch.Tensor:
-        """newest_block: [B] int32 device tensor, ceil(seq_len/S) - 1.
+            bounds_out=None, stream=None) -> torch.Tensor:
+        """summaries: in/out, every block but the newest already summarised.
         stream: None (torch's current stream) or a torch.cuda.Stream."""
-        args = (q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries, newest_block,
-                bounds_out)
+        args = (q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries, bounds_out)
         if len(self.slices) == 1:
             self._chain(self.layout, self.select_ws, self.attn_ws, slice(None), *args, stream)
             return self.out

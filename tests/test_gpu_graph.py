@@ -24,11 +24,10 @@ def test_graph_replays_match_eager(orc, parts):
     assert len(st.slices) == parts
     summ = st.new_summaries(dev)
     st.prefill_summaries(inp["k_pool"], None, inp["block_table"], inp["seq_lens"], summ)
-    newest = ((inp["seq_lens"] + w.S - 1) // w.S - 1).to(torch.int32)
 
     def step():
         return st.run(inp["q"], inp["k_pool"], inp["v_pool"], None, None, inp["block_table"],
-                      inp["seq_lens"], summ, newest)
+                      inp["seq_lens"], summ)
 
     eager_out = step().clone()
     eager_sel = st.sel.clone()
@@ -36,7 +35,7 @@ def test_graph_replays_match_eager(orc, parts):
     if parts > 1:  # the same kernels on the same rows: bit-identical to one chain
         one = SparseDecodeStep(L, w.k, dev, parts=1)
         one.run(inp["q"], inp["k_pool"], inp["v_pool"], None, None, inp["block_table"], inp["seq_lens"],
-                summ, newest)
+                summ)
         torch.cuda.synchronize()
         assert torch.equal(one.sel, eager_sel) and torch.equal(one.out, eager_out)
     side = torch.cuda.Stream()

@@ -225,6 +225,57 @@ def test_summaries_append_mode_touches_only_the_newest_block(env):
         assert np.isnan(q[b, :, : nb - 1]).all() and np.isnan(q[b, :, nb:]).all()
 
 
+APPEND = [
+    # (name, workload, overrides, seq_lens, max_blocks (None: fitted), k, bounds)
+    ("bf16-fused", "llama8b", {"B": 4, "L": 5000, "layers": 1}, [5000, 4097, 65, 1], None, 16, False),
+    ("bf16-bounds", "llama8b", {"B": 4, "L": 5000, "layers": 1}, [5000, 4097, 65, 1], None, 16, True),
+    ("bf16-s32-d64-fused", "llama8b", {"B": 2, "L": 3000, "S": 32, "D": 64, "Hq": 16, "layers": 1},
+     [3000, 1111], None, 12, False),
+    ("bf16-s16-fused", "llama8b", {"B": 2, "L": 2050, "S": 16, "Hq": 32, "Hkv": 2, "layers": 1},
+     [2050, 800], None, 20, False),
+    ("bf16-matrix-core-fused", "llama8b", {"B": 8, "L": 64 * 300, "layers": 1},
+     [64 * 300, 64 * 300 - 7, 64 * 120, 64 * 41 + 5, 64 * 300, 64 * 2, 64 * 40, 64 * 299 + 1], 2048, 40, False),
+    ("f32", "tiny", {"B": 3, "L": 1000}, [1000, 17, 513], None, 8, False),
+    ("fp8", "longfp8", {"B": 2, "L": 6000}, [6000, 2049], None, 16, False),
+    ("fp8-qg16-d64-s32", "longfp8", {"B": 2, "L": 3000, "D": 64, "quant_group": 16, "S": 32}, [3000, 100],
+     None, 9, False),
+    ("fp8-bounds", "longfp8", {"B": 2, "L": 6000}, [6000, 2049], None, 16, True),
+]
+
+
+@pytest.mark.parametrize("case", APPEND, ids=[c[0] for c in APPEND])
+def test_select_append_rebuilds_newest_summary(env, case):
+    """kvs_select_topk_append on summaries whose newest block is stale: the
+    newest block's summary comes out as the oracle's, every other byte of the
+    summary tensor is left as it was, and the selection (and bounds, when
+    asked) equal the plain definition's on the rebuilt summaries."""
+    name, base, over, lens, mb, k, with_bounds = case
+    torch, kvs = env.torch, env.kvs
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    p = Problem(env, w, seq_lens=lens, max_blocks=mb if mb else w.nb + 2, extra_pages=3)
+    L = p.L
+    print(f"[append {name}] units {L.num_seqs * L.num_kv_heads} max_blocks {L.max_blocks} k={k}", flush=True)
+    full = p.gpu_summaries()
+    summ = full.clone()
+    stale_newest(summ, p.inp["seq_lens"], w.S)
+    sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+    W = None
+    if with_bounds:
+        W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=env.dev)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    kvs.kvs_select_topk_append(L, p.inp["q"], p.inp["k_pool"], p.inp["k_scales"], p.inp["block_table"],
+                               p.inp["seq_lens"], summ, k, sel, W, ws)
+    no_device_errors(env)
+    bits = torch.int16 if summ.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(summ.view(bits), full.view(bits)), "summary tensor differs from a full rebuild"
+    check_summaries(p, summ, p.or_summaries())
+    if with_bounds:
+        check_selection(p, sel, W, k)
+    else:
+        o_sel = env.orc.select(p.OL, p.or_bounds(p.or_summaries()), p.h["lens"], k)
+        assert np.array_equal(sel.cpu().numpy(), o_sel), "selection differs"
+
+
 def test_fp8_decode_covers_every_code(env):
     """Blocks whose tokens repeat one row: min = max = the row, so every
     finite E4M3FN code and its scaled value shows up in the summaries."""
@@ -460,6 +511,15 @@ def test_hot_buffer_steps_match_oracle(env, kind):
 # the benchmark workloads at full size (sampled where the oracle needs it)
 # ---------------------------------------------------------------------------
 
+def stale_newest(summ, seq_lens, S):
+    """Overwrite each sequence's newest block summary with junk, as if its
+    K row had just been appended: the step must rebuild it."""
+    nbs = ((seq_lens.cpu() + S - 1) // S - 1).tolist()
+    for b, j in enumerate(nbs):
+        if j >= 0:
+            summ[b, :, j] = 7.0
+
+
 def test_full_llama8b_layer(env):
     """32K context, 8 sequences, k = 128 of 512: whole layer against the
     oracle (one layer instance, as the benchmark runs it)."""
@@ -470,19 +530,21 @@ def test_full_llama8b_layer(env):
     st = SparseDecodeStep(p.L, w.k, env.dev)
     summ = st.new_summaries(env.dev)
     st.prefill_summaries(p.inp["k_pool"], None, p.inp["block_table"], p.inp["seq_lens"], summ)
-    newest = torch.full((w.B,), w.nb - 1, dtype=torch.int32, device=env.dev)
+    stale_newest(summ, p.inp["seq_lens"], w.S)
     W = torch.empty((w.B, w.Hkv, w.nb), dtype=torch.float64, device=env.dev)
     out = st.run(p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], None, None, p.inp["block_table"],
-                 p.inp["seq_lens"], summ, newest, bounds_out=W)
+                 p.inp["seq_lens"], summ, bounds_out=W)
     no_device_errors(env)
     check_summaries(p, summ, p.or_summaries())
     o_sel, ties = check_selection(p, st.sel, W, w.k)
     err, rel = check_attn(out, p.or_attn(o_sel))
     print(f"[llama8b] near-tie units {ties}; attention max|err| {err:.2e} rel L2 {rel:.2e}")
-    # the benchmark's call: no bounds requested
+    # the benchmark's call: no bounds requested, the rebuild fused into scoring
+    stale_newest(summ, p.inp["seq_lens"], w.S)
     st.run(p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], None, None, p.inp["block_table"],
-           p.inp["seq_lens"], summ, newest)
+           p.inp["seq_lens"], summ)
     no_device_errors(env)
+    check_summaries(p, summ, p.or_summaries())
     assert np.array_equal(st.sel.cpu().numpy(), o_sel), "selection without bounds_out differs"
 
 
@@ -511,10 +573,10 @@ def test_full_highconc_sampled(env):
     st = SparseDecodeStep(L, w.k, env.dev)
     summ = st.new_summaries(env.dev)
     st.prefill_summaries(p_inp["k_pool"], None, p_inp["block_table"], p_inp["seq_lens"], summ)
-    newest = torch.full((w.B,), w.nb - 1, dtype=torch.int32, device=env.dev)
+    stale_newest(summ, p_inp["seq_lens"], w.S)
     W = torch.empty((w.B, w.Hkv, w.nb), dtype=torch.float64, device=env.dev)
     out = st.run(p_inp["q"], p_inp["k_pool"], p_inp["v_pool"], None, None, p_inp["block_table"],
-                 p_inp["seq_lens"], summ, newest, bounds_out=W)
+                 p_inp["seq_lens"], summ, bounds_out=W)
     no_device_errors(env)
     seqs = [0, 77, 160, 255]
     tbl = p_inp["block_table"][seqs].long()
@@ -533,9 +595,12 @@ def test_full_highconc_sampled(env):
     o_out = orc.sparse_attn(OL, q, kp, vp, None, None, new_tbl, lens, o_sel, 1 / math.sqrt(w.D))
     check_attn(out[seqs], o_out)
     exact_sel = st.sel.clone()
+    exact_summ = summ.clone()
+    stale_newest(summ, p_inp["seq_lens"], w.S)
     st.run(p_inp["q"], p_inp["k_pool"], p_inp["v_pool"], None, None, p_inp["block_table"],
-           p_inp["seq_lens"], summ, newest)
+           p_inp["seq_lens"], summ)
     no_device_errors(env)
+    assert torch.equal(summ, exact_summ), "fused newest-block rebuild differs"
     assert torch.equal(st.sel, exact_sel), "selection without bounds_out differs"
 
 
@@ -549,10 +614,10 @@ def test_full_longfp8_sampled(env):
     st = SparseDecodeStep(p.L, w.k, env.dev)
     summ = st.new_summaries(env.dev)
     st.prefill_summaries(p.inp["k_pool"], p.inp["k_scales"], p.inp["block_table"], p.inp["seq_lens"], summ)
-    newest = torch.full((w.B,), w.nb - 1, dtype=torch.int32, device=env.dev)
+    stale_newest(summ, p.inp["seq_lens"], w.S)
     W = torch.empty((w.B, w.Hkv, w.nb), dtype=torch.float64, device=env.dev)
     out = st.run(p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
-                 p.inp["block_table"], p.inp["seq_lens"], summ, newest, bounds_out=W)
+                 p.inp["block_table"], p.inp["seq_lens"], summ, bounds_out=W)
     no_device_errors(env)
     seqs = [1, 3]
     flat = p.inp["block_table"][seqs].long().reshape(-1)
