@@ -45,6 +45,7 @@ namespace kvs {
 namespace {
 
 constexpr int kGMax = 16;
+constexpr int kAttnWaves = 4;  // wavefronts per workgroup of the MFMA kernels
 constexpr int kComputeUnits = 256;  // MI355X
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -231,28 +232,60 @@ __device__ __forceinline__ void page_values(PageV<D, S>& V, int ntok, int j4, co
   }
 }
 
-// Resolves tiles [t0, t0 + 64) of a wavefront's list (pages i0 + 4*t of the
-// selection row), one tile per lane, into LDS: pool tile index and valid
-// token count (0 = nothing to do).  Vector loads in parallel across lanes:
-// two round trips for the whole chunk instead of two per tile.
-__device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int32_t* srow, int i0, int i1, int t0,
+// The selection slots a lane resolves in chunk t0 of its wavefront's list:
+// slot i = i0 + nw*(t0 + lane) (nw = wavefronts per workgroup) and the slot
+// before it, or -1 where there is none.
+__device__ __forceinline__ void fetch_slots(const int32_t* srow, int i0, int i1, int nw, int t0, int& j, int& jp) {
+  const int lane = threadIdx.x & 63;
+  const int i = i0 + nw * (t0 + lane);
+  j = -2;  // no slot
+  jp = -1;
+  if (i < i1) {
+    j = srow[i];
+    jp = i > 0 ? srow[i - 1] : -1;
+  }
+}
+
+// The unit's block-table row (paged: row b; hot: row (b, g)) copied into LDS
+// by every thread of an NT-thread workgroup, when it has at most kTabMax
+// entries; the caller synchronises the workgroup before reading it.
+constexpr int kTabMax = 2048;
+
+template <int NT>
+__device__ __forceinline__ void stage_table_row(const AttnArgs& a, int b, int g, int* trow) {
+  const int32_t* row = a.hot ? a.table + ((long long)b * a.Hkv + g) * a.MB : a.table + (long long)b * a.MB;
+  int v[kTabMax / NT];
+#pragma unroll
+  for (int x = 0; x < kTabMax / NT; ++x) {
+    const int e = x * NT + (int)threadIdx.x;
+    v[x] = e < a.MB ? row[e] : 0;
+  }
+#pragma unroll
+  for (int x = 0; x < kTabMax / NT; ++x) {
+    const int e = x * NT + (int)threadIdx.x;
+    if (e < a.MB) trow[e] = v[x];
+  }
+}
+
+// Resolves the chunk's slots (one per lane, from fetch_slots) into LDS: pool
+// tile index and valid token count (0 = nothing to do).  The table entry
+// comes from the staged row `trow` when there is one, else from memory.
+__device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow, int j, int jp, bool first_slot,
                                               int b, int g, int nb, int len, int S, long long* wl_tile,
                                               int* wl_ntok) {
   const int lane = threadIdx.x & 63;
-  const int i = i0 + 4 * (t0 + lane);
   long long tile = a.hot ? 0 : g;  // tile (0, g): always in bounds
   int ntok = 0;
-  if (i < i1) {
-    const int j = srow[i];
+  if (j != -2) {
     bool ok = j >= 0;
     if (j < -1) raise_flag(a.err, 0x4u);
     if (ok) {
-      const int jp = i > 0 ? srow[i - 1] : -1;
-      if (j >= nb || (i > 0 && (jp >= j || jp < 0))) raise_flag(a.err, 0x4u);
+      if (j >= nb || (!first_slot && (jp >= j || jp < 0))) raise_flag(a.err, 0x4u);
       ok = j < nb;
     }
     if (ok) {
-      const int entry = a.hot ? a.table[((long long)b * a.Hkv + g) * a.MB + j] : a.table[(long long)b * a.MB + j];
+      const int entry = trow ? trow[j]
+                             : (a.hot ? a.table[((long long)b * a.Hkv + g) * a.MB + j] : a.table[(long long)b * a.MB + j]);
       if (entry < 0 || entry >= a.P) {
         raise_flag(a.err, 0x2u);
       } else {
@@ -268,11 +301,11 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int32_t* 
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The end of an MFMA-kernel workgroup: merges the four wavefronts' running
+// The end of an MFMA-kernel workgroup: merges the NW wavefronts' running
 // (max, sum, acc) in LDS; lane (r, j4) holds channels ct*16 + 4*j4 + e of
 // head r.  One split: the normalised output row is written; otherwise the
 // split partial.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, int split, int wave, int r, int j4,
                                                float m_run, float l_run, const f32x4_t* o, float (*mg_m)[16],
                                                float (*mg_l)[16], float (*mg_o)[16][D + 4]) {
@@ -292,10 +325,10 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
   if (wave == 0 && r < G) {
     float M = mg_m[0][r];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) M = fmaxf(M, mg_m[w][r]);
-    float scw[4], L = 0.0f;
+    for (int w = 1; w < NW; ++w) M = fmaxf(M, mg_m[w][r]);
+    float scw[NW], L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const float mw = mg_m[w][r];
       scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
       L += mg_l[w][r] * scw[w];
@@ -319,7 +352,7 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
         const int c = ct * 16 + 4 * j4 + e;
         float x = o[ct][e] * scw[0];
 #pragma unroll
-        for (int w = 1; w < 4; ++w) x += mg_o[w - 1][r][c] * scw[w];
+        for (int w = 1; w < NW; ++w) x += mg_o[w - 1][r][c] * scw[w];
         pv[e] = x * inv;
       }
       *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = v;
@@ -327,15 +360,16 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
   }
 }
 
-template <int D, int S>
-__global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
+template <int D, int S, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CS = D / 32;  // k-steps of the score product
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
   constexpr int NSUB = S / 32;  // 32-token sub-tiles per page
-  __shared__ float mg_m[4][16], mg_l[4][16];
-  __shared__ float mg_o[3][16][D + 4];
-  __shared__ long long wl_tile[4][64];
-  __shared__ int wl_ntok[4][64];
+  __shared__ float mg_m[NW][16], mg_l[NW][16];
+  __shared__ float mg_o[NW - 1][16][D + 4];
+  __shared__ long long wl_tile[NW][64];
+  __shared__ int wl_ntok[NW][64];
+  __shared__ int trow[kTabMax];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -363,9 +397,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
-  const int i0 = split * a.bps + wave;           // this wavefront's pages: i0, i0+4, ...
+  const int i0 = split * a.bps + wave;           // this wavefront's pages: i0, i0+NW, ...
   const int i1 = min(split * a.bps + a.bps, a.k);
-  const int ntiles = i0 < i1 ? (i1 - i0 + 3) / 4 : 0;
+  const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
 
@@ -375,8 +409,18 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
   // stay exact; after the last page the request goes to the pool's first
   // tile of this KV head, which every workgroup of the head shares and the
   // caches keep (no HBM traffic)
+  // the first chunk's slots and the table row are fetched together, so the
+  // table lookups need no further round trip
+  int j0, jp0;
+  fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+  const bool staged = a.MB <= kTabMax;
+  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+  __syncthreads();
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
-    resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
+    int j = j0, jp = jp0;
+    if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
+    resolve_tiles(a, staged ? trow : nullptr, j, jp, t0 == 0 && lane == 0 && i0 == 0, b, g, nb, len, S,
+                  wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
     PageK<D, S> K;
     PageV<D, S> V;
@@ -396,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  wg_merge_write<D>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
+  wg_merge_write<D, NW>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -575,16 +619,17 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
   }
 }
 
-template <int D, int S>
-__global__ __launch_bounds__(256, 2) void attn_mfma8_kernel(AttnArgs a) {
+template <int D, int S, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a) {
   constexpr int CS = D / 32;
   constexpr int CT = D / 16;
   constexpr int NSUB = S / 32;
-  __shared__ float mg_m[4][16], mg_l[4][16];
-  __shared__ float mg_o[3][16][D + 4];
-  __shared__ long long wl_tile[4][64];
-  __shared__ int wl_ntok[4][64];
-  __shared__ __attribute__((aligned(16))) float vsl[4][S * 8];  // per wavefront: [group][S]
+  __shared__ float mg_m[NW][16], mg_l[NW][16];
+  __shared__ float mg_o[NW - 1][16][D + 4];
+  __shared__ long long wl_tile[NW][64];
+  __shared__ int wl_ntok[NW][64];
+  __shared__ int trow[kTabMax];
+  __shared__ __attribute__((aligned(16))) float vsl[NW][S * 8];  // per wavefront: [group][S]
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -620,14 +665,22 @@ __global__ __launch_bounds__(256, 2) void attn_mfma8_kernel(AttnArgs a) {
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
   const int i0 = split * a.bps + wave;
   const int i1 = min(split * a.bps + a.bps, a.k);
-  const int ntiles = i0 < i1 ? (i1 - i0 + 3) / 4 : 0;
+  const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
   float* vw = vsl[wave];
 
   // the same two-stage page pipeline as the bf16 kernel
+  int j0, jp0;
+  fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+  const bool staged = a.MB <= kTabMax;
+  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+  __syncthreads();
   for (int t0 = 0; t0 < ntiles; t0 += 64) {
-    resolve_tiles(a, srow, i0, i1, t0, b, g, nb, len, S, wl_tile[wave], wl_ntok[wave]);
+    int j = j0, jp = jp0;
+    if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
+    resolve_tiles(a, staged ? trow : nullptr, j, jp, t0 == 0 && lane == 0 && i0 == 0, b, g, nb, len, S,
+                  wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
     PageK8<D, S> K;
     PageV8<D, S> V;
@@ -658,7 +711,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma8_kernel(AttnArgs a) {
       load_page_v8<D, S>(vpool + tnext * D * S, a.v_scales + tnext * S * groups, groups, r, j4, lane, V);
     }
   }
-  wg_merge_write<D>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
+  wg_merge_write<D, NW>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
 }
 
 // ---------------------------------------------------------------------------
@@ -943,6 +996,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 // 4 output channels of one head and a quarter of the splits; all of its
 // partial loads (m, acc) are issued together, the quarters are summed in LDS.
 constexpr int kMergeHeads = 2;
+constexpr int kMaxSplits = kComputeUnits;  // attn_num_splits never exceeds it
 
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
@@ -959,24 +1013,6 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
   const int ch = tid % CH, sg = tid / CH;
   const int hh = ch / C4, c = (ch % C4) * 4;
   const long long row = h0 + hh;
-  // per head: max and normaliser over the splits (one wavefront per head)
-  if (wave < kMergeHeads && h0 + wave < nrows) {
-    const float* pm = a.part_m + (h0 + wave) * ns;
-    const float* pl = a.part_l + (h0 + wave) * ns;
-    float M = -__builtin_inff();
-    for (int s = lane; s < ns; s += kWave) M = fmaxf(M, pm[s]);
-    M = wave_max(M);
-    float L = 0.0f;
-    for (int s = lane; s < ns; s += kWave) {
-      const float ms = pm[s];
-      L += ms == -__builtin_inff() ? 0.0f : pl[s] * exp2f(ms - M);
-    }
-    L = wave_sum(L);
-    if (lane == 0) {
-      hm[wave] = M;
-      hl[wave] = L;
-    }
-  }
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   const bool live = row < nrows;
   float4 v[BATCH];
@@ -1003,10 +1039,35 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
       acc.w += w * v[x].w;
     }
   };
-  // the first batch is in flight while the per-head max is computed; every
-  // thread meets the same two barriers
+  // the first batch of partial rows goes out first; the per-head max and
+  // normaliser are computed while it is in flight (one wavefront per head,
+  // m and l of all splits fetched in one round: ns <= kMaxSplits)
   load_batch(sg);
+  if (wave < kMergeHeads && h0 + wave < nrows) {
+    const float* pm = a.part_m + (h0 + wave) * ns;
+    const float* pl = a.part_l + (h0 + wave) * ns;
+    float mv[kMaxSplits / kWave], lv[kMaxSplits / kWave];
+#pragma unroll
+    for (int x = 0; x < kMaxSplits / kWave; ++x) {
+      const int s = x * kWave + lane;
+      mv[x] = s < ns ? pm[s] : -__builtin_inff();
+      lv[x] = s < ns ? pl[s] : 0.0f;
+    }
+    float M = mv[0];
+#pragma unroll
+    for (int x = 1; x < kMaxSplits / kWave; ++x) M = fmaxf(M, mv[x]);
+    M = wave_max(M);
+    float L = 0.0f;
+#pragma unroll
+    for (int x = 0; x < kMaxSplits / kWave; ++x) L += mv[x] == -__builtin_inff() ? 0.0f : lv[x] * exp2f(mv[x] - M);
+    L = wave_sum(L);
+    if (lane == 0) {
+      hm[wave] = M;
+      hl[wave] = L;
+    }
+  }
   __syncthreads();
+  // every thread meets the same two barriers
   const float Mh = live ? hm[hh] : 0.0f;
   add_batch(Mh);
   for (int s0 = sg + SG * BATCH; s0 < ns; s0 += SG * BATCH) {
@@ -1055,9 +1116,9 @@ template <int D>
 hipError_t launch_mfma8(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
   if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1065,9 +1126,9 @@ template <int D>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
   if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 32>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 32, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 64>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 64, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1089,6 +1150,7 @@ int attn_num_splits(int units, int k) {
 
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
+  if (a.nsplit < 1 || a.nsplit > kMaxSplits) return hipErrorInvalidValue;  // merge_kernel's bound
   hipError_t e;
   if (q_kind == K_BF16 && kv_kind == K_BF16 && a.S >= 32)
     e = a.D == 64 ? launch_mfma<64>(a, st) : launch_mfma<128>(a, st);
