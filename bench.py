@@ -279,7 +279,7 @@ def bench_hot(args, w, dev) -> int:
     sels = torch.from_numpy(stream).to(dev)
     # host tier [B][Hkv][MB][S][D] (V tiles [D][S]), pinned and shared by the layer instances
     pages = inp["block_table"].long().cpu()
-    host = [None if inp[n] is None else inp[n].cpu()[pages].permute(0, 2, 1, 3, 4).contiguous().pin_memory()
+    host = [None if inp[n] is None else inp[n].cpu()[pages].transpose(1, 2).contiguous().pin_memory()
             for n in ("k_pool", "v_pool", "k_scales", "v_scales")]
     hs = [HotBufferStep(L, w.k, w.hot_slots, dev) for _ in range(n_layers)]
     for h in hs:  # warm start: the first selection fills every slot

@@ -32,9 +32,12 @@
  *  K pool (paged):    [P][Hkv][S][D] of kv_dtype (token-major tiles); page p
  *                     holds S consecutive tokens of one sequence for every
  *                     KV head.
- *  V pool (paged):    [P][Hkv][D][S] of kv_dtype (channel-major tiles: the
- *                     S tokens of one channel are contiguous, so the value
- *                     product reads whole token runs per channel).
+ *  V pool (paged):    [P][Hkv][S/T][D][T] of kv_dtype, T = min(S, 32): each
+ *                     tile is cut into runs of T consecutive tokens, and a
+ *                     run is stored channel-major (its T tokens of one
+ *                     channel are contiguous), so one 16-channel slice of a
+ *                     run is a contiguous 1 KiB (bf16) read.  For S <= 32
+ *                     this is the plain channel-major tile [D][S].
  *  fp8 scales:        [P][Hkv][S][D/quant_group] fp32, one per token and
  *                     group of quant_group adjacent channels ("分块稀疏注意力
  *                     与KV Cache量化…", §2.4; symmetric, no zero point).  The
@@ -93,7 +96,7 @@ typedef enum kvs_table_kind {
   KVS_TABLE_PAGED = 0,
   /* table = hot page table [B][Hkv][MB] of global hot-slot ids in [0, P)
    * (-1 = not resident); one KV head per slot: K pool [P][S][D], V pool
-   * [P][D][S], scales [P][S][D/quant_group]. P is then the total number of
+   * [P][S/T][D][T], scales [P][S][D/quant_group]. P is then the total number of
    * hot slots. */
   KVS_TABLE_HOT = 1
 } kvs_table_kind;
@@ -222,7 +225,7 @@ kvs_status kvs_select_topk_append(const kvs_layout* layout, const void* q, const
  *
  *  table_kind   KVS_TABLE_PAGED or KVS_TABLE_HOT (see kvs_table_kind)
  *  q            [B][Hq][D] q_dtype
- *  k_pool/v_pool, k_scales/v_scales   per table_kind (V channel-major)
+ *  k_pool/v_pool, k_scales/v_scales   per table_kind (V in T-token runs)
  *  table        [B][MB] (paged) or [B][Hkv][MB] (hot) int32
  *  seq_lens     [B] int32
  *  sel          [B][Hkv][k] int32, k >= 1
@@ -270,12 +273,12 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* layout, int32_t table_kind,
  *  page_table   [B][Hkv][MB] int32 in/out (global slot id or -1)
  *  slot_owner   [B][Hkv][num_slots] int32 in/out (block id or -1)
  *  slot_stamp   [B][Hkv][num_slots] int64 in/out (-1 when free)
- *  host_k/host_v  HOST [B][Hkv][MB][S][D] (K) and [B][Hkv][MB][D][S] (V)
+ *  host_k/host_v  HOST [B][Hkv][MB][S][D] (K) and [B][Hkv][MB][S/T][D][T] (V)
  *               kv_dtype, allocated with hipHostMalloc (pinned and mapped;
  *               the kernels read it over the host link); tiles are copied
  *               byte for byte
  *  host_k_scales/host_v_scales  HOST [B][Hkv][MB][S][D/qg] fp32 (fp8 only)
- *  hot_k/hot_v  [B*Hkv*num_slots][S][D] (K) and [B*Hkv*num_slots][D][S] (V)
+ *  hot_k/hot_v  [B*Hkv*num_slots][S][D] (K) and [B*Hkv*num_slots][S/T][D][T] (V)
  *               kv_dtype (the KVS_TABLE_HOT pools)
  *  hot_k_scales/hot_v_scales  [B*Hkv*num_slots][S][D/qg] fp32 (fp8 only)
  *  miss_list    [B][Hkv][k] int32 output;  miss_count [B][Hkv] int32 output

@@ -88,11 +88,13 @@ static double kv_value(const or_layout* L, const void* pool, const float* scales
   return pool_value(L, pool, scales, idx, page, g, s, c);
 }
 
-/* V element (page, kv head g, token s, channel c): channel-major tile
- * [D][S]. */
+/* V element (page, kv head g, token s, channel c): the tile is cut into
+ * runs of T = min(S, 32) consecutive tokens, each stored channel-major,
+ * [S/T][D][T]. */
 static double v_value(const or_layout* L, const void* pool, const float* scales,
                       int64_t page, int32_t g, int32_t s, int32_t c) {
-  int64_t idx = ((page * L->Hkv + g) * (int64_t)L->D + c) * L->S + s;
+  const int32_t T = L->S < 32 ? L->S : 32;
+  int64_t idx = (((page * L->Hkv + g) * (int64_t)(L->S / T) + s / T) * L->D + c) * T + s % T;
   return pool_value(L, pool, scales, idx, page, g, s, c);
 }
 

@@ -30,7 +30,8 @@
  *            (= page), max_blocks entries per block-table row, num_pages
  *            pages in the pool.
  *   pools  : the K pool is [num_pages][Hkv][S][D] (token-major tiles), the
- *            V pool [num_pages][Hkv][D][S] (channel-major tiles), both of
+ *            V pool [num_pages][Hkv][S/T][D][T] with T = min(S, 32) (runs
+ *            of T tokens, each channel-major), both of
  *            kv_dtype (0 = fp32, 1 = bf16 bit patterns, 2 = OCP E4M3FN
  *            codes).  fp8 scales of K and of V are both
  *            [num_pages][Hkv][S][D/quant_group] fp32, one per token and

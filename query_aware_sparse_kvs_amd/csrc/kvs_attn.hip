@@ -22,8 +22,9 @@
 //           B is Q^T, loaded once.  Token rows are permuted (tau below) so
 //           that the accumulator a lane ends up holding is exactly the
 //           8-token slice it must feed to the value product.
-//   values  O^T = V^T P^T: the A operand is 16 channels x 32 tokens of the
-//           channel-major V tile (contiguous 16-byte loads); B is P^T taken
+//   values  O^T = V^T P^T: the A operand is 16 channels x 32 tokens of one
+//           32-token run of the V tile, stored channel-major, so each load
+//           instruction reads 1 KiB contiguous; B is P^T taken
 //           from the score accumulators in registers.  P is split into
 //           hi = bf16(p) and lo = bf16(p - hi), two MFMAs, so the product
 //           keeps ~16 bits of P.  No LDS traffic inside the tile loop.
@@ -120,7 +121,8 @@ struct PageV {
   u32x4 r[S / 32][D / 16];
 };
 
-// kt: the page's K tile [S][D]; vt: its V tile [D][S].
+// kt: the page's K tile [S][D]; vt: its V tile [S/32][D][32] (32-token runs,
+// each channel-major).
 template <int D, int S>
 __device__ __forceinline__ void load_page_k(const uint16_t* kt, int r, int j4, PageK<D, S>& K) {
 #pragma unroll
@@ -140,7 +142,7 @@ __device__ __forceinline__ void load_page_v(const uint16_t* vt, int r, int j4, P
   for (int h = 0; h < S / 32; ++h)
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct)
-      V.r[h][ct] = *reinterpret_cast<const u32x4*>(vt + (ct * 16 + r) * S + h * 32 + 8 * j4);
+      V.r[h][ct] = *reinterpret_cast<const u32x4*>(vt + (h * D + ct * 16 + r) * 32 + 8 * j4);
 }
 
 // Scores of one page (ntok valid tokens, possibly 0), the online-softmax
@@ -510,7 +512,7 @@ __device__ __forceinline__ void load_page_v8(const uint8_t* vt, const float* vst
   for (int h = 0; h < S / 32; ++h)
 #pragma unroll
     for (int ct = 0; ct < D / 16; ++ct)
-      V.v[h][ct] = *reinterpret_cast<const u32x2*>(vt + (ct * 16 + r) * S + h * 32 + 8 * j4);
+      V.v[h][ct] = *reinterpret_cast<const u32x2*>(vt + (h * D + ct * 16 + r) * 32 + 8 * j4);
 #pragma unroll
   for (int y = 0; y < S * 8 / kWave; ++y) {
     const int x = y * kWave + lane;
@@ -729,6 +731,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   constexpr int KL = CPL / VEC;         // 16-byte K loads per lane
   constexpr int VPL = D / kWave;        // channels per lane in the value phase
   constexpr int VL = S * EB / 16;       // 16-byte loads per V channel row
+  constexpr int VT = S < 32 ? S : 32;   // tokens per channel-major run of the V tile
+  constexpr int TPV = 16 / EB;          // tokens per 16-byte load (divides VT)
+  static_assert(VT % TPV == 0, "a V load stays inside one run");
   static_assert(VL >= 1, "a V channel row must span at least 16 bytes");
 
   extern __shared__ float smem[];
@@ -819,7 +824,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
     for (int e = 0; e < VPL; ++e)
 #pragma unroll
       for (int x = 0; x < VL; ++x)
-        vraw[e][x] = *reinterpret_cast<const uint4*>(vb + ((tile * D + c0 + e) * S) * EB + x * 16);
+        vraw[e][x] = *reinterpret_cast<const uint4*>(
+            vb + (tile * S * D + ((x * TPV) / VT * D + c0 + e) * VT + (x * TPV) % VT) * EB);
     if constexpr (KVK == K_FP8) {
       // at most 8 groups per token: a fixed-trip loop, all loads in flight together
       float vsv[S * 8 / kWave];

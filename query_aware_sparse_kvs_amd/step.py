@@ -115,7 +115,8 @@ class HotBufferStep:
         self.slot_stamp = torch.full((L.num_seqs, L.num_kv_heads, num_slots), -1, dtype=torch.int64, device=dev)
         pool_dt = {kvs.KVS_F32: torch.float32, kvs.KVS_BF16: torch.bfloat16, kvs.KVS_FP8_E4M3: torch.uint8}[L.kv_dtype]
         self.hot_k = torch.zeros((units * num_slots, L.block_size, L.head_dim), dtype=pool_dt, device=dev)
-        self.hot_v = torch.zeros((units * num_slots, L.head_dim, L.block_size), dtype=pool_dt, device=dev)
+        T = min(L.block_size, 32)  # V tiles: runs of T tokens, each channel-major
+        self.hot_v = torch.zeros((units * num_slots, L.block_size // T, L.head_dim, T), dtype=pool_dt, device=dev)
         if L.quant_group:
             sshape = (units * num_slots, L.block_size, L.head_dim // L.quant_group)
             self.hot_ks = torch.ones(sshape, dtype=torch.float32, device=dev)

@@ -173,13 +173,27 @@ def quantize_e4m3(x: torch.Tensor, group: int):
     return codes.contiguous(), scale.contiguous()
 
 
+def v_pool_shape(P: int, Hkv: int, D: int, S: int) -> tuple:
+    """Shape of a V pool: each tile is cut into runs of T = min(S, 32)
+    consecutive tokens, each stored channel-major."""
+    T = min(S, 32)
+    return (P, Hkv, S // T, D, T)
+
+
+def v_tiles_from_token_major(x: torch.Tensor) -> torch.Tensor:
+    """[..., S, D] token-major tiles -> the V pool layout [..., S/T, D, T]."""
+    S, D = x.shape[-2], x.shape[-1]
+    T = min(S, 32)
+    return x.reshape(*x.shape[:-2], S // T, T, D).transpose(-1, -2).contiguous()
+
+
 def make_inputs(w: Workload, device="cpu", layer: int = 0, seq_lens=None,
                 max_blocks: int | None = None, num_pages: int | None = None) -> dict:
     """All inputs of one decode layer-step.
 
     Returns a dict with q [B][Hq][D], k_pool [P][Hkv][S][D] and v_pool
-    [P][Hkv][D][S] (channel-major V tiles; fp32, bf16 or uint8 E4M3FN
-    codes), k_scales / v_scales
+    [P][Hkv][S/T][D][T], T = min(S, 32) (V tiles as runs of T tokens, each
+    channel-major; fp32, bf16 or uint8 E4M3FN codes), k_scales / v_scales
     [P][Hkv][S][D/group] fp32 (fp8 only, else None), block_table
     [B][max_blocks] int32, seq_lens [B] int32.  Token positions at or past a
     sequence's length still hold random data (they must not be read)."""
@@ -194,7 +208,7 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0, seq_lens=None,
     if w.kv_dtype in ("f32", "bf16"):
         dt = _TORCH_DT[w.kv_dtype]
         kp = _randn(shape, dt, device, _gen(device, w.seed, base + 2))
-        vp = _randn((P, w.Hkv, w.D, w.S), dt, device, _gen(device, w.seed, base + 3))
+        vp = _randn(v_pool_shape(P, w.Hkv, w.D, w.S), dt, device, _gen(device, w.seed, base + 3))
         _plant_heavy(w, kp, tbl, layer, 10_000)
         out.update(k_pool=kp, v_pool=vp, k_scales=None, v_scales=None)
     else:
@@ -210,8 +224,8 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0, seq_lens=None,
                 _plant_heavy(w, x, tbl, layer, 10_000)
             codes, scales = quantize_e4m3(x, w.quant_group)
             del x
-            if name == "v":  # channel-major V tiles
-                codes = codes.transpose(-1, -2).contiguous()
+            if name == "v":  # token-major [S][D] -> runs of T tokens, channel-major
+                codes = v_tiles_from_token_major(codes)
             out[name + "_pool"] = codes
             out[name + "_scales"] = scales
     if seq_lens is None:

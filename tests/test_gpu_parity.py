@@ -452,7 +452,7 @@ def host_tier(p):
     out = []
     for n in ("k_pool", "v_pool", "k_scales", "v_scales"):
         t = p.inp[n]
-        out.append(None if t is None else t.cpu()[pages].permute(0, 2, 1, 3, 4).contiguous().pin_memory())
+        out.append(None if t is None else t.cpu()[pages].transpose(1, 2).contiguous().pin_memory())
     return out
 
 

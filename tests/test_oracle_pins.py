@@ -43,8 +43,11 @@ def make_problem(orc, rng, B=2, Hq=4, Hkv=2, D=8, S=4, max_blocks=6, lens=(21, 9
     L = orc.Layout(B, Hq, Hkv, D, S, max_blocks, P, kv_dtype, quant_group)
     prob = dict(L=L, table=pages, lens=lens, k_scales=None, v_scales=None)
     # values are drawn token-major [P][Hkv][S][D]; the V pool stores each
-    # tile channel-major [P][Hkv][D][S] (the *_val arrays stay token-major)
-    tr = lambda a, n: np.ascontiguousarray(np.swapaxes(a, -1, -2)) if n == "v" else a
+    # tile as runs of T = min(S, 32) tokens, each channel-major,
+    # [P][Hkv][S/T][D][T] (the *_val arrays stay token-major)
+    T = min(S, 32)
+    tr = lambda a, n: (np.ascontiguousarray(np.swapaxes(a.reshape(P, Hkv, S // T, T, D), -1, -2))
+                       if n == "v" else a)
     if kv_dtype == orc.KV_F32:
         for i, n in enumerate("kv"):
             prob[n + "_pool"] = tr(x[i].astype(np.float32), n)
@@ -344,10 +347,12 @@ def _all_blocks_sel(L, lens, k):
     return sel
 
 
+@pytest.mark.parametrize("S,mb,lens", [(4, 6, (22, 1)), (64, 2, (100, 33))])
 @pytest.mark.parametrize("kv_dtype,qg", [(0, 0), (1, 0), (2, 4)])
-def test_dense_attention_matches_sdpa_and_numpy(orc, kv_dtype, qg):
+def test_dense_attention_matches_sdpa_and_numpy(orc, kv_dtype, qg, S, mb, lens):
+    """Also at S = 64, where a V tile is two 32-token runs."""
     rng = np.random.default_rng(8)
-    p = make_problem(orc, rng, D=16, kv_dtype=kv_dtype, quant_group=qg, lens=(22, 1))
+    p = make_problem(orc, rng, D=16, S=S, max_blocks=mb, kv_dtype=kv_dtype, quant_group=qg, lens=lens)
     L = p["L"]
     scale = 1.0 / math.sqrt(L.D)
     out = orc.dense_attn(L, p["q"], p["k_pool"], p["v_pool"], p["k_scales"], p["v_scales"],
@@ -398,7 +403,7 @@ def test_attention_of_uniform_values_is_that_value(orc):
     rng = np.random.default_rng(11)
     p = make_problem(orc, rng, D=16, lens=(21, 9))
     row = rng.standard_normal(16).astype(np.float32)
-    p["v_pool"][:] = row[:, None]  # channel-major tiles: V[c][t] = row[c]
+    p["v_pool"][:] = row[:, None]  # channel-major runs: V[run][c][t] = row[c]
     L = p["L"]
     sel = np.array([[[0, 2, 5, -1], [1, 5, -1, -1]], [[0, 2, -1, -1], [1, -1, -1, -1]]], np.int32)
     out = orc.sparse_attn(L, p["q"], p["k_pool"], p["v_pool"], None, None, p["table"], p["lens"],
