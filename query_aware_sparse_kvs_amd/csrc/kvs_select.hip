@@ -3,9 +3,10 @@
 // summaries, keep the top-k; the sink block and the newest block are always
 // kept, same page §2 and "SparDA：把KV選擇提前一層…" §4.2).
 //
-// bounds_kernel: a 256-thread workgroup stages 64 consecutive blocks'
-// summaries in LDS with coalesced 16-byte loads; lane = block, wavefront w
-// takes query heads w, w+4, ...  The block score is
+// bounds_kernel: a workgroup of 4 wavefronts (8 for bf16 summaries and
+// groups of 8 or more query heads, one per head) stages 64 consecutive blocks' summaries in LDS
+// with coalesced 16-byte loads; lane = block, wavefront w takes query heads
+// w, w+NW, ...  The block score is
 // U = sum_c max(q_c*mn_c, q_c*mx_c); since mx_c >= mn_c the larger product is
 // q_c*mx_c when q_c >= 0 and q_c*mn_c otherwise.  That choice depends only
 // on the head, so it is uniform over a wavefront: a per-head bit mask picks
@@ -33,14 +34,24 @@ namespace {
 
 constexpr int kBoundBlocks = 64;  // blocks per bounds workgroup (lane = block)
 
+// wavefronts per bounds workgroup: one per query head of the group, 4 to 8
+// (4 with fp32 summaries, whose chunk fills half the LDS)
+template <int G, int SK>
+constexpr int bound_waves() {
+  return G >= 8 && SK == K_BF16 ? 8 : 4;
+}
+
 template <int QK, int SK, int D, int G>
-__global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
+__global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, SK>())) void bounds_kernel(BoundArgs a) {
+  constexpr int NWB = bound_waves<G, SK>();
+  constexpr int NT = 64 * NWB;
   constexpr int NB = kBoundBlocks;
   constexpr int EB = elem_bytes<SK>();
   constexpr int ROWB = 2 * D * EB;           // bytes of one block's summary
   constexpr int ROWP = ROWB + 16;            // padded LDS row (bank spread)
   constexpr int NV = NB * ROWB / 16;         // 16-byte vectors of the chunk
-  constexpr int NPT = NV / 256;
+  constexpr int NPT = NV / NT;
+  static_assert(NV % NT == 0, "whole vectors per thread");
   constexpr int VEC = 16 / EB;               // summary elements per 16 bytes
   constexpr int WPR = D * EB / 4;            // 32-bit words per half row
   __shared__ __attribute__((aligned(16))) char sm[NB * ROWP];
@@ -48,14 +59,14 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   __shared__ __attribute__((aligned(16))) uint32_t qm[G][WPR];
   const int b = blockIdx.z, g = blockIdx.y;
   if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
-    static_assert(sizeof(sm) >= kSummRed<D> * sizeof(float), "summary reduction fits the chunk buffer");
+    static_assert(sizeof(sm) >= kSummRed<D, NT> * sizeof(float), "summary reduction fits the chunk buffer");
     float* red = reinterpret_cast<float*>(sm);
     if constexpr (SK == K_BF16) {
-      rebuild_newest_summary<K_BF16, D>(a.app, b, g, red);
+      rebuild_newest_summary<K_BF16, D, NT>(a.app, b, g, red);
     } else if (a.app_kv == K_FP8) {
-      rebuild_newest_summary<K_FP8, D>(a.app, b, g, red);
+      rebuild_newest_summary<K_FP8, D, NT>(a.app, b, g, red);
     } else {
-      rebuild_newest_summary<K_F32, D>(a.app, b, g, red);
+      rebuild_newest_summary<K_F32, D, NT>(a.app, b, g, red);
     }
     return;
   }
@@ -70,12 +81,12 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   u32x4 raw[NPT];
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
-    const int v = x * 256 + tid;
+    const int v = x * NT + tid;
     raw[x] = u32x4{0u, 0u, 0u, 0u};
     if (v / (ROWB / 16) < nmem) raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)v * 16);
   }
   // the query as fp64, and per head the words' choice of max (mask bits set) or min
-  for (int i = tid; i < G * D; i += 256) {
+  for (int i = tid; i < G * D; i += NT) {
     const int h = i / D, c = i % D;
     const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
     float v;
@@ -94,14 +105,14 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   const int nb = (len + a.S - 1) / a.S;
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
-    const int v = x * 256 + tid;
+    const int v = x * NT + tid;
     if (v / (ROWB / 16) < nmem) {
       const int blk = v / (ROWB / 16), off = (v % (ROWB / 16)) * 16;
       *reinterpret_cast<u32x4*>(sm + blk * ROWP + off) = raw[x];
     }
   }
   __syncthreads();
-  for (int i = tid; i < G * WPR; i += 256) {
+  for (int i = tid; i < G * WPR; i += NT) {
     const int h = i / WPR, w = i % WPR;
     uint32_t m;
     if constexpr (EB == 2)
@@ -112,7 +123,7 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   }
   __syncthreads();
 
-  constexpr int HPW = (G + 3) / 4;  // heads per wavefront
+  constexpr int HPW = (G + NWB - 1) / NWB;  // heads per wavefront
   const bool valid = j0 + lane < nb;
   double acc[HPW];
 #pragma unroll
@@ -126,7 +137,7 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
       const u32x4 vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
 #pragma unroll
       for (int i = 0; i < HPW; ++i) {
-        const int h = wave + 4 * i;
+        const int h = wave + NWB * i;
         if (h >= G) break;
         const u32x4 m = *reinterpret_cast<const u32x4*>(&qm[h][c0 * EB / 4]);
         const u32x4 x = (vmx & m) | (vmn & ~m);
@@ -150,7 +161,7 @@ __global__ __launch_bounds__(256, 4) void bounds_kernel(BoundArgs a) {
   double* ured = reinterpret_cast<double*>(sm);  // [G][NB]
 #pragma unroll
   for (int i = 0; i < HPW; ++i) {
-    const int h = wave + 4 * i;
+    const int h = wave + NWB * i;
     if (h < G) ured[h * NB + lane] = acc[i];
   }
   __syncthreads();
@@ -386,7 +397,7 @@ template <int QK, int SK, int D, int G>
 void launch_bounds_one(const BoundArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks + (a.append ? 1 : 0)), (unsigned)a.Hkv,
                   (unsigned)a.B);
-  hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(64 * bound_waves<G, SK>()), 0, s, a);
 }
 
 template <int QK, int SK, int D>

@@ -1,6 +1,6 @@
 // kvs_summarize.h -- the summary of one block (per channel: min and max of
 // K over the block's valid tokens; page "KV 稀疏化", §5 "Quest"), computed by
-// one 256-thread workgroup.  Shared by the summaries kernel and by the
+// one workgroup (256 threads unless the caller's kernel has more).  Shared by the summaries kernel and by the
 // scoring kernels, whose extra workgroups rebuild each sequence's newest
 // block while the others score.
 //
@@ -18,20 +18,21 @@
 namespace kvs {
 
 // Block j of (sequence b, KV head g), len = that sequence's clamped length,
-// j < ceil(len / S).  Every thread of the workgroup must call it; `red` is
-// kSummRed<D> floats of the caller's LDS, free for this call.
-template <int D>
-constexpr int kSummRed = 8 * D;
+// j < ceil(len / S).  Every thread of the NT-thread workgroup must call it;
+// `red` is kSummRed<D, NT> floats of the caller's LDS, free for this call.
+template <int D, int NT = 256>
+constexpr int kSummRed = 2 * D * (NT / 64);
 
-template <int KVK, int D, int S>
+template <int KVK, int D, int S, int NT = 256>
 __device__ __forceinline__ void summarize_block(const SummArgs& a, int b, int g, int j, int len, float* red) {
   constexpr int VEC = Vec16<KVK>::N;              // elements per 16-byte vector
   constexpr int LPR = D / VEC;                    // vectors per token row
   constexpr int NV = S * LPR;                     // vectors per tile
-  constexpr int NPT = (NV + 255) / 256;           // vectors per thread
-  constexpr int RSTEP = 256 / LPR;                // row stride between a thread's vectors
-  static_assert(256 % LPR == 0 && LPR <= kWave, "row split must divide the workgroup");
-  static_assert(4 * 2 * LPR * VEC == kSummRed<D>, "reduction buffer size");
+  constexpr int NPT = (NV + NT - 1) / NT;         // vectors per thread
+  constexpr int RSTEP = NT / LPR;                 // row stride between a thread's vectors
+  constexpr int NW = NT / kWave;
+  static_assert(NT % LPR == 0 && LPR <= kWave, "row split must divide the workgroup");
+  static_assert(NW * 2 * LPR * VEC == kSummRed<D, NT>, "reduction buffer size");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int page = a.block_table[(long long)b * a.MB + j];
   if (page < 0 || page >= a.P) {
@@ -111,7 +112,7 @@ __device__ __forceinline__ void summarize_block(const SummArgs& a, int b, int g,
   __syncthreads();
   if (wave != 0 || lane >= LPR) return;
 #pragma unroll
-  for (int w = 1; w < 4; ++w)
+  for (int w = 1; w < NW; ++w)
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       mn[e] = fminf(mn[e], red[((w * 2 + 0) * LPR + lane) * VEC + e]);
@@ -143,7 +144,7 @@ __device__ __forceinline__ void summarize_block(const SummArgs& a, int b, int g,
 // The summary of sequence b's newest block (nb - 1) for KV head g, from a
 // workgroup of a kernel launched for other work (uniform early role); `red`
 // as for summarize_block.
-template <int KVK, int D>
+template <int KVK, int D, int NT = 256>
 __device__ __forceinline__ void rebuild_newest_summary(const SummArgs& a, int b, int g, float* red) {
   int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
@@ -151,9 +152,9 @@ __device__ __forceinline__ void rebuild_newest_summary(const SummArgs& a, int b,
   const int nb = (len + a.S - 1) / a.S;
   if (nb == 0) return;
   switch (a.S) {
-    case 16: summarize_block<KVK, D, 16>(a, b, g, nb - 1, len, red); break;
-    case 32: summarize_block<KVK, D, 32>(a, b, g, nb - 1, len, red); break;
-    default: summarize_block<KVK, D, 64>(a, b, g, nb - 1, len, red); break;
+    case 16: summarize_block<KVK, D, 16, NT>(a, b, g, nb - 1, len, red); break;
+    case 32: summarize_block<KVK, D, 32, NT>(a, b, g, nb - 1, len, red); break;
+    default: summarize_block<KVK, D, 64, NT>(a, b, g, nb - 1, len, red); break;
   }
 }
 
