@@ -62,6 +62,9 @@ def lib():
             "or_summaries": (ctypes.c_int, [LP, P, P, P, P, P, i32, P]),
             "or_bounds": (ctypes.c_int, [LP, P, P, P, P, P]),
             "or_select": (ctypes.c_int, [LP, P, P, i32, P]),
+            "or_select_window": (ctypes.c_int, [LP, P, P, i32, i32, P]),
+            "or_ema_scores": (ctypes.c_int, [LP, P, P, f64, P, P]),
+            "or_append_token": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
             "or_sparse_attn": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, i32, f64, P]),
             "or_dense_attn": (ctypes.c_int, [LP, P, P, P, P, P, P, P, f64, P]),
             "or_hot_step": (ctypes.c_int, [i32, i32, i32, i64, i32, P, P, P, P, P, P]),
@@ -164,6 +167,48 @@ def select(L: Layout, W, seq_lens, k):
     sel = np.empty((L.B, L.Hkv, k), dtype=np.int32)
     _check(lib().or_select(ctypes.byref(L.c()), _ptr(W), _ptr(sl), k, _ptr(sel)), "or_select")
     return sel
+
+
+def select_window(L: Layout, W, seq_lens, k, recent):
+    W = _c(W, np.float64)
+    sl = _c(seq_lens, np.int32)
+    sel = np.empty((L.B, L.Hkv, k), dtype=np.int32)
+    _check(lib().or_select_window(ctypes.byref(L.c()), _ptr(W), _ptr(sl), k, recent, _ptr(sel)),
+           "or_select_window")
+    return sel
+
+
+def ema_scores(L: Layout, W, seq_lens, alpha, state):
+    """Smoothed scores; `state` ([B][Hkv][max_blocks] fp64, NaN = no history)
+    is updated in place."""
+    W = _c(W, np.float64)
+    sl = _c(seq_lens, np.int32)
+    assert state.dtype == np.float64 and state.flags.c_contiguous
+    out = np.empty((L.B, L.Hkv, L.max_blocks), dtype=np.float64)
+    _check(lib().or_ema_scores(ctypes.byref(L.c()), _ptr(W), _ptr(sl), float(alpha), _ptr(state),
+                               _ptr(out)), "or_ema_scores")
+    return out
+
+
+def append_token(L: Layout, k_new, v_new, k_new_scales, v_new_scales, block_table, seq_lens,
+                 k_pool, v_pool, k_scales, v_scales, summ, host_k=None, host_v=None,
+                 host_k_scales=None, host_v_scales=None):
+    """Appends one token per sequence; pools, scales, summaries and the host
+    tier (numpy, C-contiguous) are updated in place."""
+    kn, vn = _pool(L, k_new), _pool(L, v_new)
+    kns, vns = _c(k_new_scales, np.float32), _c(v_new_scales, np.float32)
+    bt, sl = _c(block_table, np.int32), _c(seq_lens, np.int32)
+    for a in (k_pool, v_pool, host_k, host_v):
+        if a is not None:
+            assert a.dtype == _POOL_DTYPE[L.kv_dtype] and a.flags.c_contiguous
+    for a in (k_scales, v_scales, host_k_scales, host_v_scales):
+        if a is not None:
+            assert a.dtype == np.float32 and a.flags.c_contiguous
+    assert summ.dtype == np.float64 and summ.flags.c_contiguous
+    _check(lib().or_append_token(ctypes.byref(L.c()), _ptr(kn), _ptr(vn), _ptr(kns), _ptr(vns),
+                                 _ptr(bt), _ptr(sl), _ptr(k_pool), _ptr(v_pool), _ptr(k_scales),
+                                 _ptr(v_scales), _ptr(summ), _ptr(host_k), _ptr(host_v),
+                                 _ptr(host_k_scales), _ptr(host_v_scales)), "or_append_token")
 
 
 def sparse_attn(L: Layout, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, sel,

@@ -110,6 +110,26 @@ static int len_ok(const or_layout* L, int32_t len) {
 /* summaries                                                           */
 /* ------------------------------------------------------------------ */
 
+/* min and max per channel of K over the valid tokens of block j of
+ * (sequence b, KV head g), stored in page `page`, into the summary table. */
+static void block_min_max(const or_layout* L, const void* k_pool, const float* k_scales,
+                          int32_t page, int32_t b, int32_t g, int32_t j, int32_t len,
+                          double* out) {
+  int32_t t_end = (j + 1) * L->S < len ? (j + 1) * L->S : len;
+  double* mn = out + ((((int64_t)b * L->Hkv + g) * L->max_blocks + j) * 2 + 0) * L->D;
+  double* mx = mn + L->D;
+  for (int32_t c = 0; c < L->D; ++c) {
+    double lo = INFINITY, hi = -INFINITY;
+    for (int32_t t = j * L->S; t < t_end; ++t) {
+      double v = kv_value(L, k_pool, k_scales, page, g, t - j * L->S, c);
+      if (v < lo) lo = v;
+      if (v > hi) hi = v;
+    }
+    mn[c] = lo;
+    mx[c] = hi;
+  }
+}
+
 int or_summaries(const or_layout* L, const void* k_pool, const float* k_scales,
                  const int32_t* block_table, const int32_t* seq_lens,
                  const int32_t* first_block, int32_t num_rebuild,
@@ -128,21 +148,7 @@ int or_summaries(const or_layout* L, const void* k_pool, const float* k_scales,
     for (int32_t j = j0; j < j1; ++j) {
       int32_t page = block_table[(int64_t)b * L->max_blocks + j];
       if (page < 0 || page >= L->num_pages) return OR_ERANGE;
-      int32_t t_end = (j + 1) * L->S < len ? (j + 1) * L->S : len;
-      for (int32_t g = 0; g < L->Hkv; ++g) {
-        double* mn = out + ((((int64_t)b * L->Hkv + g) * L->max_blocks + j) * 2 + 0) * L->D;
-        double* mx = mn + L->D;
-        for (int32_t c = 0; c < L->D; ++c) {
-          double lo = INFINITY, hi = -INFINITY;
-          for (int32_t t = j * L->S; t < t_end; ++t) {
-            double v = kv_value(L, k_pool, k_scales, page, g, t - j * L->S, c);
-            if (v < lo) lo = v;
-            if (v > hi) hi = v;
-          }
-          mn[c] = lo;
-          mx[c] = hi;
-        }
-      }
+      for (int32_t g = 0; g < L->Hkv; ++g) block_min_max(L, k_pool, k_scales, page, b, g, j, len, out);
     }
   }
   return OR_OK;
@@ -208,10 +214,10 @@ static int cand_cmp(const void* pa, const void* pb) {
   return (a->j > b->j) - (a->j < b->j);
 }
 
-int or_select(const or_layout* L, const double* W, const int32_t* seq_lens,
-              int32_t k, int32_t* sel) {
+int or_select_window(const or_layout* L, const double* W, const int32_t* seq_lens,
+                     int32_t k, int32_t recent, int32_t* sel) {
   if (!layout_ok(L) || !W || !seq_lens || !sel) return OR_EARG;
-  if (k < 2) return OR_EARG;
+  if (recent < 1 || k < recent + 1) return OR_EARG;
   cand_t* cands = (cand_t*)malloc(sizeof(cand_t) * (size_t)(L->max_blocks > 0 ? L->max_blocks : 1));
   unsigned char* chosen = (unsigned char*)malloc((size_t)(L->max_blocks > 0 ? L->max_blocks : 1));
   if (!cands || !chosen) {
@@ -234,16 +240,17 @@ int or_select(const or_layout* L, const double* W, const int32_t* seq_lens,
       if (nb <= k) {
         for (int32_t j = 0; j < nb; ++j) chosen[j] = 1;
       } else {
-        chosen[0] = 1;       /* attention sink */
-        chosen[nb - 1] = 1;  /* newest block   */
+        /* nb > k >= recent + 1, so the sink and the window do not meet */
+        chosen[0] = 1;                                       /* attention sink */
+        for (int32_t j = nb - recent; j < nb; ++j) chosen[j] = 1;  /* recent window */
         int32_t n = 0;
-        for (int32_t j = 1; j <= nb - 2; ++j) {
+        for (int32_t j = 1; j < nb - recent; ++j) {
           cands[n].w = w[j];
           cands[n].j = j;
           ++n;
         }
         qsort(cands, (size_t)n, sizeof(cand_t), cand_cmp);
-        for (int32_t i = 0; i < k - 2; ++i) chosen[cands[i].j] = 1;
+        for (int32_t i = 0; i < k - 1 - recent; ++i) chosen[cands[i].j] = 1;
       }
       int32_t pos = 0;
       for (int32_t j = 0; j < nb; ++j)
@@ -254,6 +261,50 @@ int or_select(const or_layout* L, const double* W, const int32_t* seq_lens,
   free(cands);
   free(chosen);
   return rc;
+}
+
+int or_select(const or_layout* L, const double* W, const int32_t* seq_lens,
+              int32_t k, int32_t* sel) {
+  if (k < 2) return OR_EARG;
+  return or_select_window(L, W, seq_lens, k, 1, sel);
+}
+
+/* ------------------------------------------------------------------ */
+/* score smoothing across decode steps                                 */
+/* ------------------------------------------------------------------ */
+
+int or_ema_scores(const or_layout* L, const double* W, const int32_t* seq_lens,
+                  double alpha, double* state, double* Wout) {
+  if (!layout_ok(L) || !W || !seq_lens || !state || !Wout) return OR_EARG;
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return OR_EARG;
+  const double beta = 1.0 - alpha;  /* the history's weight */
+  for (int32_t b = 0; b < L->B; ++b) {
+    int32_t len = seq_lens[b];
+    if (!len_ok(L, len)) return OR_ERANGE;
+    int32_t nb = num_blocks(L, len);
+    for (int32_t g = 0; g < L->Hkv; ++g) {
+      int64_t row = ((int64_t)b * L->Hkv + g) * L->max_blocks;
+      for (int32_t j = 0; j < L->max_blocks; ++j) {
+        if (j >= nb) {
+          Wout[row + j] = -INFINITY;
+          continue;
+        }
+        double now = W[row + j];
+        double hist = state[row + j];
+        double s;
+        if (isnan(hist)) {
+          s = now;  /* a block with no history yet */
+        } else {
+          double a = alpha * now;
+          double h = beta * hist;
+          s = a + h;
+        }
+        state[row + j] = s;
+        Wout[row + j] = s;
+      }
+    }
+  }
+  return OR_OK;
 }
 
 /* ------------------------------------------------------------------ */
@@ -487,5 +538,67 @@ int or_hot_step(int32_t nb, int32_t ns, int32_t k, int64_t step,
   }
   free(in_sel);
   free(vict);
+  return OR_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* appending the decode token                                          */
+/* ------------------------------------------------------------------ */
+
+static size_t elem_bytes(const or_layout* L) {
+  return L->kv_dtype == 0 ? 4 : (L->kv_dtype == 1 ? 2 : 1);
+}
+
+int or_append_token(const or_layout* L, const void* k_new, const void* v_new,
+                    const float* k_new_scales, const float* v_new_scales,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                    double* summ, void* host_k, void* host_v,
+                    float* host_k_scales, float* host_v_scales) {
+  if (!layout_ok(L) || !k_new || !v_new || !block_table || !seq_lens || !k_pool || !v_pool || !summ)
+    return OR_EARG;
+  const int fp8 = L->kv_dtype == 2;
+  if (fp8 && (!k_new_scales || !v_new_scales || !k_scales || !v_scales)) return OR_EARG;
+  if ((host_k != NULL) != (host_v != NULL)) return OR_EARG;
+  if (host_k && fp8 && (!host_k_scales || !host_v_scales)) return OR_EARG;
+  const size_t eb = elem_bytes(L);
+  const int32_t S = L->S, D = L->D, T = L->S < 32 ? L->S : 32;
+  const int32_t groups = fp8 ? D / L->quant_group : 0;
+  for (int32_t b = 0; b < L->B; ++b) {
+    int32_t len = seq_lens[b];
+    if (!len_ok(L, len)) return OR_ERANGE;
+    if (len == 0) continue;  /* nothing to append */
+    int32_t t = len - 1, j = t / S, s = t % S;
+    int32_t page = block_table[(int64_t)b * L->max_blocks + j];
+    if (page < 0 || page >= L->num_pages) return OR_ERANGE;
+    for (int32_t g = 0; g < L->Hkv; ++g) {
+      int64_t tile = (int64_t)page * L->Hkv + g;  /* (page, head) tile */
+      int64_t src = ((int64_t)b * L->Hkv + g) * D;
+      for (int32_t c = 0; c < D; ++c) {
+        int64_t kd = (tile * S + s) * D + c;                               /* [S][D] */
+        int64_t vd = ((tile * (S / T) + s / T) * D + c) * T + s % T;       /* [S/T][D][T] */
+        memcpy((char*)k_pool + kd * eb, (const char*)k_new + (src + c) * eb, eb);
+        memcpy((char*)v_pool + vd * eb, (const char*)v_new + (src + c) * eb, eb);
+      }
+      for (int32_t q = 0; q < groups; ++q) {
+        k_scales[(tile * S + s) * groups + q] = k_new_scales[((int64_t)b * L->Hkv + g) * groups + q];
+        v_scales[(tile * S + s) * groups + q] = v_new_scales[((int64_t)b * L->Hkv + g) * groups + q];
+      }
+      /* the block's summary over its valid tokens, the new one included */
+      block_min_max(L, k_pool, k_scales, page, b, g, j, len, summ);
+      /* a block that is now full is sealed: it goes to the host tier */
+      if (host_k && len % S == 0) {
+        int64_t hb = ((int64_t)b * L->Hkv + g) * L->max_blocks + j;  /* host tile */
+        size_t tile_bytes = (size_t)S * D * eb;
+        memcpy((char*)host_k + hb * (int64_t)tile_bytes, (const char*)k_pool + tile * (int64_t)tile_bytes, tile_bytes);
+        memcpy((char*)host_v + hb * (int64_t)tile_bytes, (const char*)v_pool + tile * (int64_t)tile_bytes, tile_bytes);
+        if (fp8) {
+          size_t sc = (size_t)S * groups;
+          memcpy(host_k_scales + hb * (int64_t)sc, k_scales + tile * (int64_t)sc, sc * sizeof(float));
+          memcpy(host_v_scales + hb * (int64_t)sc, v_scales + tile * (int64_t)sc, sc * sizeof(float));
+        }
+      }
+    }
+  }
   return OR_OK;
 }

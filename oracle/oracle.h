@@ -105,6 +105,26 @@ int or_bounds(const or_layout* L, const double* q, const double* summ,
 int or_select(const or_layout* L, const double* W, const int32_t* seq_lens,
               int32_t k, int32_t* sel);
 
+/* The same selection with a recent window of `recent` >= 1 newest blocks
+ * ("SparDA…" §4.2: besides the sink, the most recent 512 or 1024 tokens
+ * are kept by default): if nb <= k every block; otherwise block 0, blocks
+ * nb-recent..nb-1 and the k-1-recent best of blocks 1..nb-recent-1 under
+ * (W descending, block id ascending).  Requires k >= recent + 1; recent = 1
+ * is or_select. */
+int or_select_window(const or_layout* L, const double* W, const int32_t* seq_lens,
+                     int32_t k, int32_t recent, int32_t* sel);
+
+/* Score smoothing across decode steps ("SparDA…" §6.1: the score a block is
+ * ranked by mixes 70% of this step's value with 30% of its history).  Per
+ * (b, g) and block j < nb_b:
+ *   state[j] = isnan(state[j]) ? W[j] : alpha*W[j] + (1-alpha)*state[j]
+ * (each product and the sum rounded to fp64 as written, 1-alpha computed in
+ * fp64; NaN marks a block with no history yet), and Wout[j] = state[j];
+ * Wout[j] = -inf and state[j] untouched for j >= nb_b.  state and Wout are
+ * [B][Hkv][max_blocks]; 0 <= alpha <= 1. */
+int or_ema_scores(const or_layout* L, const double* W, const int32_t* seq_lens,
+                  double alpha, double* state, double* Wout);
+
 /* Softmax attention of every query head over the tokens of its group's
  * selected blocks (t < len only), two passes (max, then sums):
  *   s_t = sm_scale * q_h . K_t ;  out_h = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m)
@@ -140,6 +160,26 @@ int or_hot_step(int32_t nb, int32_t ns, int32_t k, int64_t step,
                 int32_t slot_base, const int32_t* sel, int32_t* pt,
                 int32_t* owner, int64_t* stamp, int32_t* miss_list,
                 int32_t* miss_cnt);
+
+/* Appends one decode token per sequence ("KV 稀疏化" §7: the newest KV is
+ * written to the device cache; a block that is no longer being written
+ * sinks to the host tier).  seq_lens[b] counts the new token; for len > 0,
+ * t = len-1 goes to block j = t/S, slot s = t%S of page block_table[b][j]:
+ *   K[page][g][s][c] = k_new[b][g][c], the V element (page, g, s, c) =
+ *   v_new[b][g][c] (V tile [S/T][D][T]), and for fp8 the token's group
+ *   scales from k_new_scales / v_new_scales [B][Hkv][D/quant_group];
+ * then the summary of block j becomes the min/max over its valid tokens
+ * (recomputed from the pool), and when len % S == 0 and host_k is given
+ * the block is sealed: its K and V tiles (and scales) are copied byte for
+ * byte to host_k/host_v [B][Hkv][max_blocks][tile] (scales
+ * [B][Hkv][max_blocks][S][D/quant_group]).  k_new/v_new hold kv_dtype
+ * elements (fp8: codes); len == 0 sequences are skipped. */
+int or_append_token(const or_layout* L, const void* k_new, const void* v_new,
+                    const float* k_new_scales, const float* v_new_scales,
+                    const int32_t* block_table, const int32_t* seq_lens,
+                    void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                    double* summ, void* host_k, void* host_v,
+                    float* host_k_scales, float* host_v_scales);
 
 #ifdef __cplusplus
 }
