@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 1
+#define KVS_ABI_VERSION 2
 
 typedef enum kvs_status {
   KVS_OK = 0,
@@ -210,6 +210,107 @@ kvs_status kvs_select_topk_append(const kvs_layout* layout, const void* q, const
                                   const int32_t* seq_lens, void* summaries, int32_t k, int32_t* sel,
                                   double* bounds_out, void* workspace, size_t workspace_bytes,
                                   void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_append_token -- write the decode token into the paged cache, update
+ * its block's summary, and seal a block that has just filled into the host
+ * tier
+ *
+ * Page "KV 稀疏化", §7 "HiSparse": the newest KV is written to the device
+ * cache, and KV that is no longer being written sinks to host memory (the
+ * tier kvs_hot_lookup_swapin reads back).  For every sequence b with
+ * len = seq_lens[b] > 0 (the count includes the new token), token t = len-1
+ * goes to block j = t/S, slot s = t%S of page block_table[b][j], for every KV
+ * head g:
+ *   K pool [page][g][s][c] = k_new[b][g][c]; V pool element (page, g, s, c)
+ *   (run s/T, column s%T) = v_new[b][g][c]; fp8: the token's group scales
+ *   [page][g][s][:] = k_new_scales / v_new_scales [b][g][:];
+ *   summary (b, g, j) = min/max of the block's valid tokens.  It is
+ *   computed incrementally: the stored summary must cover tokens jS..t-1
+ *   (as kvs_build_summaries or earlier appends leave it); s = 0 starts the
+ *   block afresh;
+ *   when len % S == 0 and host_k is given, the block's K and V tiles (and
+ *   fp8 scales) are copied byte for byte to host tile [b][g][j].
+ * Sequences with len == 0 are skipped.
+ *
+ *  k_new/v_new  [B][Hkv][D] kv_dtype (fp8: E4M3FN codes, quantised by the
+ *               caller)
+ *  k_new_scales/v_new_scales  fp8 only: [B][Hkv][D/quant_group] fp32
+ *  block_table  [B][MB] int32;  k_pool/v_pool/k_scales/v_scales  in/out
+ *  host_k/host_v  optional HOST tier [B][Hkv][MB][S][D] (K) and
+ *               [B][Hkv][MB][S/T][D][T] (V), pinned with hipHostMalloc (the
+ *               layout kvs_hot_lookup_swapin reads); both NULL = no sealing
+ *  host_k_scales/host_v_scales  fp8 with a host tier: [B][Hkv][MB][S][D/qg]
+ *  summaries    [B][Hkv][MB][2][D] in/out (kvs_build_summaries layout)
+ * A page must not be shared by two sequences that append in the same call.
+ * Errors: INVALID_ARG (also a host tier that is not pinned), UNSUPPORTED,
+ * HIP.  Device flags: KVS_DEVERR_SEQLEN, KVS_DEVERR_TABLE (the sequence is
+ * skipped).
+ * ---------------------------------------------------------------------- */
+typedef struct kvs_append_args {
+  const void* k_new;
+  const void* v_new;
+  const float* k_new_scales;
+  const float* v_new_scales;
+  const int32_t* block_table;
+  void* k_pool;
+  void* v_pool;
+  float* k_scales;
+  float* v_scales;
+  void* host_k;
+  void* host_v;
+  float* host_k_scales;
+  float* host_v_scales;
+} kvs_append_args;
+
+kvs_status kvs_append_token(const kvs_layout* layout, const kvs_append_args* append,
+                            const int32_t* seq_lens, void* summaries, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_select_topk_ex -- kvs_select_topk with the selection options of
+ * "SparDA…" and an optional token append in the same call
+ *
+ *  opts->recent_blocks  R >= 1: besides the sink, the R newest blocks are
+ *               always kept ("SparDA…" §4.2: the most recent 512 or 1024
+ *               tokens are kept by default).  If nb(b) <= k every block;
+ *               otherwise block 0, blocks nb-R..nb-1 and the k-1-R best of
+ *               blocks 1..nb-R-1.  Needs k >= R + 1.  R = 1 is
+ *               kvs_select_topk.
+ *  opts->use_ema, ema_alpha, ema_state  score smoothing across decode
+ *               steps ("SparDA…" §6.1: 70% of the current score, 30% of
+ *               its history).  Per (b, g) and block j < nb(b):
+ *                 state[j] = isnan(state[j]) ? W[j]
+ *                            : alpha*W[j] + (1-alpha)*state[j]
+ *               with each product and the sum rounded to fp64 separately;
+ *               blocks are ranked by state[j].  ema_state is
+ *               [B][Hkv][MB] fp64 in/out (NaN = no history; reset a row when
+ *               its sequence slot is reused); entries j >= nb(b) are left
+ *               untouched.  0 <= alpha <= 1.
+ *  opts = NULL  R = 1, no smoothing.
+ *  append       NULL, or the token append of kvs_append_token (same
+ *               arguments), done before the blocks are scored.  Without
+ *               bounds_out and smoothing it runs as one more workgroup per
+ *               (sequence, KV head) of the scoring launch, beside the
+ *               workgroups that score (the newest block is always kept, so
+ *               its own score is not used); otherwise as a launch of its own
+ *               first.
+ *  bounds_out   optional [B][Hkv][MB] fp64: the unsmoothed W.
+ *  summaries    in/out when append is given, else only read.
+ *  others       as for kvs_select_topk.
+ * Matrix-core scoring (see kvs_select_topk) is not used with smoothing.
+ * Errors: as kvs_select_topk and kvs_append_token.
+ * ---------------------------------------------------------------------- */
+typedef struct kvs_select_opts {
+  int32_t recent_blocks;
+  int32_t use_ema;
+  double ema_alpha;
+  double* ema_state;
+} kvs_select_opts;
+
+kvs_status kvs_select_topk_ex(const kvs_layout* layout, const void* q, void* summaries,
+                              const int32_t* seq_lens, int32_t k, const kvs_select_opts* opts,
+                              const kvs_append_args* append, int32_t* sel, double* bounds_out,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_sparse_decode_attn -- attention over the selected blocks only

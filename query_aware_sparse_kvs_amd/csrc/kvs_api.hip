@@ -221,36 +221,115 @@ kvs_status kvs_build_summaries(const kvs_layout* L, const void* k_pool, const fl
 
 namespace {
 
-// kvs_select_topk's checks and launches; with `app`, each sequence's newest
-// block summary is also rebuilt from K -- by one more workgroup per
-// (sequence, KV head) inside the scoring launch when no bounds are returned,
-// else by a summaries launch before scoring.
+// Validates a kvs_append_args block and fills the kernels' argument block
+// (the host tier is passed to the kernels through its device aliases).
+kvs_status make_append(const kvs_layout* L, const kvs_append_args* ap, const int32_t* seq_lens, void* summaries,
+                       kvs::AppendArgs* out) {
+  if (!ap || !seq_lens || !summaries) return fail(KVS_ERR_INVALID_ARG, "append, seq_lens and summaries must be non-NULL");
+  if (!ap->k_new || !ap->v_new || !ap->block_table || !ap->k_pool || !ap->v_pool)
+    return fail(KVS_ERR_INVALID_ARG, "k_new, v_new, block_table, k_pool and v_pool must be non-NULL");
+  const bool fp8 = L->kv_dtype == KVS_FP8_E4M3;
+  if (fp8 && (!ap->k_new_scales || !ap->v_new_scales || !ap->k_scales || !ap->v_scales))
+    return fail(KVS_ERR_INVALID_ARG, "fp8 K/V need new-token and pool scales");
+  if ((ap->host_k != nullptr) != (ap->host_v != nullptr))
+    return fail(KVS_ERR_INVALID_ARG, "host_k and host_v must both be given or both be NULL");
+  if (ap->host_k && fp8 && (!ap->host_k_scales || !ap->host_v_scales))
+    return fail(KVS_ERR_INVALID_ARG, "an fp8 host tier needs host scales");
+  if (!aligned(ap->k_pool, 16) || !aligned(ap->v_pool, 16) || !aligned(summaries, 16) ||
+      (ap->host_k && (!aligned(ap->host_k, 16) || !aligned(ap->host_v, 16))))
+    return fail(KVS_ERR_INVALID_ARG, "pools, summaries and host tier must be 16-byte aligned");
+  void* dev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (ap->host_k) {
+    void* host[4] = {ap->host_k, ap->host_v, ap->host_k_scales, ap->host_v_scales};
+    for (int i = 0; i < (fp8 ? 4 : 2); ++i) {
+      hipError_t e = hipHostGetDevicePointer(&dev[i], host[i], 0);
+      if (e != hipSuccess || !dev[i]) {
+        (void)hipGetLastError();
+        return fail(KVS_ERR_INVALID_ARG, "the host tier must be pinned host memory (hipHostMalloc)");
+      }
+    }
+  }
+  kvs::AppendArgs a{};
+  a.k_new = ap->k_new;
+  a.v_new = ap->v_new;
+  a.k_new_scales = ap->k_new_scales;
+  a.v_new_scales = ap->v_new_scales;
+  a.block_table = ap->block_table;
+  a.seq_lens = seq_lens;
+  a.k_pool = ap->k_pool;
+  a.v_pool = ap->v_pool;
+  a.k_scales = ap->k_scales;
+  a.v_scales = ap->v_scales;
+  a.summ = summaries;
+  a.host_k = dev[0];
+  a.host_v = dev[1];
+  a.host_ks = static_cast<float*>(dev[2]);
+  a.host_vs = static_cast<float*>(dev[3]);
+  a.B = L->num_seqs;
+  a.Hkv = L->num_kv_heads;
+  a.D = L->head_dim;
+  a.S = L->block_size;
+  a.MB = L->max_blocks;
+  a.P = L->num_pages;
+  a.qg = fp8 ? L->quant_group : 0;
+  *out = a;
+  return KVS_OK;
+}
+
+// Selection options after validation.
+struct SelectOpts {
+  int recent = 1;
+  bool ema = false;
+  double alpha = 1.0;
+  double* state = nullptr;
+};
+
+// kvs_select_topk's checks and launches.  With `app`, each sequence's newest
+// block summary is also rebuilt from K; with `tok`, the decode token is
+// appended -- either by one more workgroup per (sequence, KV head) inside the
+// scoring launch (no bounds returned, no smoothing), else by a launch of its
+// own before scoring.
 kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries, const int32_t* seq_lens, int32_t k,
                        int32_t* sel, double* bounds_out, void* workspace, size_t workspace_bytes, void* stream,
-                       const kvs::SummArgs* app) {
+                       const kvs::SummArgs* app, const SelectOpts& opt, const kvs_append_args* tok_in) {
   kvs_status st = check_layout(L, true);
   if (st != KVS_OK) return st;
   if (!q || !summaries || !seq_lens || !sel)
     return fail(KVS_ERR_INVALID_ARG, "q, summaries, seq_lens and sel must be non-NULL");
   if (k < 2 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [2, max_blocks]");
+  if (opt.recent < 1 || k < opt.recent + 1)
+    return fail(KVS_ERR_INVALID_ARG, "recent_blocks must be >= 1 and k >= recent_blocks + 1");
+  if (opt.ema && (!opt.state || !aligned(opt.state, 8) || !(opt.alpha >= 0.0 && opt.alpha <= 1.0)))
+    return fail(KVS_ERR_INVALID_ARG, "smoothing needs an 8-byte aligned ema_state and 0 <= ema_alpha <= 1");
   if (!workspace || workspace_bytes < select_ws(L))
     return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_select_workspace_size()");
   if (!aligned(summaries, 16) || !aligned(workspace, 16) || (bounds_out && !aligned(bounds_out, 8)))
     return fail(KVS_ERR_INVALID_ARG, "summaries/workspace must be 16-byte aligned, bounds_out 8-byte");
+  kvs::AppendArgs tok{};
+  if (tok_in && (st = make_append(L, tok_in, seq_lens, const_cast<void*>(summaries), &tok)) != KVS_OK) return st;
   unsigned int* err = nullptr;
   if ((st = error_word(&err)) != KVS_OK) return st;
+  tok.err = err;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int summ_kind = L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32;
   const int G = L->num_q_heads / L->num_kv_heads;
   kvs::SummArgs ap{};
-  bool fuse = false;
+  int fuse = 0;  // the scoring launch's extra-workgroup role (BoundArgs::append)
   if (app) {
     ap = *app;
     ap.err = err;
-    fuse = !bounds_out;
+    fuse = bounds_out ? 0 : 1;
     if (!fuse) {  // bounds must see the new summary: rebuild it first
       hipError_t e = kvs::launch_summaries(ap, kind_of(L->kv_dtype), s);
       if (e != hipSuccess) return hip_status(e, "summaries launch");
+    }
+  } else if (tok_in) {
+    // fused only where the newest block's racing score is never used: it
+    // would reach bounds_out, and through smoothing the next steps
+    fuse = (bounds_out || opt.ema) ? 0 : 2;
+    if (!fuse) {
+      hipError_t e = kvs::launch_append(tok, kind_of(L->kv_dtype), s);
+      if (e != hipSuccess) return hip_status(e, "append launch");
     }
   }
   // Two implementations with identical selections.  The exact one spends a
@@ -260,7 +339,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   // of thousands of blocks (8 x 4 x 512: 15.0 vs 16.5 us; 256 x 4 x 512:
   // 108 vs 75 us).
   const long long blocks = (long long)L->num_seqs * L->num_kv_heads * L->max_blocks;
-  if (!bounds_out && blocks >= kSelectMfmaMinBlocks &&
+  if (!bounds_out && !opt.ema && blocks >= kSelectMfmaMinBlocks &&
       kvs::select_mfma_supported(kind_of(L->q_dtype), summ_kind, L->head_dim, L->max_blocks, G)) {
     kvs::SelMfmaArgs ma{};
     ma.q = q;
@@ -278,8 +357,10 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
     ma.S = L->block_size;
     ma.MB = L->max_blocks;
     ma.k = k;
-    ma.append = fuse ? 1 : 0;
+    ma.recent = opt.recent;
+    ma.append = fuse;
     ma.app = ap;
+    ma.tok = tok;
     return hip_status(kvs::launch_select_mfma(ma, s), "select launch");
   }
   kvs::BoundArgs ba{};
@@ -295,9 +376,14 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   ba.D = L->head_dim;
   ba.S = L->block_size;
   ba.MB = L->max_blocks;
-  ba.append = fuse ? 1 : 0;
+  ba.append = fuse;
   ba.app_kv = kind_of(L->kv_dtype);
   ba.app = ap;
+  ba.tok = tok;
+  ba.ema = opt.ema ? 1 : 0;
+  ba.ema_alpha = opt.alpha;
+  ba.ema_beta = 1.0 - opt.alpha;
+  ba.ema_state = opt.state;
   hipError_t e = kvs::launch_bounds(ba, kind_of(L->q_dtype), summ_kind, s);
   if (e != hipSuccess) return hip_status(e, "bounds launch");
   kvs::TopkArgs ta{};
@@ -309,6 +395,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   ta.S = L->block_size;
   ta.MB = L->max_blocks;
   ta.k = k;
+  ta.recent = opt.recent;
   return hip_status(kvs::launch_topk(ta, s), "top-k launch");
 }
 
@@ -319,7 +406,34 @@ extern "C" {
 kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summaries,
                            const int32_t* seq_lens, int32_t k, int32_t* sel, double* bounds_out,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr);
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr,
+                     SelectOpts{}, nullptr);
+}
+
+kvs_status kvs_select_topk_ex(const kvs_layout* L, const void* q, void* summaries, const int32_t* seq_lens,
+                              int32_t k, const kvs_select_opts* opts, const kvs_append_args* append, int32_t* sel,
+                              double* bounds_out, void* workspace, size_t workspace_bytes, void* stream) {
+  SelectOpts o;
+  if (opts) {
+    o.recent = opts->recent_blocks;
+    o.ema = opts->use_ema != 0;
+    o.alpha = opts->ema_alpha;
+    o.state = opts->ema_state;
+  }
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr, o,
+                     append);
+}
+
+kvs_status kvs_append_token(const kvs_layout* L, const kvs_append_args* append, const int32_t* seq_lens,
+                            void* summaries, void* stream) {
+  kvs_status st = check_layout(L, false);
+  if (st != KVS_OK) return st;
+  kvs::AppendArgs a{};
+  if ((st = make_append(L, append, seq_lens, summaries, &a)) != KVS_OK) return st;
+  unsigned int* err = nullptr;
+  if ((st = error_word(&err)) != KVS_OK) return st;
+  a.err = err;
+  return hip_status(kvs::launch_append(a, kind_of(L->kv_dtype), static_cast<hipStream_t>(stream)), "append launch");
 }
 
 kvs_status kvs_select_topk_append(const kvs_layout* L, const void* q, const void* k_pool, const float* k_scales,
@@ -347,7 +461,8 @@ kvs_status kvs_select_topk_append(const kvs_layout* L, const void* q, const void
   ap.qg = L->quant_group;
   ap.num_rebuild = 1;
   ap.newest = 1;
-  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, &ap);
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, &ap,
+                     SelectOpts{}, nullptr);
 }
 
 kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const void* q,

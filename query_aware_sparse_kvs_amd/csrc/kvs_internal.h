@@ -126,6 +126,28 @@ struct SummArgs {
   int32_t newest;  // 1: rebuild block nb(b)-1 of every sequence (first_block unused)
 };
 
+// One decode token per sequence written into its page, its block's summary
+// updated, and a block that has just filled copied to the host tier.
+struct AppendArgs {
+  const void* k_new;            // [B][Hkv][D] K/V storage kind
+  const void* v_new;
+  const float* k_new_scales;    // fp8: [B][Hkv][D/qg]
+  const float* v_new_scales;
+  const int32_t* block_table;   // [B][MB]
+  const int32_t* seq_lens;      // [B], the new token included
+  void* k_pool;                 // [P][Hkv][S][D]
+  void* v_pool;                 // [P][Hkv][S/T][D][T]
+  float* k_scales;              // fp8: [P][Hkv][S][D/qg]
+  float* v_scales;
+  void* summ;                   // [B][Hkv][MB][2][D], bf16 for bf16 K else fp32
+  void* host_k;                 // device aliases of the pinned host tier, or null
+  void* host_v;
+  float* host_ks;
+  float* host_vs;
+  unsigned int* err;
+  int32_t B, Hkv, D, S, MB, P, qg;
+};
+
 struct BoundArgs {
   const void* q;
   const void* summ;
@@ -134,9 +156,15 @@ struct BoundArgs {
   double* bounds_out;  // optional copy
   unsigned int* err;
   int32_t B, Hq, Hkv, D, S, MB;
-  int32_t append;      // 1: one more workgroup per (b, g) rebuilds the newest block's summary
-  int32_t app_kv;      // K storage kind of that rebuild (Kind; bf16 with bf16 summaries)
+  int32_t append;      // one more workgroup per (b, g): 1 rebuilds the newest block's
+                       // summary (app), 2 appends the decode token (tok)
+  int32_t app_kv;      // K storage kind of that work (Kind; bf16 with bf16 summaries)
   SummArgs app;
+  AppendArgs tok;
+  int32_t ema;         // 1: W is smoothed with ema_state before it is stored
+  double ema_alpha;    // weight of this step's score
+  double ema_beta;     // 1 - ema_alpha (fp64)
+  double* ema_state;   // [B][Hkv][MB] in/out, NaN = no history
 };
 
 struct TopkArgs {
@@ -144,6 +172,7 @@ struct TopkArgs {
   const int32_t* seq_lens;
   int32_t* sel;
   int32_t B, Hkv, S, MB, k;
+  int32_t recent;  // newest blocks always kept (>= 1)
 };
 
 struct SelMfmaArgs {
@@ -155,8 +184,10 @@ struct SelMfmaArgs {
   int32_t* sel;
   unsigned int* err;
   int32_t B, Hq, Hkv, G, D, S, MB, k;
+  int32_t recent;  // as in TopkArgs
   int32_t append;  // as in BoundArgs
   SummArgs app;
+  AppendArgs tok;
 };
 
 struct AttnArgs {
@@ -200,6 +231,7 @@ struct HotArgs {
 // launchers (return the launch status); kinds/shapes are validated by the
 // caller
 hipError_t launch_summaries(const SummArgs& a, int kv_kind, hipStream_t s);
+hipError_t launch_append(const AppendArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_bounds(const BoundArgs& a, int q_kind, int summ_kind, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G);

@@ -22,11 +22,17 @@
 // mapped to order-preserving 64-bit keys.  A most-significant-digit radix
 // select (8-bit digits, LDS histogram) over the high 32 bits, starting at
 // the first bit where the candidates' keys differ, finds the bucket of the
-// (k-2)-th largest key among blocks 1..nb-2; only when that bucket holds
+// (k-1-R)-th largest key among blocks 1..nb-R-1 (R = the recent window, the
+// newest blocks that are always kept; "SparDA…" §4.2 keeps the last 512 or
+// 1024 tokens); only when that bucket holds
 // more keys than are needed does a second select run on the low 32 bits of
 // the tied keys.  Ties on the full key go to the lowest block ids, the
 // (W desc, id asc) order.  A block-wide prefix sum writes the chosen ids in
 // ascending order.  Latency-bound.
+//
+// With score smoothing on, the bounds kernel ranks blocks by the smoothed
+// score alpha*W + (1-alpha)*history ("SparDA…" §6.1) instead of W itself.
+#include "kvs_append.h"
 #include "kvs_summarize.h"
 
 namespace kvs {
@@ -39,6 +45,24 @@ constexpr int kBoundBlocks = 64;  // blocks per bounds workgroup (lane = block)
 template <int G, int SK>
 constexpr int bound_waves() {
   return G >= 8 && SK == K_BF16 ? 8 : 4;
+}
+
+// Score smoothing across decode steps ("SparDA…" §6.1): the score a block is
+// ranked by is alpha * (this step's W) + (1 - alpha) * (its smoothed score of
+// the previous step), or W itself when the state holds NaN (no history).
+// The state keeps the result.  Each product and the sum are rounded to fp64
+// separately (no fused multiply-add), as the plain definition reads.
+__device__ __forceinline__ double smooth_score(double w, double* state, double alpha, double beta) {
+#pragma clang fp contract(off)
+  const double h = *state;
+  double r = w;
+  if (!__builtin_isnan(h)) {
+    const double x = alpha * w;
+    const double y = beta * h;
+    r = x + y;
+  }
+  *state = r;
+  return r;
 }
 
 template <int QK, int SK, int D, int G>
@@ -61,6 +85,15 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
     static_assert(sizeof(sm) >= kSummRed<D, NT> * sizeof(float), "summary reduction fits the chunk buffer");
     float* red = reinterpret_cast<float*>(sm);
+    if (a.append == 2) {  // the decode token: written, folded into its block's summary
+      if constexpr (SK == K_BF16)
+        append_token_unit<K_BF16, D, NT>(a.tok, b, g);
+      else if (a.app_kv == K_FP8)
+        append_token_unit<K_FP8, D, NT>(a.tok, b, g);
+      else
+        append_token_unit<K_F32, D, NT>(a.tok, b, g);
+      return;
+    }
     if constexpr (SK == K_BF16) {
       rebuild_newest_summary<K_BF16, D, NT>(a.app, b, g, red);
     } else if (a.app_kv == K_FP8) {
@@ -176,8 +209,9 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
       }
     }
     const long long wi = ((long long)b * a.Hkv + g) * a.MB + j0 + lane;
-    a.W[wi] = w;
     if (a.bounds_out) a.bounds_out[wi] = w;
+    if (a.ema && valid) w = smooth_score(w, a.ema_state + wi, a.ema_alpha, a.ema_beta);
+    a.W[wi] = w;
   }
 }
 
@@ -288,7 +322,8 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
     return;
   }
-  const int M = k - 2;  // free picks among blocks 1..nb-2
+  const int R = a.recent;  // newest blocks always kept
+  const int M = k - 1 - R;  // free picks among blocks 1..nb-R-1
 
   bool cand[PT];
   unsigned hi[PT], lo[PT];
@@ -296,7 +331,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int j = j0 + i;
-    cand[i] = i < per && j >= 1 && j <= nb - 2;
+    cand[i] = i < per && j >= 1 && j < nb - R;
     const unsigned long long key = cand[i] ? order_key(wv[i]) : 0ull;
     hi[i] = (unsigned)(key >> 32);
     lo[i] = (unsigned)key;
@@ -367,7 +402,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     const int j = j0 + i;
     if (i >= per || j >= nb) continue;
     bool take;
-    if (j == 0 || j == nb - 1) {
+    if (j == 0 || j >= nb - R) {
       take = true;
     } else if (!cand[i] || M == 0) {
       take = false;

@@ -18,13 +18,15 @@
 // refine_kernel -- one 512-thread workgroup per (sequence, KV head).
 // |W32 - W| <= eps = 2^-13 * max A (+ a floor for underflow) bounds the
 // rounding of the 2D-term fp32 sums (an eight-fold margin over the worst
-// case).  A radix select over the candidates' (blocks 1..nb-2) W32 gives the
-// M-th and (M+1)-th largest values vM, vM1 (M = k-2): a block with
+// case).  A radix select over the candidates' (blocks 1..nb-R-1, R newest
+// blocks always kept) W32 gives the
+// M-th and (M+1)-th largest values vM, vM1 (M = k-1-R): a block with
 // W32 > vM1 + 2*eps is in the exact top M, one with W32 < vM - 2*eps is not.
 // Only the blocks in between (a handful) get their bound recomputed exactly
 // -- fp64, ascending channels, the sum of the plain definition -- one thread
 // per (block, head), and are ranked by (W desc, id asc) for the places left.
 // The selection therefore equals the one the exact scores give.
+#include "kvs_append.h"
 #include "kvs_summarize.h"
 
 namespace kvs {
@@ -94,7 +96,10 @@ __global__ __launch_bounds__(256, 4) void scores32_kernel(SelMfmaArgs a) {
   const int g = blockIdx.y, b = blockIdx.z;
   if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
     __shared__ float red[kSummRed<D>];
-    rebuild_newest_summary<K_BF16, D>(a.app, b, g, red);
+    if (a.append == 2)  // the decode token: written, folded into its block's summary
+      append_token_unit<K_BF16, D, 256>(a.tok, b, g);
+    else
+      rebuild_newest_summary<K_BF16, D>(a.app, b, g, red);
     return;
   }
   const int tid = threadIdx.x, lane = tid & 63;
@@ -200,12 +205,10 @@ __global__ __launch_bounds__(kFT) void refine_kernel(SelMfmaArgs a) {
     for (int i = tid; i < k; i += kFT) out[i] = i < nb ? i : -1;
     return;
   }
-  const int M = k - 2;  // places besides the sink and the newest block
+  const int RW = a.recent;
+  const int M = k - 1 - RW;  // places besides the sink and the RW newest blocks
   if (M == 0) {
-    if (tid == 0) {
-      out[0] = 0;
-      out[1] = nb - 1;
-    }
+    for (int i = tid; i < k; i += kFT) out[i] = i == 0 ? 0 : nb - RW + (i - 1);
     return;
   }
 
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(kFT) void refine_kernel(SelMfmaArgs a) {
 #pragma unroll
   for (int i = 0; i < kFPT; ++i) {
     const int j = j0 + i;
-    cand[i] = j >= 1 && j <= nb - 2;
+    cand[i] = j >= 1 && j < nb - RW;
     key[i] = cand[i] ? order_u32(wv[i]) : 0u;
     if (cand[i]) {
       kmin = min(kmin, key[i]);
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(kFT) void refine_kernel(SelMfmaArgs a) {
     const int j = j0 + i;
     if (j >= nb) continue;
     bool take;
-    if (j == 0 || j == nb - 1)
+    if (j == 0 || j >= nb - RW)
       take = true;
     else if (cls[i] == 1)
       take = true;

@@ -65,6 +65,45 @@ class Layout:
         return torch.bfloat16 if self.kv_dtype == KVS_BF16 else torch.float32
 
 
+class _CAppendArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_new", "v_new", "k_new_scales", "v_new_scales", "block_table", "k_pool", "v_pool",
+        "k_scales", "v_scales", "host_k", "host_v", "host_k_scales", "host_v_scales")]
+
+
+class _CSelectOpts(ctypes.Structure):
+    _fields_ = [("recent_blocks", ctypes.c_int32), ("use_ema", ctypes.c_int32),
+                ("ema_alpha", ctypes.c_double), ("ema_state", ctypes.c_void_p)]
+
+
+@dataclass
+class AppendArgs:
+    """Tensors of kvs_append_args (include/kvs.h); host_* are pinned host
+    tensors or None (no sealing)."""
+    k_new: torch.Tensor
+    v_new: torch.Tensor
+    k_new_scales: torch.Tensor | None
+    v_new_scales: torch.Tensor | None
+    block_table: torch.Tensor
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_scales: torch.Tensor | None = None
+    v_scales: torch.Tensor | None = None
+    host_k: torch.Tensor | None = None
+    host_v: torch.Tensor | None = None
+    host_k_scales: torch.Tensor | None = None
+    host_v_scales: torch.Tensor | None = None
+
+
+@dataclass
+class SelectOpts:
+    """kvs_select_opts: recent window and score smoothing."""
+    recent_blocks: int = 1
+    use_ema: bool = False
+    ema_alpha: float = 0.7
+    ema_state: torch.Tensor | None = None
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -77,6 +116,9 @@ def _load():
         "kvs_select_topk": (i32, [LP, P, P, P, i32, P, P, P, sz, P]),
         "kvs_select_topk_append": (i32, [LP, P, P, P, P, P, P, i32, P, P, P, sz, P]),
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
+        "kvs_append_token": (i32, [LP, ctypes.POINTER(_CAppendArgs), P, P, P]),
+        "kvs_select_topk_ex": (i32, [LP, P, P, P, i32, ctypes.POINTER(_CSelectOpts),
+                                     ctypes.POINTER(_CAppendArgs), P, P, P, sz, P]),
         "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvs_select_workspace_size": (sz, [LP, i32]),
         "kvs_attn_workspace_size": (sz, [LP, i32]),
@@ -94,6 +136,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
+            "kvs_append_token", "kvs_select_topk_ex",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
 
@@ -194,6 +237,64 @@ def kvs_select_topk_append(layout: Layout, q, k_pool, k_scales, block_table, seq
         _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
         ws, workspace.numel() if workspace is not None else 0,
         _stream(stream)), "kvs_select_topk_append")
+
+
+def _append_struct(L: Layout, a: AppendArgs) -> _CAppendArgs:
+    units = L.num_seqs * L.num_kv_heads
+    tile = L.num_kv_heads * L.block_size * L.head_dim
+    qg = L.quant_group
+    host_n = units * L.max_blocks * L.block_size * L.head_dim
+    dt = _pool_dtype(L)
+    return _CAppendArgs(
+        _ptr(a.k_new, "k_new", dt, units * L.head_dim),
+        _ptr(a.v_new, "v_new", dt, units * L.head_dim),
+        _ptr(a.k_new_scales, "k_new_scales", torch.float32, units * L.head_dim // qg if qg else None),
+        _ptr(a.v_new_scales, "v_new_scales", torch.float32, units * L.head_dim // qg if qg else None),
+        _ptr(a.block_table, "block_table", torch.int32, L.num_seqs * L.max_blocks),
+        _ptr(a.k_pool, "k_pool", dt, L.num_pages * tile),
+        _ptr(a.v_pool, "v_pool", dt, L.num_pages * tile),
+        _ptr(a.k_scales, "k_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(a.v_scales, "v_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(a.host_k, "host_k", dt, host_n, device=False, pinned=True),
+        _ptr(a.host_v, "host_v", dt, host_n, device=False, pinned=True),
+        _ptr(a.host_k_scales, "host_k_scales", torch.float32, host_n // qg if qg else None, device=False,
+             pinned=True),
+        _ptr(a.host_v_scales, "host_v_scales", torch.float32, host_n // qg if qg else None, device=False,
+             pinned=True))
+
+
+def kvs_append_token(layout: Layout, append: AppendArgs, seq_lens, summaries, stream=None) -> None:
+    L = layout
+    ca = _append_struct(L, append)
+    _check(_lib.kvs_append_token(
+        ctypes.byref(L.c()), ctypes.byref(ca),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
+        _stream(stream)), "kvs_append_token")
+
+
+def kvs_select_topk_ex(layout: Layout, q, summaries, seq_lens, k: int, opts: SelectOpts | None,
+                       append: AppendArgs | None, sel, bounds_out, workspace, stream=None) -> None:
+    L = layout
+    co = None
+    if opts is not None:
+        co = _CSelectOpts(int(opts.recent_blocks), 1 if opts.use_ema else 0, float(opts.ema_alpha),
+                          _ptr(opts.ema_state, "ema_state", torch.float64,
+                               L.num_seqs * L.num_kv_heads * L.max_blocks))
+    ca = _append_struct(L, append) if append is not None else None
+    ws = _ptr(workspace, "workspace", torch.uint8)
+    _check(_lib.kvs_select_topk_ex(
+        ctypes.byref(L.c()),
+        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        int(k),
+        ctypes.byref(co) if co is not None else None,
+        ctypes.byref(ca) if ca is not None else None,
+        _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
+        _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
+        ws, workspace.numel() if workspace is not None else 0,
+        _stream(stream)), "kvs_select_topk_ex")
 
 
 def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(kvs):
 
 
 def test_abi_version_and_status_strings(kvs):
-    assert kvs.kvs_abi_version() == 1
+    assert kvs.kvs_abi_version() == 2
     for st in range(5):
         assert kvs.kvs_status_string(st).startswith("KVS_")
     assert "unknown" in kvs.kvs_status_string(99)
@@ -137,3 +137,37 @@ def test_summaries_and_hot_argument_checks(kvs):
     assert hot(4, 5000) == kvs.KVS_ERR_UNSUPPORTED
     assert hot(0, 4) == kvs.KVS_ERR_INVALID_ARG
     assert hot(4, 4, step=-1) == kvs.KVS_ERR_INVALID_ARG
+
+
+def _append_args(kvs, **kw):
+    base = {n: FAKE.value for n, _ in kvs._CAppendArgs._fields_}
+    for n in ("k_new_scales", "v_new_scales", "k_scales", "v_scales", "host_k", "host_v",
+              "host_k_scales", "host_v_scales"):
+        base[n] = None
+    base.update(kw)
+    return kvs._CAppendArgs(**base)
+
+
+def test_append_and_select_ex_argument_checks(kvs):
+    lib = kvs.library()
+    L = _layout(kvs)
+    c = ctypes.byref(L.c())
+    ok = _append_args(kvs)
+    assert lib.kvs_append_token(c, None, FAKE, FAKE, None) == kvs.KVS_ERR_INVALID_ARG
+    assert lib.kvs_append_token(c, ctypes.byref(_append_args(kvs, k_new=None)), FAKE, FAKE, None) == 1
+    assert lib.kvs_append_token(c, ctypes.byref(_append_args(kvs, host_k=FAKE.value)), FAKE, FAKE, None) == 1
+    assert lib.kvs_append_token(c, ctypes.byref(_append_args(kvs, k_pool=0x100002)), FAKE, FAKE, None) == 1
+    fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
+    assert lib.kvs_append_token(ctypes.byref(fp8.c()), ctypes.byref(ok), FAKE, FAKE, None) == 1  # no scales
+
+    def sel_ex(k, recent=1, ema=0, alpha=0.7, state=FAKE.value, app=None):
+        o = kvs._CSelectOpts(recent, ema, alpha, state)
+        return lib.kvs_select_topk_ex(c, FAKE, FAKE, FAKE, k, ctypes.byref(o),
+                                      ctypes.byref(app) if app is not None else None,
+                                      FAKE, None, FAKE, 1 << 20, None)
+    assert sel_ex(4, recent=0) == kvs.KVS_ERR_INVALID_ARG
+    assert sel_ex(4, recent=4) == kvs.KVS_ERR_INVALID_ARG  # k < recent + 1
+    assert sel_ex(4, ema=1, alpha=1.5) == kvs.KVS_ERR_INVALID_ARG
+    assert sel_ex(4, ema=1, state=None) == kvs.KVS_ERR_INVALID_ARG
+    assert sel_ex(4, ema=1, state=0x100004) == kvs.KVS_ERR_INVALID_ARG  # misaligned state
+    assert sel_ex(4, app=_append_args(kvs, v_new=None)) == kvs.KVS_ERR_INVALID_ARG

@@ -1,0 +1,287 @@
+"""GPU parity of the decode-loop calls, through the C ABI, against the oracle
+on the same seeded inputs:
+
+  kvs_append_token     pools, fp8 scales and the host tier bit-exact,
+                       summaries equal by value, over many consecutive
+                       decode steps (blocks opened, filled and sealed,
+                       sequences of different lengths, empty sequences)
+  kvs_select_topk_ex   selections bit-exact, smoothing state bit-exact and
+                       bounds bit-exact, with a recent window and score
+                       smoothing over a drifting query; its fused token
+                       append gives the same cache and selection as the
+                       separate call
+"""
+import numpy as np
+import pytest
+
+from test_gpu_parity import Problem, np_pool, no_device_errors
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def env(orc):
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from query_aware_sparse_kvs_amd import kvs, synth
+    torch.cuda.set_device(0)
+    kvs.kvs_device_errors(clear=True)
+
+    class Env:
+        pass
+    e = Env()
+    e.torch, e.kvs, e.synth, e.orc, e.dev = torch, kvs, synth, orc, torch.device("cuda:0")
+    return e
+
+
+class Cache:
+    """A paged cache on the GPU and its oracle twin (numpy), with a pinned
+    host tier on each side, that decode tokens are appended to."""
+
+    def __init__(self, env, w, lens0, seed, host_tier=True, max_blocks=None):
+        torch, kvs = env.torch, env.kvs
+        self.env, self.w = env, w
+        self.p = Problem(env, w, seq_lens=lens0, max_blocks=max_blocks or w.nb + 1, extra_pages=2)
+        p, L = self.p, self.p.L
+        self.rng = np.random.default_rng(seed)
+        self.fp8 = w.kv_dtype == "e4m3"
+        # the state before the first append: summaries of lens0 tokens
+        self.summ = p.gpu_summaries()
+        self.o_summ = p.or_summaries()
+        self.o = {n: (None if p.h[n] is None else p.h[n].copy()) for n in ("k_pool", "v_pool", "k_scales", "v_scales")}
+        self.host = {}
+        self.o_host = {}
+        if host_tier:
+            units = L.num_seqs * L.num_kv_heads
+            tile = L.block_size * L.head_dim
+            shape = (units * L.max_blocks * tile,)
+            dt = kvs._TORCH_OF[L.kv_dtype]
+            fill = {torch.float32: 3.5, torch.bfloat16: -2.25, torch.uint8: 0x55}[dt]
+            for n in ("host_k", "host_v"):
+                self.host[n] = torch.full(shape, fill, dtype=dt).pin_memory()
+                self.o_host[n] = np_pool(self.host[n]).copy()
+            if self.fp8:
+                for n in ("host_k_scales", "host_v_scales"):
+                    self.host[n] = torch.full((shape[0] // L.quant_group,), -1.0).pin_memory()
+                    self.o_host[n] = self.host[n].numpy().copy()
+        self.lens = np.asarray(lens0, np.int64)
+
+    def new_token(self):
+        """k_new, v_new (+ scales) as stored elements: device tensors and numpy."""
+        torch, L = self.env.torch, self.p.L
+        out = {}
+        for n in ("k", "v"):
+            x = torch.from_numpy(self.rng.standard_normal((L.num_seqs, L.num_kv_heads, L.head_dim)).astype(np.float32))
+            if self.fp8:
+                codes, scales = self.env.synth.quantize_e4m3(x, L.quant_group)
+                out[n] = codes
+                out[n + "_s"] = scales
+            else:
+                out[n] = x.to(self.env.kvs._TORCH_OF[L.kv_dtype])
+                out[n + "_s"] = None
+        return out
+
+    def args(self, tok):
+        kvs, dev, inp = self.env.kvs, self.env.dev, self.p.inp
+        return kvs.AppendArgs(
+            k_new=tok["k"].to(dev), v_new=tok["v"].to(dev),
+            k_new_scales=None if tok["k_s"] is None else tok["k_s"].to(dev),
+            v_new_scales=None if tok["v_s"] is None else tok["v_s"].to(dev),
+            block_table=inp["block_table"], k_pool=inp["k_pool"], v_pool=inp["v_pool"],
+            k_scales=inp["k_scales"], v_scales=inp["v_scales"],
+            host_k=self.host.get("host_k"), host_v=self.host.get("host_v"),
+            host_k_scales=self.host.get("host_k_scales"), host_v_scales=self.host.get("host_v_scales"))
+
+    def oracle_append(self, tok, lens):
+        o, h = self.o, self.o_host
+        self.env.orc.append_token(
+            self.p.OL, np_pool(tok["k"]), np_pool(tok["v"]),
+            None if tok["k_s"] is None else tok["k_s"].numpy(),
+            None if tok["v_s"] is None else tok["v_s"].numpy(),
+            self.p.h["table"], lens, o["k_pool"], o["v_pool"], o["k_scales"], o["v_scales"],
+            self.o_summ, h.get("host_k"), h.get("host_v"), h.get("host_k_scales"), h.get("host_v_scales"))
+
+    def set_lens(self, lens):
+        self.lens = np.asarray(lens, np.int64)
+        self.p.inp["seq_lens"].copy_(self.env.torch.as_tensor(self.lens, dtype=self.env.torch.int32))
+        self.p.h["lens"] = self.lens.astype(np.int32)
+        self.p.nbs = [(int(n) + self.w.S - 1) // self.w.S for n in self.lens]
+
+    def check(self, what):
+        p = self.p
+        for n in ("k_pool", "v_pool", "k_scales", "v_scales"):
+            if self.o[n] is None:
+                continue
+            g = np_pool(p.inp[n]) if n.endswith("pool") else p.inp[n].cpu().numpy()
+            assert np.array_equal(g.view(np.uint8), self.o[n].view(np.uint8)), f"{what}: {n} differs"
+        g = self.summ.double().cpu().numpy()
+        for b, n in enumerate(self.lens):
+            nb = (int(n) + self.w.S - 1) // self.w.S
+            assert np.array_equal(g[b, :, :nb], self.o_summ[b, :, :nb]), f"{what}: summaries of sequence {b} differ"
+        for n, t in self.host.items():
+            gh = np_pool(t) if n in ("host_k", "host_v") else t.numpy()
+            assert np.array_equal(gh.view(np.uint8), self.o_host[n].view(np.uint8)), f"{what}: {n} differs"
+
+
+APPEND_CASES = [
+    # (name, workload, overrides, first lengths, steps)
+    ("bf16-s64-d128", "llama8b", {"B": 4, "L": 64 * 6, "layers": 1, "heavy": "none"}, [64 * 3 - 5, 64, 1, 0], 70),
+    ("bf16-s16-d64", "llama8b", {"B": 3, "L": 16 * 12, "S": 16, "D": 64, "Hq": 8, "Hkv": 2, "layers": 1,
+                                 "heavy": "none"}, [30, 16, 3], 40),
+    ("f32-s16", "tiny", {"B": 3, "L": 16 * 10}, [50, 15, 1], 36),
+    ("fp8-s64-qg32", "longfp8", {"B": 2, "L": 64 * 5}, [64 * 2 - 3, 64], 67),
+    ("fp8-s32-d64-qg16", "longfp8", {"B": 2, "L": 32 * 6, "S": 32, "D": 64, "quant_group": 16}, [40, 32], 35),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_append_token_steps_match_oracle(env, case):
+    name, base, over, lens0, steps = case
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=4)
+    print(f"[append {name}] B={w.B} Hkv={w.Hkv} D={w.D} S={w.S} lens0={lens0} steps={steps} {w.kv_dtype}",
+          flush=True)
+    c = Cache(env, w, lens0, seed=7)
+    kvs = env.kvs
+    lens = np.asarray(lens0, np.int64)
+    for step in range(steps):
+        # a sequence that started empty stays empty (nothing is appended to it)
+        lens = np.where(np.asarray(lens0) > 0, lens + 1, 0)
+        c.set_lens(lens)
+        tok = c.new_token()
+        kvs.kvs_append_token(c.p.L, c.args(tok), c.p.inp["seq_lens"], c.summ)
+        c.oracle_append(tok, lens.astype(np.int32))
+        if step % 17 == 16 or step == steps - 1:
+            no_device_errors(env)
+            c.check(f"step {step}")
+    sealed = sum(int(n) // w.S - int(m) // w.S for n, m in zip(lens, lens0))
+    print(f"[append {name}] {steps} steps, {sealed} blocks sealed into the host tier")
+    assert sealed > 0
+
+
+def _drift_q(env, q, rng):
+    """Next step's query: a bf16 random walk that keeps most of the last one."""
+    torch = env.torch
+    x = q.float().cpu().numpy()
+    x = 0.8 * x + 0.6 * rng.standard_normal(x.shape)
+    return torch.from_numpy(x.astype(np.float32)).to(q.dtype).to(q.device)
+
+
+SELECT_CASES = [
+    # (name, workload, overrides, lens, max_blocks (None: fitted), k, recent, ema, bounds)
+    ("window8", "llama8b", {"B": 3, "L": 64 * 90, "layers": 1}, [64 * 90, 64 * 70 + 9, 64 * 10], None, 24, 8,
+     False, True),
+    ("window8-no-bounds", "llama8b", {"B": 3, "L": 64 * 90, "layers": 1}, [64 * 90, 64 * 70 + 9, 64 * 10], None,
+     24, 8, False, False),
+    ("ema", "llama8b", {"B": 3, "L": 64 * 90, "layers": 1}, [64 * 90, 64 * 70 + 9, 64 * 10], None, 24, 1, True,
+     True),
+    ("ema-window16-no-bounds", "llama8b", {"B": 3, "L": 64 * 90, "layers": 1}, [64 * 90, 64 * 33, 64 * 20 + 1],
+     None, 20, 16, True, False),
+    ("ema-fp8", "longfp8", {"B": 2, "L": 64 * 60}, [64 * 60, 64 * 41 + 3], None, 12, 4, True, True),
+    ("ema-f32-s16", "tiny", {"B": 2, "L": 1000}, [1000, 517], None, 10, 3, True, False),
+    ("window-matrix-core", "llama8b", {"B": 8, "L": 64 * 300, "layers": 1},
+     [64 * 300, 64 * 300 - 7, 64 * 120, 64 * 41 + 5, 64 * 300, 64 * 2, 64 * 40, 64 * 299 + 1], 2048, 40, 8,
+     False, False),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=[c[0] for c in SELECT_CASES])
+def test_select_ex_window_and_smoothing_over_steps(env, case):
+    name, base, over, lens, mb, k, recent, ema, with_bounds = case
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    p = Problem(env, w, seq_lens=lens, max_blocks=mb if mb else w.nb + 2, extra_pages=3)
+    L = p.L
+    print(f"[select-ex {name}] units {L.num_seqs * L.num_kv_heads} max_blocks {L.max_blocks} k={k} "
+          f"recent={recent} ema={ema} bounds={with_bounds}", flush=True)
+    summ = p.gpu_summaries()
+    o_summ = p.or_summaries()
+    state = torch.full((L.num_seqs, L.num_kv_heads, L.max_blocks), float("nan"), dtype=torch.float64,
+                       device=env.dev)
+    o_state = np.full(tuple(state.shape), np.nan)
+    opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    rng = np.random.default_rng(99)
+    changed = 0
+    prev = None
+    for step in range(6):
+        sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+        W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64,
+                        device=env.dev) if with_bounds else None
+        kvs.kvs_select_topk_ex(L, p.inp["q"], summ, p.inp["seq_lens"], k, opts, None, sel, W, ws)
+        no_device_errors(env)
+        p.h["q"] = p.inp["q"].double().cpu().numpy()
+        o_W = orc.bounds(p.OL, p.h["q"], o_summ, p.h["lens"])
+        rank = orc.ema_scores(p.OL, o_W, p.h["lens"], 0.7, o_state) if ema else o_W
+        o_sel = orc.select_window(p.OL, rank, p.h["lens"], k, recent)
+        if with_bounds:
+            gW = W.cpu().numpy()
+            for b, nb in enumerate(p.nbs):
+                assert np.array_equal(gW[b, :, :nb], o_W[b, :, :nb]), f"step {step}: bounds differ"
+        assert np.array_equal(sel.cpu().numpy(), o_sel), f"step {step}: selection differs"
+        if ema:
+            gs = state.cpu().numpy()
+            assert np.array_equal(np.isnan(gs), np.isnan(o_state)), f"step {step}: state NaN pattern differs"
+            assert np.array_equal(np.nan_to_num(gs), np.nan_to_num(o_state)), f"step {step}: state differs"
+        if prev is not None:
+            changed += int((o_sel != prev).any(axis=-1).sum())
+        prev = o_sel
+        p.inp["q"] = _drift_q(env, p.inp["q"], rng)
+    print(f"[select-ex {name}] 6 steps; units whose selection changed between steps: {changed}")
+
+
+FUSED_CASES = [
+    # (name, workload, overrides, lens0, max_blocks, k, recent, ema, bounds)
+    ("bf16-fused", "llama8b", {"B": 3, "L": 64 * 40, "layers": 1, "heavy": "none"}, [64 * 30 - 1, 64 * 7, 5],
+     None, 12, 2, False, False),
+    ("bf16-matrix-core-fused", "llama8b", {"B": 8, "L": 64 * 300, "layers": 1, "heavy": "none"},
+     [64 * 290 - 1, 64 * 200, 64 * 100 + 3, 64 * 41 + 5, 64 * 280, 64 * 2, 64 * 40, 64 * 250 + 1], 2048, 40, 4,
+     False, False),
+    ("bf16-bounds", "llama8b", {"B": 3, "L": 64 * 40, "layers": 1, "heavy": "none"}, [64 * 30 - 1, 64 * 7, 5],
+     None, 12, 1, False, True),
+    ("bf16-ema", "llama8b", {"B": 3, "L": 64 * 40, "layers": 1, "heavy": "none"}, [64 * 30 - 1, 64 * 7, 5],
+     None, 12, 3, True, False),
+    ("fp8-fused", "longfp8", {"B": 2, "L": 64 * 40}, [64 * 30 - 1, 64 * 7], None, 10, 2, False, False),
+    ("f32-fused", "tiny", {"B": 2, "L": 16 * 40}, [16 * 30 - 1, 16 * 7], None, 10, 2, False, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_select_ex_with_token_append(env, case):
+    """kvs_select_topk_ex with the append: the cache, summaries and host tier
+    come out as the oracle's append leaves them, and the selection is the
+    oracle's on the updated summaries -- whether the append runs inside the
+    scoring launch or before it."""
+    name, base, over, lens0, mb, k, recent, ema, with_bounds = case
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    c = Cache(env, w, lens0, seed=3, max_blocks=mb)
+    p, L = c.p, c.p.L
+    print(f"[select-ex+append {name}] units {L.num_seqs * L.num_kv_heads} k={k} recent={recent} ema={ema} "
+          f"bounds={with_bounds}", flush=True)
+    state = torch.full((L.num_seqs, L.num_kv_heads, L.max_blocks), float("nan"), dtype=torch.float64,
+                       device=env.dev)
+    o_state = np.full(tuple(state.shape), np.nan)
+    opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    lens = np.asarray(lens0, np.int64)
+    for step in range(3):
+        lens = lens + 1
+        c.set_lens(lens)
+        tok = c.new_token()
+        sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+        W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64,
+                        device=env.dev) if with_bounds else None
+        kvs.kvs_select_topk_ex(L, p.inp["q"], c.summ, p.inp["seq_lens"], k, opts, c.args(tok), sel, W, ws)
+        no_device_errors(env)
+        c.oracle_append(tok, lens.astype(np.int32))
+        c.check(f"step {step}")
+        o_W = orc.bounds(p.OL, p.h["q"], c.o_summ, p.h["lens"])
+        rank = orc.ema_scores(p.OL, o_W, p.h["lens"], 0.7, o_state) if ema else o_W
+        o_sel = orc.select_window(p.OL, rank, p.h["lens"], k, recent)
+        assert np.array_equal(sel.cpu().numpy(), o_sel), f"step {step}: selection differs"
+        if with_bounds:
+            gW = W.cpu().numpy()
+            for b, nb in enumerate(p.nbs):
+                assert np.array_equal(gW[b, :, :nb], o_W[b, :, :nb]), f"step {step}: bounds differ"
+        if ema:
+            assert np.array_equal(np.nan_to_num(state.cpu().numpy()), np.nan_to_num(o_state))
