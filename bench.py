@@ -1,9 +1,11 @@
 """Decode-step benchmark of query-aware block-sparse attention on one MI355X.
 
-A step is one decode layer-step of the whole path over one batch: rebuild
-the newest block's summary of every sequence while scoring every block and
-selecting the top-k (one call), then attend over the selected blocks (split
-partials + merge).  The
+A step is one decode layer-step of the whole path over one batch: append
+every sequence's decode token to the paged cache and fold it into its
+block's summary while scoring every block and selecting the top-k (one
+call), then attend over the selected blocks (split partials + merge).  The
+appended token is the one the cache already holds at that position, so the
+replayed step leaves the cache as it was.  The
 default workload is 8 sequences x 32 query / 4 KV heads, head dim 128, 32768
 tokens of bf16 K/V in 64-token pages, k = 128 of 512 blocks, over 32 layer
 instances with their own buffers (step i uses instance i mod 32, so no step
@@ -42,8 +44,9 @@ PEAK_HBM_GBPS = 8000.0
 
 def algorithmic_bytes(w, summ_elem: int, kv_elem: int, q_elem: int) -> dict:
     """Bytes one layer-step must move: the summaries of every block, the
-    selected K/V tiles (and fp8 scales), q, the fp32 output, and the newest
-    block's K tile read plus its summary written."""
+    selected K/V tiles (and fp8 scales), q, the fp32 output, and the decode
+    token's append (its K and V read and written, with fp8 scales, and its
+    block's summary row read and written)."""
     units = w.B * w.Hkv
     summ = units * w.nb * 2 * w.D * summ_elem
     tile = w.S * w.D * kv_elem
@@ -51,7 +54,8 @@ def algorithmic_bytes(w, summ_elem: int, kv_elem: int, q_elem: int) -> dict:
     scales = units * w.k * 2 * w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0
     q = w.B * w.Hq * w.D * q_elem
     out = w.B * w.Hq * w.D * 4
-    append = units * (tile + (w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0) + 2 * w.D * summ_elem)
+    tok = 2 * w.D * kv_elem + (2 * (w.D // w.quant_group) * 4 if w.quant_group else 0)  # K and V of one token
+    append = units * (2 * tok + 2 * 2 * w.D * summ_elem)
     return {"summaries": summ, "kv": kv, "scales": scales, "q": q, "out": out, "append": append,
             "attention": kv + scales + q + out,
             "step": summ + kv + scales + q + out + append}
@@ -114,7 +118,12 @@ def main(argv=None) -> int:
         summ = st.new_summaries(dev)
         st.prefill_summaries(inp["k_pool"], inp["k_scales"], inp["block_table"], inp["seq_lens"], summ)
         newest = ((inp["seq_lens"] + w.S - 1) // w.S - 1).to(torch.int32)
-        layers.append(dict(inp=inp, summ=summ, newest=newest))
+        nt = synth.newest_tokens(w, inp)
+        tok = kvs.AppendArgs(k_new=nt["k_new"], v_new=nt["v_new"], k_new_scales=nt["k_new_scales"],
+                             v_new_scales=nt["v_new_scales"], block_table=inp["block_table"],
+                             k_pool=inp["k_pool"], v_pool=inp["v_pool"], k_scales=inp["k_scales"],
+                             v_scales=inp["v_scales"])
+        layers.append(dict(inp=inp, summ=summ, newest=newest, tok=tok, nt=nt))
         steps.append(st)
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0
@@ -124,6 +133,12 @@ def main(argv=None) -> int:
         inp = d["inp"]
         kvs.kvs_select_topk_append(L, inp["q"], inp["k_pool"], inp["k_scales"], inp["block_table"],
                                    inp["seq_lens"], d["summ"], w.k, st.sel, None, st.select_ws)
+
+    def run_append_select(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_select_topk_ex(L, inp["q"], d["summ"], inp["seq_lens"], w.k, None, d["tok"], st.sel, None,
+                               st.select_ws)
 
     def run_select(i):
         d, st = layers[i], steps[i]
@@ -140,8 +155,11 @@ def main(argv=None) -> int:
     def run_step(i):
         d, st = layers[i], steps[i]
         inp = d["inp"]
-        st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
-               inp["seq_lens"], d["summ"])
+        if args.parts > 1:  # the summary-rebuild chain, cut into concurrent batch slices
+            st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
+                   inp["seq_lens"], d["summ"])
+        else:
+            st.run_decode(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
 
     def capture(fn):
         """One graph over every layer instance in order (as a decoder runs its
@@ -192,11 +210,12 @@ def main(argv=None) -> int:
     print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
     # per-phase graphs: the dominant kernel (attention) for the roofline entry,
-    # the selection with its newest-summary rebuild as the step runs it, and
-    # the selection alone (the rebuild's cost is the difference)
+    # the token append with the selection as the step runs it, the selection
+    # alone (the append's cost is the difference), and the selection with a
+    # rebuild of the newest block's summary from its K tile instead
     phase = {}
-    for name, fn in (("select_topk_append", run_select_append), ("select_topk_only", run_select),
-                     ("attention", run_attn)):
+    for name, fn in (("append_select", run_append_select), ("select_topk_only", run_select),
+                     ("select_topk_rebuild", run_select_append), ("attention", run_attn)):
         t, _ = timed(capture(fn), args.steps, args.warmup)
         phase[name] = t / args.steps
     t_attn = phase["attention"] * args.steps
@@ -406,8 +425,8 @@ def measured_traffic(workload: str):
 
 def cpu_baseline(w, layers, n_steps):
     """The oracle (single thread, fp64, as written) on `n_steps` whole
-    layer-steps of the same workload: newest-block summaries, bounds,
-    selection, sparse attention."""
+    layer-steps of the same workload: decode-token append (with its block's
+    summary), bounds, selection, sparse attention."""
     import numpy as np
     import torch
 
@@ -428,13 +447,20 @@ def cpu_baseline(w, layers, n_steps):
         h["lens"] = inp["seq_lens"].cpu().numpy()
         h["q"] = inp["q"].double().cpu().numpy()
         h["newest"] = layers[li]["newest"].cpu().numpy()
+        nt = layers[li]["nt"]
+        for n in ("k_new", "v_new"):
+            t = nt[n].cpu()
+            h[n] = t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        for n in ("k_new_scales", "v_new_scales"):
+            h[n] = None if nt[n] is None else nt[n].cpu().numpy()
         # prefill-time summaries of every block, built by the oracle (untimed)
         h["summ"] = oracle.summaries(OL, h["k_pool"], h["k_scales"], h["table"], h["lens"])
         host.append(h)
     print(f"[bench] CPU oracle on {n_steps} layer-step(s)", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for h in host:
-        oracle.summaries(OL, h["k_pool"], h["k_scales"], h["table"], h["lens"], h["newest"], 1, out=h["summ"])
+        oracle.append_token(OL, h["k_new"], h["v_new"], h["k_new_scales"], h["v_new_scales"], h["table"],
+                            h["lens"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["summ"])
         W = oracle.bounds(OL, h["q"], h["summ"], h["lens"])
         sel = oracle.select(OL, W, h["lens"], w.k)
         oracle.sparse_attn(OL, h["q"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["table"],

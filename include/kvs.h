@@ -289,11 +289,10 @@ kvs_status kvs_append_token(const kvs_layout* layout, const kvs_append_args* app
  *  opts = NULL  R = 1, no smoothing.
  *  append       NULL, or the token append of kvs_append_token (same
  *               arguments), done before the blocks are scored.  Without
- *               bounds_out and smoothing it runs as one more workgroup per
- *               (sequence, KV head) of the scoring launch, beside the
- *               workgroups that score (the newest block is always kept, so
- *               its own score is not used); otherwise as a launch of its own
- *               first.
+ *               bounds_out and smoothing it runs inside the scoring launch,
+ *               beside the scoring of the other blocks (the newest block is
+ *               always kept, so its own score is not used); otherwise as a
+ *               launch of its own first.
  *  bounds_out   optional [B][Hkv][MB] fp64: the unsmoothed W.
  *  summaries    in/out when append is given, else only read.
  *  others       as for kvs_select_topk.

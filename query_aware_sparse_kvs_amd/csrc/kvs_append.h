@@ -1,8 +1,9 @@
 // kvs_append.h -- appending one decode token of one (sequence, KV head)
 // unit (page "KV 稀疏化", §7 "HiSparse": the newest KV is written to the
 // device cache, and KV that is no longer being written sinks to the host
-// tier).  Shared by the append kernel and by the scoring kernels, whose extra
-// workgroups do it while the others score.
+// tier).  Shared by the append kernel and by the scoring kernels, which run
+// it beside their scoring work (the exact bounds kernel in each unit's first
+// workgroup, the matrix-core one in one more workgroup per unit).
 //
 // For len = seq_lens[b] > 0 the token t = len-1 lands in block j = t/S, slot
 // s = t%S of page block_table[b][j]: thread c writes channel c of K (row s of
@@ -42,7 +43,15 @@ __device__ __forceinline__ void append_token_unit(const AppendArgs& a, int b, in
   using E = typename ElemT<KVK>::T;
   constexpr int EB = elem_bytes<KVK>();
   const int tid = threadIdx.x;
-  int len = a.seq_lens[b];
+  const long long unit = (long long)b * a.Hkv + g;
+  const int groups = KVK == K_FP8 ? D / a.qg : 0;
+  const int c = tid < D ? tid : D - 1;  // threads past D only help with the seal copy
+  // loads that need no length go out with the length itself
+  const int len = a.seq_lens[b];
+  const E kv = static_cast<const E*>(a.k_new)[unit * D + c];
+  const E vv = static_cast<const E*>(a.v_new)[unit * D + c];
+  float ksc = 1.0f;
+  if constexpr (KVK == K_FP8) ksc = a.k_new_scales[unit * groups + c / a.qg];
   if (len < 0 || len > a.MB * a.S) {
     if (tid == 0 && g == 0) raise_flag(a.err, 0x1u);
     return;
@@ -51,17 +60,26 @@ __device__ __forceinline__ void append_token_unit(const AppendArgs& a, int b, in
   const int S = a.S, T = S < 32 ? S : 32;
   const int t = len - 1, j = t / S, s = t % S;
   const int page = a.block_table[(long long)b * a.MB + j];
+  // the block's stored summary (its tokens before t) is read beside the page
+  const long long row = (unit * a.MB + j) * 2 * D;  // min at [0, D), max at [D, 2D)
+  float old_mn = 0.0f, old_mx = 0.0f;
+  if (s > 0) {
+    if constexpr (KVK == K_BF16) {
+      const uint16_t* ps = static_cast<const uint16_t*>(a.summ) + row;
+      old_mn = bf16_lo(ps[c]);
+      old_mx = bf16_lo(ps[D + c]);
+    } else {
+      const float* ps = static_cast<const float*>(a.summ) + row;
+      old_mn = ps[c];
+      old_mx = ps[D + c];
+    }
+  }
   if (page < 0 || page >= a.P) {
     if (tid == 0) raise_flag(a.err, 0x2u);
     return;
   }
   const long long tile = (long long)page * a.Hkv + g;  // (page, head) tile
-  const long long unit = (long long)b * a.Hkv + g;
-  const int groups = KVK == K_FP8 ? D / a.qg : 0;
   if (tid < D) {
-    const int c = tid;
-    const E kv = static_cast<const E*>(a.k_new)[unit * D + c];
-    const E vv = static_cast<const E*>(a.v_new)[unit * D + c];
     static_cast<E*>(a.k_pool)[(tile * S + s) * D + c] = kv;
     static_cast<E*>(a.v_pool)[((tile * (S / T) + s / T) * D + c) * T + s % T] = vv;
     float x;  // the K element's value, as the summaries and attention read it
@@ -72,25 +90,16 @@ __device__ __forceinline__ void append_token_unit(const AppendArgs& a, int b, in
     } else {
       float f[4];
       fp8x4_to_f32((uint32_t)kv, f);
-      x = f[0] * a.k_new_scales[unit * groups + c / a.qg];
+      x = f[0] * ksc;
     }
-    const long long row = (unit * a.MB + j) * 2 * D;  // min at [0, D), max at [D, 2D)
+    const float mn = s > 0 ? fminf(old_mn, x) : x;
+    const float mx = s > 0 ? fmaxf(old_mx, x) : x;
     if constexpr (KVK == K_BF16) {
       uint16_t* ps = static_cast<uint16_t*>(a.summ) + row;
-      float mn = x, mx = x;
-      if (s > 0) {
-        mn = fminf(bf16_lo(ps[c]), x);
-        mx = fmaxf(bf16_lo(ps[D + c]), x);
-      }
       ps[c] = (uint16_t)bf16_bits_exact(mn);
       ps[D + c] = (uint16_t)bf16_bits_exact(mx);
     } else {
       float* ps = static_cast<float*>(a.summ) + row;
-      float mn = x, mx = x;
-      if (s > 0) {
-        mn = fminf(ps[c], x);
-        mx = fmaxf(ps[D + c], x);
-      }
       ps[c] = mn;
       ps[D + c] = mx;
     }

@@ -156,8 +156,9 @@ struct BoundArgs {
   double* bounds_out;  // optional copy
   unsigned int* err;
   int32_t B, Hq, Hkv, D, S, MB;
-  int32_t append;      // one more workgroup per (b, g): 1 rebuilds the newest block's
-                       // summary (app), 2 appends the decode token (tok)
+  int32_t append;      // 1: one more workgroup per (b, g) rebuilds the newest block's
+                       // summary (app); 2: the first workgroup of each (b, g) also
+                       // appends the decode token (tok)
   int32_t app_kv;      // K storage kind of that work (Kind; bf16 with bf16 summaries)
   SummArgs app;
   AppendArgs tok;
@@ -185,7 +186,7 @@ struct SelMfmaArgs {
   unsigned int* err;
   int32_t B, Hq, Hkv, G, D, S, MB, k;
   int32_t recent;  // as in TopkArgs
-  int32_t append;  // as in BoundArgs
+  int32_t append;  // 1 / 2 as in BoundArgs, both done by one more workgroup per (b, g)
   SummArgs app;
   AppendArgs tok;
 };

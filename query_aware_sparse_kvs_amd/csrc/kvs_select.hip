@@ -82,18 +82,9 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   __shared__ __attribute__((aligned(16))) double qd[G][D];
   __shared__ __attribute__((aligned(16))) uint32_t qm[G][WPR];
   const int b = blockIdx.z, g = blockIdx.y;
-  if (a.append && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup refreshes a summary
+  if (a.append == 1 && blockIdx.x == gridDim.x - 1) {  // uniform: this workgroup rebuilds a summary
     static_assert(sizeof(sm) >= kSummRed<D, NT> * sizeof(float), "summary reduction fits the chunk buffer");
     float* red = reinterpret_cast<float*>(sm);
-    if (a.append == 2) {  // the decode token: written, folded into its block's summary
-      if constexpr (SK == K_BF16)
-        append_token_unit<K_BF16, D, NT>(a.tok, b, g);
-      else if (a.app_kv == K_FP8)
-        append_token_unit<K_FP8, D, NT>(a.tok, b, g);
-      else
-        append_token_unit<K_F32, D, NT>(a.tok, b, g);
-      return;
-    }
     if constexpr (SK == K_BF16) {
       rebuild_newest_summary<K_BF16, D, NT>(a.app, b, g, red);
     } else if (a.app_kv == K_FP8) {
@@ -128,6 +119,17 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     else
       v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
     qd[h][c] = (double)v;
+  }
+  // the decode token is appended by the unit's first workgroup while its
+  // chunk loads are in flight (a workgroup of its own would leave some
+  // compute units with two scoring workgroups)
+  if (a.append == 2 && blockIdx.x == 0) {
+    if constexpr (SK == K_BF16)
+      append_token_unit<K_BF16, D, NT>(a.tok, b, g);
+    else if (a.app_kv == K_FP8)
+      append_token_unit<K_FP8, D, NT>(a.tok, b, g);
+    else
+      append_token_unit<K_F32, D, NT>(a.tok, b, g);
   }
   int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
@@ -430,7 +432,7 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
 
 template <int QK, int SK, int D, int G>
 void launch_bounds_one(const BoundArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks + (a.append ? 1 : 0)), (unsigned)a.Hkv,
+  const dim3 grid((unsigned)((a.MB + kBoundBlocks - 1) / kBoundBlocks + (a.append == 1 ? 1 : 0)), (unsigned)a.Hkv,
                   (unsigned)a.B);
   hipLaunchKernelGGL((bounds_kernel<QK, SK, D, G>), grid, dim3(64 * bound_waves<G, SK>()), 0, s, a);
 }

@@ -68,6 +68,21 @@ class SparseDecodeStep:
                                    block_table[sl], seq_lens[sl], self.sel[sl], k, self.sm_scale,
                                    self.out[sl], aws, stream)
 
+    def run_decode(self, q, tok: kvs.AppendArgs, seq_lens, summaries, opts: kvs.SelectOpts | None = None,
+                   bounds_out=None, stream=None) -> torch.Tensor:
+        """A whole decode layer-step on one chain: the decode token appended
+        to the cache (its block's summary updated incrementally; a block that
+        fills is sealed into tok's host tier, if any), the blocks scored and
+        selected with `opts` (recent window, score smoothing), attention over
+        the selection."""
+        L, k = self.layout, self.k
+        kvs.kvs_select_topk_ex(L, q, summaries, seq_lens, k, opts, tok, self.sel, bounds_out, self.select_ws,
+                               stream)
+        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, tok.k_pool, tok.v_pool, tok.k_scales, tok.v_scales,
+                                   tok.block_table, seq_lens, self.sel, k, self.sm_scale, self.out,
+                                   self.attn_ws, stream)
+        return self.out
+
     def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,
             bounds_out=None, stream=None) -> torch.Tensor:
         """summaries: in/out, every block but the newest already summarised.

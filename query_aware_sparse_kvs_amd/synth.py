@@ -236,6 +236,24 @@ def make_inputs(w: Workload, device="cpu", layer: int = 0, seq_lens=None,
     return out
 
 
+def newest_tokens(w: Workload, inp: dict) -> dict:
+    """The K/V elements (and fp8 scales) each sequence holds at its last
+    position seq_lens[b]-1, gathered from the pools as [B][Hkv][D] (scales
+    [B][Hkv][D/group]): a decode token that, appended again, leaves the cache
+    as it is."""
+    lens = inp["seq_lens"].long()
+    t = (lens - 1).clamp(min=0)
+    pages = inp["block_table"].long().gather(1, (t // w.S)[:, None])[:, 0]
+    s = t % w.S
+    T = min(w.S, 32)
+    out = {"k_new": inp["k_pool"][pages, :, s, :].contiguous(),
+           "v_new": inp["v_pool"][pages, :, s // T, :, s % T].contiguous()}
+    for n in ("k", "v"):
+        sc = inp[n + "_scales"]
+        out[n + "_new_scales"] = None if sc is None else sc[pages, :, s, :].contiguous()
+    return out
+
+
 def random_selection(w: Workload, seq_lens, k: int, seed: int, max_fill: bool = True) -> np.ndarray:
     """A valid selection [B][Hkv][k] (ascending ids then -1), drawn at random
     for attention-only tests: sink and newest block included, the rest a
