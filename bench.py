@@ -75,6 +75,9 @@ def main(argv=None) -> int:
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--fused-topk", action="store_true",
+                    help="time the step with the top-k inside the attention launch (kvs_score_blocks + "
+                         "kvs_select_attn) instead of as a launch of its own")
     ap.add_argument("--cpu-steps", type=int, default=6, help="layer-steps in the CPU oracle sample (about 2 s each)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -158,8 +161,22 @@ def main(argv=None) -> int:
         if args.parts > 1:  # the summary-rebuild chain, cut into concurrent batch slices
             st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
                    inp["seq_lens"], d["summ"])
+        elif args.fused_topk:
+            st.run_decode_fused(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
         else:
             st.run_decode(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
+
+    def run_score(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_score_blocks(L, inp["q"], d["summ"], inp["seq_lens"], None, d["tok"], st.scores, None)
+
+    def run_select_attn(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_select_attn(L, inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"],
+                            inp["block_table"], inp["seq_lens"], st.scores, w.k, 1, st.sel, st.sm_scale, st.out,
+                            st.attn_ws)
 
     def capture(fn):
         """One graph over every layer instance in order (as a decoder runs its
@@ -214,7 +231,8 @@ def main(argv=None) -> int:
     # alone (the append's cost is the difference), and the selection with a
     # rebuild of the newest block's summary from its K tile instead
     phase = {}
-    for name, fn in (("append_select", run_append_select), ("select_topk_only", run_select),
+    for name, fn in (("score_blocks", run_score), ("select_attn", run_select_attn),
+                     ("append_select", run_append_select), ("select_topk_only", run_select),
                      ("select_topk_rebuild", run_select_append), ("attention", run_attn)):
         t, _ = timed(capture(fn), args.steps, args.warmup)
         phase[name] = t / args.steps

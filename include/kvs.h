@@ -344,6 +344,49 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* layout, int32_t table_kind,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_score_blocks + kvs_select_attn -- the layer-step of kvs_select_topk_ex
+ * followed by kvs_sparse_decode_attn, with the top-k done inside the
+ * attention launch
+ *
+ * kvs_score_blocks does everything kvs_select_topk_ex does before the top-k
+ * (the optional token append, the block scores of kvs_select_topk, the
+ * optional smoothing of opts; opts->recent_blocks is not used here) and
+ * writes each block's score -- the smoothed score with smoothing on, else W
+ * -- to scores [B][Hkv][MB] fp64 (-inf for j >= nb(b)).  Scores are always
+ * the exact fp64 ones.  With an append and neither bounds_out nor smoothing,
+ * the append runs inside the scoring launch and the score of each sequence's
+ * newest block nb(b)-1 is taken from a summary being updated at the same
+ * time: that one entry is unspecified (the block is always kept, so no
+ * selection reads it).
+ *
+ * kvs_select_attn selects, per (b, g), the blocks kvs_select_topk_ex would
+ * select from those scores (sink, the recent_blocks newest blocks, the best
+ * of the rest), writes that selection to sel [B][Hkv][k], and returns the
+ * attention of kvs_sparse_decode_attn (paged table) over it.  With bf16 q,
+ * bf16 or fp8 K/V, S >= 32 and MB, k <= 2048 every attention workgroup
+ * selects its own blocks from the scores, so no separate selection launch or
+ * round trip through memory is needed; other shapes run the selection
+ * launch first.  Same results either way.
+ *
+ *  scores       [B][Hkv][MB] fp64, as kvs_score_blocks writes them
+ *  k            2 <= k <= MB;  recent_blocks >= 1, k >= recent_blocks + 1
+ *  sel          [B][Hkv][k] int32 output
+ *  others       as for kvs_sparse_decode_attn (workspace: its size query)
+ * Errors: as kvs_select_topk_ex and kvs_sparse_decode_attn.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_score_blocks(const kvs_layout* layout, const void* q, void* summaries,
+                            const int32_t* seq_lens, const kvs_select_opts* opts,
+                            const kvs_append_args* append, double* scores, double* bounds_out,
+                            void* stream);
+
+kvs_status kvs_select_attn(const kvs_layout* layout, const void* q, const void* k_pool,
+                           const void* v_pool, const float* k_scales, const float* v_scales,
+                           const int32_t* block_table, const int32_t* seq_lens,
+                           const double* scores, int32_t k, int32_t recent_blocks, int32_t* sel,
+                           float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_hot_lookup_swapin -- hot-buffer page-table step and swap-in copy
  *
  * Page "KV 稀疏化", §7 "HiSparse" table: the hot device buffer keeps the KV

@@ -291,19 +291,25 @@ struct SelectOpts {
 // own before scoring.
 kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries, const int32_t* seq_lens, int32_t k,
                        int32_t* sel, double* bounds_out, void* workspace, size_t workspace_bytes, void* stream,
-                       const kvs::SummArgs* app, const SelectOpts& opt, const kvs_append_args* tok_in) {
+                       const kvs::SummArgs* app, const SelectOpts& opt, const kvs_append_args* tok_in,
+                       double* scores_out = nullptr) {
+  // scores_out: stop after the (exact) scores, written there; no selection
   kvs_status st = check_layout(L, true);
   if (st != KVS_OK) return st;
-  if (!q || !summaries || !seq_lens || !sel)
+  if (!q || !summaries || !seq_lens || (!sel && !scores_out))
     return fail(KVS_ERR_INVALID_ARG, "q, summaries, seq_lens and sel must be non-NULL");
-  if (k < 2 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [2, max_blocks]");
-  if (opt.recent < 1 || k < opt.recent + 1)
-    return fail(KVS_ERR_INVALID_ARG, "recent_blocks must be >= 1 and k >= recent_blocks + 1");
+  if (!scores_out) {
+    if (k < 2 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [2, max_blocks]");
+    if (opt.recent < 1 || k < opt.recent + 1)
+      return fail(KVS_ERR_INVALID_ARG, "recent_blocks must be >= 1 and k >= recent_blocks + 1");
+    if (!workspace || workspace_bytes < select_ws(L))
+      return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_select_workspace_size()");
+  } else if (!aligned(scores_out, 8)) {
+    return fail(KVS_ERR_INVALID_ARG, "scores must be 8-byte aligned");
+  }
   if (opt.ema && (!opt.state || !aligned(opt.state, 8) || !(opt.alpha >= 0.0 && opt.alpha <= 1.0)))
     return fail(KVS_ERR_INVALID_ARG, "smoothing needs an 8-byte aligned ema_state and 0 <= ema_alpha <= 1");
-  if (!workspace || workspace_bytes < select_ws(L))
-    return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_select_workspace_size()");
-  if (!aligned(summaries, 16) || !aligned(workspace, 16) || (bounds_out && !aligned(bounds_out, 8)))
+  if (!aligned(summaries, 16) || (workspace && !aligned(workspace, 16)) || (bounds_out && !aligned(bounds_out, 8)))
     return fail(KVS_ERR_INVALID_ARG, "summaries/workspace must be 16-byte aligned, bounds_out 8-byte");
   kvs::AppendArgs tok{};
   if (tok_in && (st = make_append(L, tok_in, seq_lens, const_cast<void*>(summaries), &tok)) != KVS_OK) return st;
@@ -339,7 +345,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   // of thousands of blocks (8 x 4 x 512: 15.0 vs 16.5 us; 256 x 4 x 512:
   // 108 vs 75 us).
   const long long blocks = (long long)L->num_seqs * L->num_kv_heads * L->max_blocks;
-  if (!bounds_out && !opt.ema && blocks >= kSelectMfmaMinBlocks &&
+  if (!scores_out && !bounds_out && !opt.ema && blocks >= kSelectMfmaMinBlocks &&
       kvs::select_mfma_supported(kind_of(L->q_dtype), summ_kind, L->head_dim, L->max_blocks, G)) {
     kvs::SelMfmaArgs ma{};
     ma.q = q;
@@ -367,7 +373,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   ba.q = q;
   ba.summ = summaries;
   ba.seq_lens = seq_lens;
-  ba.W = static_cast<double*>(workspace);
+  ba.W = scores_out ? scores_out : static_cast<double*>(workspace);
   ba.bounds_out = bounds_out;
   ba.err = err;
   ba.B = L->num_seqs;
@@ -385,7 +391,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   ba.ema_beta = 1.0 - opt.alpha;
   ba.ema_state = opt.state;
   hipError_t e = kvs::launch_bounds(ba, kind_of(L->q_dtype), summ_kind, s);
-  if (e != hipSuccess) return hip_status(e, "bounds launch");
+  if (e != hipSuccess || scores_out) return hip_status(e, "bounds launch");
   kvs::TopkArgs ta{};
   ta.W = ba.W;
   ta.seq_lens = seq_lens;
@@ -465,11 +471,61 @@ kvs_status kvs_select_topk_append(const kvs_layout* L, const void* q, const void
                      SelectOpts{}, nullptr);
 }
 
+}  // extern "C"
+
+namespace {
+kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, const void* k_pool, const void* v_pool,
+                     const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
+                     const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent);
+}  // namespace
+
+extern "C" {
+
 kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const void* q,
                                   const void* k_pool, const void* v_pool, const float* k_scales,
                                   const float* v_scales, const int32_t* table, const int32_t* seq_lens,
                                   const int32_t* sel, int32_t k, float sm_scale, float* out,
                                   void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_impl(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out,
+                   workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kvs_status kvs_score_blocks(const kvs_layout* L, const void* q, void* summaries, const int32_t* seq_lens,
+                            const kvs_select_opts* opts, const kvs_append_args* append, double* scores,
+                            double* bounds_out, void* stream) {
+  if (!scores) return fail(KVS_ERR_INVALID_ARG, "scores must be non-NULL");
+  SelectOpts o;
+  if (opts) {
+    o.ema = opts->use_ema != 0;
+    o.alpha = opts->ema_alpha;
+    o.state = opts->ema_state;
+  }
+  return select_impl(L, q, summaries, seq_lens, 0, nullptr, bounds_out, nullptr, 0, stream, nullptr, o, append,
+                     scores);
+}
+
+kvs_status kvs_select_attn(const kvs_layout* L, const void* q, const void* k_pool, const void* v_pool,
+                           const float* k_scales, const float* v_scales, const int32_t* block_table,
+                           const int32_t* seq_lens, const double* scores, int32_t k, int32_t recent_blocks,
+                           int32_t* sel, float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!scores || !aligned(scores, 8)) return fail(KVS_ERR_INVALID_ARG, "scores must be non-NULL and 8-byte aligned");
+  if (k < 2 || (L && k > L->max_blocks)) return fail(KVS_ERR_INVALID_ARG, "k must be in [2, max_blocks]");
+  if (recent_blocks < 1 || k < recent_blocks + 1)
+    return fail(KVS_ERR_INVALID_ARG, "recent_blocks must be >= 1 and k >= recent_blocks + 1");
+  return attn_impl(L, KVS_TABLE_PAGED, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, sel, k,
+                   sm_scale, out, workspace, workspace_bytes, stream, scores, recent_blocks);
+}
+
+}  // extern "C"
+
+namespace {
+
+kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, const void* k_pool, const void* v_pool,
+                     const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
+                     const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
+                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent) {
   kvs_status st = check_layout(L, true);
   if (st != KVS_OK) return st;
   if (table_kind != KVS_TABLE_PAGED && table_kind != KVS_TABLE_HOT)
@@ -520,9 +576,33 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const
   a.nsplit = nsplit;
   a.bps = (k + nsplit - 1) / nsplit;
   a.hot = table_kind == KVS_TABLE_HOT ? 1 : 0;
-  return hip_status(kvs::launch_attn(a, kind_of(L->q_dtype), kind_of(L->kv_dtype), static_cast<hipStream_t>(stream)),
-                    "attention launch");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scores) {
+    if (kvs::attn_self_select_supported(kind_of(L->q_dtype), kind_of(L->kv_dtype), L->block_size, L->max_blocks, k)) {
+      a.W = scores;  // each workgroup selects its own blocks
+      a.sel_out = const_cast<int32_t*>(sel);
+      a.recent = recent;
+    } else {  // the attention kernel for this shape reads a selection: select first
+      kvs::TopkArgs ta{};
+      ta.W = scores;
+      ta.seq_lens = seq_lens;
+      ta.sel = const_cast<int32_t*>(sel);
+      ta.B = L->num_seqs;
+      ta.Hkv = L->num_kv_heads;
+      ta.S = L->block_size;
+      ta.MB = L->max_blocks;
+      ta.k = k;
+      ta.recent = recent;
+      hipError_t e = kvs::launch_topk(ta, s);
+      if (e != hipSuccess) return hip_status(e, "top-k launch");
+    }
+  }
+  return hip_status(kvs::launch_attn(a, kind_of(L->q_dtype), kind_of(L->kv_dtype), s), "attention launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots,
                                  int64_t step, int32_t* page_table, int32_t* slot_owner,

@@ -41,6 +41,7 @@
 // Roofline: HBM-bound gather of 2*S*D*elem bytes (+ fp8 scales) per
 // selected block.
 #include "kvs_internal.h"
+#include "kvs_topk.h"
 
 namespace kvs {
 namespace {
@@ -303,6 +304,30 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Self-selecting mode: the workgroup picks its unit's blocks itself, from
+// the scores, with the selection of kvs_topk.h (the same one topk_kernel
+// runs), instead of reading a selection another launch wrote; the table
+// row's loads go out beside the scores'.  Returns the selection row (in
+// LDS) after a workgroup barrier; the first split's workgroup also writes
+// it to sel_out.
+constexpr int kSelfSelMax = 2048;               // largest MB and k of the mode
+constexpr int kSelfSelPT = kSelfSelMax / 256;   // score ids per thread
+
+template <int NW>
+__device__ __forceinline__ const int32_t* self_select(const AttnArgs& a, int b, int g, int split, int nb,
+                                                      bool staged, int* trow, int32_t* lsel, TopkLds& tk) {
+  static_assert(NW * 64 == 256, "the selection runs on 256 threads");
+  const long long unit = (long long)b * a.Hkv + g;
+  double wv[kSelfSelPT];
+  load_unit_scores<kSelfSelPT>(a.W + unit * a.MB, a.MB, wv);
+  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+  select_unit<kSelfSelPT>(wv, a.MB, nb, a.k, a.recent, lsel, tk);
+  __syncthreads();
+  if (split == 0)
+    for (int i = threadIdx.x; i < a.k; i += 64 * NW) a.sel_out[unit * a.k + i] = lsel[i];
+  return lsel;
+}
+
 // The end of an MFMA-kernel workgroup: merges the NW wavefronts' running
 // (max, sum, acc) in LDS; lane (r, j4) holds channels ct*16 + 4*j4 + e of
 // head r.  One split: the normalised output row is written; otherwise the
@@ -362,7 +387,7 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
   }
 }
 
-template <int D, int S, int NW>
+template <int D, int S, int NW, bool SELF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CS = D / 32;  // k-steps of the score product
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
@@ -372,6 +397,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   __shared__ long long wl_tile[NW][64];
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
+  __shared__ int32_t lsel[SELF ? kSelfSelMax : 1];
+  __shared__ TopkLds tk;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -398,7 +425,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
+  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;  // self-selecting: replaced below
   const int i0 = split * a.bps + wave;           // this wavefront's pages: i0, i0+NW, ...
   const int i1 = min(split * a.bps + a.bps, a.k);
   const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
@@ -414,10 +441,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // the first chunk's slots and the table row are fetched together, so the
   // table lookups need no further round trip
   int j0, jp0;
-  fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
   const bool staged = a.MB <= kTabMax;
-  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
-  __syncthreads();
+  if constexpr (SELF) {
+    srow = self_select<NW>(a, b, g, split, nb, staged, trow, lsel, tk);
+    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+  } else {
+    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+    __syncthreads();
+  }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
     int j = j0, jp = jp0;
     if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
@@ -621,7 +653,7 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
   }
 }
 
-template <int D, int S, int NW>
+template <int D, int S, int NW, bool SELF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a) {
   constexpr int CS = D / 32;
   constexpr int CT = D / 16;
@@ -632,6 +664,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
   __shared__ __attribute__((aligned(16))) float vsl[NW][S * 8];  // per wavefront: [group][S]
+  __shared__ int32_t lsel[SELF ? kSelfSelMax : 1];
+  __shared__ TopkLds tk;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -674,10 +708,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
 
   // the same two-stage page pipeline as the bf16 kernel
   int j0, jp0;
-  fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
   const bool staged = a.MB <= kTabMax;
-  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
-  __syncthreads();
+  if constexpr (SELF) {
+    srow = self_select<NW>(a, b, g, split, nb, staged, trow, lsel, tk);
+    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+  } else {
+    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+    __syncthreads();
+  }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {
     int j = j0, jp = jp0;
     if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
@@ -1118,23 +1157,39 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, bool SELF>
+void launch_mfma8_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
+  if (a.S == 32)
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+}
+
 template <int D>
 hipError_t launch_mfma8(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  if (a.W)
+    launch_mfma8_s<D, true>(a, grid, st);
   else
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    launch_mfma8_s<D, false>(a, grid, st);
   return hipGetLastError();
+}
+
+template <int D, bool SELF>
+void launch_mfma_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
+  if (a.S == 32)
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma_kernel<D, 64, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
 }
 
 template <int D>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 32, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  if (a.W)
+    launch_mfma_s<D, true>(a, grid, st);
   else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 64, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    launch_mfma_s<D, false>(a, grid, st);
   return hipGetLastError();
 }
 
@@ -1154,9 +1209,17 @@ int attn_num_splits(int units, int k) {
   return n < 1 ? 1 : n;
 }
 
+bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k) {
+  // the matrix-core kernels (bf16 q; bf16 or fp8 K/V; S >= 32) carry the
+  // selection prologue
+  return q_kind == K_BF16 && (kv_kind == K_BF16 || kv_kind == K_FP8) && S >= 32 && MB <= kSelfSelMax &&
+         k <= kSelfSelMax;
+}
+
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   if (a.nsplit < 1 || a.nsplit > kMaxSplits) return hipErrorInvalidValue;  // merge_kernel's bound
+  if (a.W && !attn_self_select_supported(q_kind, kv_kind, a.S, a.MB, a.k)) return hipErrorInvalidValue;
   hipError_t e;
   if (q_kind == K_BF16 && kv_kind == K_BF16 && a.S >= 32)
     e = a.D == 64 ? launch_mfma<64>(a, st) : launch_mfma<128>(a, st);

@@ -207,6 +207,12 @@ struct AttnArgs {
   unsigned int* err;
   float q_scale;    // sm_scale * log2(e): scores are kept in base 2
   int32_t B, Hq, Hkv, G, D, S, MB, P, qg, k, nsplit, bps, hot;
+  // self-selecting mode (W non-null): every workgroup selects its unit's
+  // blocks from the scores W [B][Hkv][MB] (recent = newest blocks always
+  // kept), and the first split's workgroup writes the selection to sel_out
+  const double* W;
+  int32_t* sel_out;
+  int32_t recent;
 };
 
 struct HotArgs {
@@ -238,6 +244,8 @@ hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G);
 hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s);
+// whether launch_attn can run this shape in self-selecting mode
+bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k);
 hipError_t launch_hot(const HotArgs& a, hipStream_t s);
 
 // attention split heuristic shared by the launcher and the workspace query

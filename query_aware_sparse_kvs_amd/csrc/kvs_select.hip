@@ -18,22 +18,14 @@
 // of the summaries (2*D*elem bytes per block and KV head); the fp64 chain
 // costs about four vector instructions per (block, head, channel).
 //
-// topk_kernel: one 256-thread workgroup per (sequence, KV head).  Scores are
-// mapped to order-preserving 64-bit keys.  A most-significant-digit radix
-// select (8-bit digits, LDS histogram) over the high 32 bits, starting at
-// the first bit where the candidates' keys differ, finds the bucket of the
-// (k-1-R)-th largest key among blocks 1..nb-R-1 (R = the recent window, the
-// newest blocks that are always kept; "SparDA…" §4.2 keeps the last 512 or
-// 1024 tokens); only when that bucket holds
-// more keys than are needed does a second select run on the low 32 bits of
-// the tied keys.  Ties on the full key go to the lowest block ids, the
-// (W desc, id asc) order.  A block-wide prefix sum writes the chosen ids in
-// ascending order.  Latency-bound.
+// topk_kernel: one 256-thread workgroup per (sequence, KV head) runs the
+// selection of kvs_topk.h.  Latency-bound.
 //
 // With score smoothing on, the bounds kernel ranks blocks by the smoothed
 // score alpha*W + (1-alpha)*history ("SparDA…" §6.1) instead of W itself.
 #include "kvs_append.h"
 #include "kvs_summarize.h"
+#include "kvs_topk.h"
 
 namespace kvs {
 namespace {
@@ -217,217 +209,18 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   }
 }
 
-// order-preserving map of a double (no NaN) to uint64; -0 and +0 coincide
-__device__ __forceinline__ unsigned long long order_key(double w) {
-  const double z = w + 0.0;  // -0 -> +0
-  const unsigned long long u = (unsigned long long)__double_as_longlong(z);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-// Radix select over the active 32-bit keys of a 256-thread workgroup: finds
-// the value T of the rem-th largest active key (rem is 1-based) and how many
-// keys equal to T are needed (*rem_eq).  Keys share the bits above byte
-// `start_byte` (given in `prefix`), so only bytes start_byte..0 are scanned.
-template <int PT>
-__device__ __forceinline__ void radix_select_u32(const unsigned (&key)[PT], const bool (&act)[PT], int rem,
-                                                 int start_byte, unsigned prefix, unsigned* hist,
-                                                 unsigned* sh_T, int* sh_rem, unsigned* T, int* rem_eq) {
-  const int tid = threadIdx.x;
-  unsigned mask = start_byte >= 3 ? 0u : (0xFFFFFFFFu << (8 * (start_byte + 1)));
-  prefix &= mask;
-  for (int pass = start_byte; pass >= 0; --pass) {
-    const int shift = pass * 8;
-    hist[tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PT; ++i)
-      if (act[i] && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 255-4l .. 252-4l (highest digits first)
-      unsigned c4[4], s = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = hist[255 - 4 * tid - e];
-        s += c4[e];
-      }
-      unsigned incl = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned o = __shfl_up(incl, off);
-        if (tid >= off) incl += o;
-      }
-      unsigned above = incl - s;  // keys in higher digits
-      if ((int)above < rem && rem <= (int)incl) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((int)(above + c4[e]) >= rem) {
-            *sh_T = prefix | ((unsigned)(255 - 4 * tid - e) << shift);
-            *sh_rem = rem - (int)above;
-            break;
-          }
-          above += c4[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix = *sh_T;
-    rem = *sh_rem;
-    mask |= 0xFFu << shift;
-  }
-  *T = prefix;
-  *rem_eq = rem;
-}
-
-// block-wide min and max of v over 256 threads (tmp: 8 words of LDS)
-__device__ __forceinline__ void block_min_max_256(unsigned v_min, unsigned v_max, unsigned* tmp, unsigned* mn,
-                                                  unsigned* mx) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    v_min = min(v_min, (unsigned)__shfl_xor((int)v_min, off));
-    v_max = max(v_max, (unsigned)__shfl_xor((int)v_max, off));
-  }
-  if (lane == 0) {
-    tmp[wave] = v_min;
-    tmp[4 + wave] = v_max;
-  }
-  __syncthreads();
-  *mn = min(min(tmp[0], tmp[1]), min(tmp[2], tmp[3]));
-  *mx = max(max(tmp[4], tmp[5]), max(tmp[6], tmp[7]));
-}
-
 template <int PT>  // candidates per thread (contiguous block ids)
 __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
-  __shared__ unsigned hist[256];
-  __shared__ unsigned mm_tmp[8];
-  __shared__ int scan_tmp[4];
-  __shared__ unsigned sh_T;
-  __shared__ int sh_rem;
-  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int k = a.k;
+  __shared__ TopkLds sh;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const long long unit = (long long)b * a.Hkv + g;
+  double wv[PT];
+  load_unit_scores<PT>(a.W + unit * a.MB, a.MB, wv);
   int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int nb = (len + a.S - 1) / a.S;
-  int32_t* out = a.sel + ((long long)b * a.Hkv + g) * k;
-
-  // scores of every id below MB are loaded before nb is known (ids past nb
-  // are never candidates); ids are spread as contiguous runs of `per`
-  const double* W = a.W + ((long long)b * a.Hkv + g) * a.MB;
-  const int per = (a.MB + 255) / 256;  // ids per thread, <= PT
-  const int j0 = tid * per;
-  double wv[PT];
-#pragma unroll
-  for (int i = 0; i < PT; ++i) wv[i] = (i < per && j0 + i < a.MB) ? W[j0 + i] : 0.0;
-  if (nb <= k) {  // every block, then padding
-    for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
-    return;
-  }
-  const int R = a.recent;  // newest blocks always kept
-  const int M = k - 1 - R;  // free picks among blocks 1..nb-R-1
-
-  bool cand[PT];
-  unsigned hi[PT], lo[PT];
-  unsigned hmin = 0xFFFFFFFFu, hmax = 0u;
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int j = j0 + i;
-    cand[i] = i < per && j >= 1 && j < nb - R;
-    const unsigned long long key = cand[i] ? order_key(wv[i]) : 0ull;
-    hi[i] = (unsigned)(key >> 32);
-    lo[i] = (unsigned)key;
-    if (cand[i]) {
-      hmin = min(hmin, hi[i]);
-      hmax = max(hmax, hi[i]);
-    }
-  }
-  // phase 1: threshold on the high 32 bits of the key
-  unsigned T_hi = 0u, T_lo = 0u;
-  int rem_hi = 0, rem_lo = 0, n_eq = 0;
-  bool need_lo = false;
-  bool eqh[PT];
-  if (M > 0) {
-    unsigned mn, mx;
-    block_min_max_256(hmin, hmax, mm_tmp, &mn, &mx);
-    if (mn == mx) {
-      T_hi = mn;
-      rem_hi = M;
-    } else {
-      const int top_bit = 31 - __clz(mn ^ mx);
-      radix_select_u32<PT>(hi, cand, M, top_bit / 8, mn, hist, &sh_T, &sh_rem, &T_hi, &rem_hi);
-    }
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      eqh[i] = cand[i] && hi[i] == T_hi;
-      cnt += eqh[i] ? 1 : 0;
-    }
-    int tot;
-    (void)block_exclusive_scan_256(cnt, scan_tmp, &tot);
-    n_eq = tot;
-    // phase 2 (only when the threshold bucket holds more keys than needed):
-    // threshold on the low 32 bits among the keys tied on the high bits
-    need_lo = rem_hi < n_eq;
-    if (need_lo) {
-      unsigned lmin = 0xFFFFFFFFu, lmax = 0u;
-#pragma unroll
-      for (int i = 0; i < PT; ++i)
-        if (eqh[i]) {
-          lmin = min(lmin, lo[i]);
-          lmax = max(lmax, lo[i]);
-        }
-      unsigned mn2, mx2;
-      block_min_max_256(lmin, lmax, mm_tmp, &mn2, &mx2);
-      if (mn2 == mx2) {
-        T_lo = mn2;
-        rem_lo = rem_hi;
-      } else {
-        const int top_bit = 31 - __clz(mn2 ^ mx2);
-        radix_select_u32<PT>(lo, eqh, rem_hi, top_bit / 8, mn2, hist, &sh_T, &sh_rem, &T_lo, &rem_lo);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < PT; ++i) eqh[i] = false;
-  }
-  // ties on the full key go to the lowest block ids
-  int n_tie = 0;
-#pragma unroll
-  for (int i = 0; i < PT; ++i) n_tie += (need_lo && eqh[i] && lo[i] == T_lo) ? 1 : 0;
-  int tot;
-  int tie_before = block_exclusive_scan_256(n_tie, scan_tmp, &tot);
-  int n_sel = 0;
-  unsigned chosen = 0u;  // bit i: id j0+i selected
-#pragma unroll
-  for (int i = 0; i < PT; ++i) {
-    const int j = j0 + i;
-    if (i >= per || j >= nb) continue;
-    bool take;
-    if (j == 0 || j >= nb - R) {
-      take = true;
-    } else if (!cand[i] || M == 0) {
-      take = false;
-    } else if (hi[i] != T_hi) {
-      take = hi[i] > T_hi;
-    } else if (!need_lo) {
-      take = true;  // the whole bucket is needed
-    } else if (lo[i] != T_lo) {
-      take = lo[i] > T_lo;
-    } else {
-      take = tie_before < rem_lo;
-      ++tie_before;
-    }
-    if (take) {
-      chosen |= 1u << i;
-      ++n_sel;
-    }
-  }
-  int pos = block_exclusive_scan_256(n_sel, scan_tmp, &tot);
-#pragma unroll
-  for (int i = 0; i < PT; ++i)
-    if ((chosen & (1u << i)) && pos < k) out[pos++] = j0 + i;
-  for (int i = tot + tid; i < k; i += 256) out[i] = -1;
+  select_unit<PT>(wv, a.MB, nb, a.k, a.recent, a.sel + unit * a.k, sh);
 }
 
 template <int QK, int SK, int D, int G>

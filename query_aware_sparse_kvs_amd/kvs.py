@@ -117,6 +117,9 @@ def _load():
         "kvs_select_topk_append": (i32, [LP, P, P, P, P, P, P, i32, P, P, P, sz, P]),
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
         "kvs_append_token": (i32, [LP, ctypes.POINTER(_CAppendArgs), P, P, P]),
+        "kvs_score_blocks": (i32, [LP, P, P, P, ctypes.POINTER(_CSelectOpts), ctypes.POINTER(_CAppendArgs),
+                                   P, P, P]),
+        "kvs_select_attn": (i32, [LP, P, P, P, P, P, P, P, P, i32, i32, P, ctypes.c_float, P, P, sz, P]),
         "kvs_select_topk_ex": (i32, [LP, P, P, P, i32, ctypes.POINTER(_CSelectOpts),
                                      ctypes.POINTER(_CAppendArgs), P, P, P, sz, P]),
         "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
@@ -136,7 +139,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
-            "kvs_append_token", "kvs_select_topk_ex",
+            "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
 
@@ -295,6 +298,56 @@ def kvs_select_topk_ex(layout: Layout, q, summaries, seq_lens, k: int, opts: Sel
         _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
         ws, workspace.numel() if workspace is not None else 0,
         _stream(stream)), "kvs_select_topk_ex")
+
+
+def _opts_struct(L: Layout, opts: SelectOpts | None):
+    if opts is None:
+        return None
+    return _CSelectOpts(int(opts.recent_blocks), 1 if opts.use_ema else 0, float(opts.ema_alpha),
+                        _ptr(opts.ema_state, "ema_state", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks))
+
+
+def kvs_score_blocks(layout: Layout, q, summaries, seq_lens, opts: SelectOpts | None, append: AppendArgs | None,
+                     scores, bounds_out, stream=None) -> None:
+    L = layout
+    co = _opts_struct(L, opts)
+    ca = _append_struct(L, append) if append is not None else None
+    n = L.num_seqs * L.num_kv_heads * L.max_blocks
+    _check(_lib.kvs_score_blocks(
+        ctypes.byref(L.c()),
+        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(summaries, "summaries", L.summary_dtype, n * 2 * L.head_dim),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        ctypes.byref(co) if co is not None else None,
+        ctypes.byref(ca) if ca is not None else None,
+        _ptr(scores, "scores", torch.float64, n),
+        _ptr(bounds_out, "bounds_out", torch.float64, n),
+        _stream(stream)), "kvs_score_blocks")
+
+
+def kvs_select_attn(layout: Layout, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, scores,
+                    k: int, recent_blocks: int, sel, sm_scale: float, out, workspace, stream=None) -> None:
+    L = layout
+    tile = L.num_kv_heads * L.block_size * L.head_dim
+    qg = L.quant_group
+    sc_n = L.num_pages * tile // qg if qg else None
+    _check(_lib.kvs_select_attn(
+        ctypes.byref(L.c()),
+        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(k_pool, "k_pool", _pool_dtype(L), L.num_pages * tile),
+        _ptr(v_pool, "v_pool", _pool_dtype(L), L.num_pages * tile),
+        _ptr(k_scales, "k_scales", torch.float32, sc_n),
+        _ptr(v_scales, "v_scales", torch.float32, sc_n),
+        _ptr(block_table, "block_table", torch.int32, L.num_seqs * L.max_blocks),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        _ptr(scores, "scores", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
+        int(k), int(recent_blocks),
+        _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
+        float(sm_scale),
+        _ptr(out, "out", torch.float32, L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(workspace, "workspace", torch.uint8),
+        workspace.numel() if workspace is not None else 0,
+        _stream(stream)), "kvs_select_attn")
 
 
 def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,

@@ -48,6 +48,7 @@ class SparseDecodeStep:
         self.streams = [torch.cuda.Stream(device=dev) for _ in self.slices[1:]]
         # whole-batch workspaces for the single-chain path
         self.select_ws = torch.empty(max(kvs.kvs_select_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
+        self.scores = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=dev)
         self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
 
     def new_summaries(self, device="cuda") -> torch.Tensor:
@@ -81,6 +82,17 @@ class SparseDecodeStep:
         kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, tok.k_pool, tok.v_pool, tok.k_scales, tok.v_scales,
                                    tok.block_table, seq_lens, self.sel, k, self.sm_scale, self.out,
                                    self.attn_ws, stream)
+        return self.out
+
+    def run_decode_fused(self, q, tok: kvs.AppendArgs, seq_lens, summaries,
+                         opts: kvs.SelectOpts | None = None, bounds_out=None, stream=None) -> torch.Tensor:
+        """run_decode's layer-step with the top-k done inside the attention
+        launch: kvs_score_blocks (append, scores), then kvs_select_attn."""
+        L, k = self.layout, self.k
+        kvs.kvs_score_blocks(L, q, summaries, seq_lens, opts, tok, self.scores, bounds_out, stream)
+        recent = opts.recent_blocks if opts is not None else 1
+        kvs.kvs_select_attn(L, q, tok.k_pool, tok.v_pool, tok.k_scales, tok.v_scales, tok.block_table, seq_lens,
+                            self.scores, k, recent, self.sel, self.sm_scale, self.out, self.attn_ws, stream)
         return self.out
 
     def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,

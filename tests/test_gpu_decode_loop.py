@@ -285,3 +285,81 @@ def test_select_ex_with_token_append(env, case):
                 assert np.array_equal(gW[b, :, :nb], o_W[b, :, :nb]), f"step {step}: bounds differ"
         if ema:
             assert np.array_equal(np.nan_to_num(state.cpu().numpy()), np.nan_to_num(o_state))
+
+
+SPLIT_CASES = [
+    # (name, workload, overrides, lens0, max_blocks, k, recent, ema)
+    ("bf16-self", "llama8b", {"B": 3, "L": 64 * 60, "layers": 1}, [64 * 50 - 1, 64 * 20 + 7, 5], None, 24, 1, False),
+    ("bf16-self-window8", "llama8b", {"B": 3, "L": 64 * 60, "layers": 1}, [64 * 50 - 1, 64 * 20 + 7, 64 * 9],
+     None, 24, 8, False),
+    ("bf16-self-ema", "llama8b", {"B": 2, "L": 64 * 60, "layers": 1}, [64 * 50 - 1, 64 * 33], None, 16, 2, True),
+    ("bf16-s32-d64-self", "llama8b", {"B": 2, "L": 32 * 70, "S": 32, "D": 64, "Hq": 16, "layers": 1},
+     [32 * 60 + 3, 32 * 11], None, 20, 1, False),
+    ("bf16-self-one-split", "llama8b", {"B": 2, "L": 64 * 40, "layers": 1}, [64 * 30, 64 * 4], None, 4, 1, False),
+    ("fp8-self", "longfp8", {"B": 2, "L": 64 * 80}, [64 * 70 + 1, 64 * 12], None, 16, 3, False),
+    ("bf16-s16-fallback", "llama8b", {"B": 2, "L": 16 * 90, "S": 16, "Hq": 32, "Hkv": 2, "layers": 1},
+     [16 * 80 + 5, 16 * 7], None, 20, 2, False),
+    ("f32-fallback", "tiny", {"B": 2, "L": 16 * 60}, [16 * 50, 16 * 9 + 2], None, 10, 1, True),
+    ("bf16-mb-over-2048-fallback", "llama8b", {"B": 1, "L": 64 * 100, "layers": 1}, [64 * 90 + 3], 2100, 12, 2,
+     False),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_score_blocks_then_select_attn(env, case):
+    """kvs_score_blocks (with the token append) then kvs_select_attn: the
+    scores, the smoothing state and the selection equal the oracle's bit for
+    bit (the same selection kvs_select_topk_ex makes), and the attention is
+    within the bars, over three decode steps."""
+    from test_gpu_parity import check_attn
+    name, base, over, lens0, mb, k, recent, ema = case
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    c = Cache(env, w, lens0, seed=11, max_blocks=mb)
+    p, L = c.p, c.p.L
+    print(f"[score+select-attn {name}] units {L.num_seqs * L.num_kv_heads} max_blocks {L.max_blocks} k={k} "
+          f"recent={recent} ema={ema} splits={kvs.kvs_attn_num_splits(L, k)}", flush=True)
+    state = torch.full((L.num_seqs, L.num_kv_heads, L.max_blocks), float("nan"), dtype=torch.float64,
+                       device=env.dev)
+    o_state = np.full(tuple(state.shape), np.nan)
+    opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None)
+    scores = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=env.dev)
+    aws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    sws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    lens = np.asarray(lens0, np.int64)
+    rng = np.random.default_rng(5)
+    for step in range(3):
+        lens = lens + 1
+        c.set_lens(lens)
+        tok = c.new_token()
+        sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+        out = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=env.dev)
+        kvs.kvs_score_blocks(L, p.inp["q"], c.summ, p.inp["seq_lens"], opts, c.args(tok), scores, None)
+        kvs.kvs_select_attn(L, p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
+                            p.inp["block_table"], p.inp["seq_lens"], scores, k, recent, sel, p.sm_scale, out, aws)
+        no_device_errors(env)
+        c.oracle_append(tok, lens.astype(np.int32))
+        c.check(f"step {step}")
+        p.h["q"] = p.inp["q"].double().cpu().numpy()
+        o_W = orc.bounds(p.OL, p.h["q"], c.o_summ, p.h["lens"])
+        rank = orc.ema_scores(p.OL, o_W, p.h["lens"], 0.7, o_state) if ema else o_W
+        gs = scores.cpu().numpy()
+        for b, nb in enumerate(p.nbs):
+            # fused append (no smoothing): the newest block's score is unspecified
+            upto = nb if ema else nb - 1
+            assert np.array_equal(gs[b, :, :upto], rank[b, :, :upto]), f"step {step}: scores differ"
+            assert np.isneginf(gs[b, :, nb:]).all()
+        o_sel = orc.select_window(p.OL, rank, p.h["lens"], k, recent)
+        assert np.array_equal(sel.cpu().numpy(), o_sel), f"step {step}: selection differs"
+        # the separate selection launch picks the same blocks from the same scores
+        if not ema:
+            sel2 = torch.full_like(sel, -7)
+            kvs.kvs_select_topk_ex(L, p.inp["q"], c.summ, p.inp["seq_lens"], k,
+                                   kvs.SelectOpts(recent_blocks=recent), None, sel2, None, sws)
+            no_device_errors(env)
+            assert torch.equal(sel, sel2), f"step {step}: kvs_select_topk_ex picks other blocks"
+        o_out = orc.sparse_attn(p.OL, p.h["q"], c.o["k_pool"], c.o["v_pool"], c.o["k_scales"], c.o["v_scales"],
+                                p.h["table"], p.h["lens"], o_sel, p.sm_scale)
+        err, rel = check_attn(out, o_out)
+        p.inp["q"] = _drift_q(env, p.inp["q"], rng)
+    print(f"[score+select-attn {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
