@@ -2,8 +2,9 @@
 
 A step is one decode layer-step of the whole path over one batch: append
 every sequence's decode token to the paged cache and fold it into its
-block's summary while scoring every block and selecting the top-k (one
-call), then attend over the selected blocks (split partials + merge).  The
+block's summary while scoring every block (kvs_score_blocks), then attend
+over the top-k blocks, each attention workgroup selecting its unit's blocks
+from the scores itself (kvs_select_attn: split partials + merge).  The
 appended token is the one the cache already holds at that position, so the
 replayed step leaves the cache as it was.  The
 default workload is 8 sequences x 32 query / 4 KV heads, head dim 128, 32768
@@ -58,6 +59,7 @@ def algorithmic_bytes(w, summ_elem: int, kv_elem: int, q_elem: int) -> dict:
     append = units * (2 * tok + 2 * 2 * w.D * summ_elem)
     return {"summaries": summ, "kv": kv, "scales": scales, "q": q, "out": out, "append": append,
             "attention": kv + scales + q + out,
+            "scores": units * w.nb * 8,
             "step": summ + kv + scales + q + out + append}
 
 
@@ -75,9 +77,9 @@ def main(argv=None) -> int:
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--fused-topk", action="store_true",
-                    help="time the step with the top-k inside the attention launch (kvs_score_blocks + "
-                         "kvs_select_attn) instead of as a launch of its own")
+    ap.add_argument("--separate-topk", action="store_true",
+                    help="time the step with the top-k as a launch of its own (kvs_select_topk_ex + "
+                         "kvs_sparse_decode_attn) instead of inside the attention launch")
     ap.add_argument("--cpu-steps", type=int, default=6, help="layer-steps in the CPU oracle sample (about 2 s each)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
@@ -161,10 +163,10 @@ def main(argv=None) -> int:
         if args.parts > 1:  # the summary-rebuild chain, cut into concurrent batch slices
             st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
                    inp["seq_lens"], d["summ"])
-        elif args.fused_topk:
-            st.run_decode_fused(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
-        else:
+        elif args.separate_topk:
             st.run_decode(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
+        else:
+            st.run_decode_fused(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
 
     def run_score(i):
         d, st = layers[i], steps[i]
@@ -236,7 +238,10 @@ def main(argv=None) -> int:
                      ("select_topk_rebuild", run_select_append), ("attention", run_attn)):
         t, _ = timed(capture(fn), args.steps, args.warmup)
         phase[name] = t / args.steps
-    t_attn = phase["attention"] * args.steps
+    # the roofline entry is for the step's dominant call: the attention with
+    # its own selection (or, with --separate-topk, the attention alone)
+    fused = not args.separate_topk and args.parts == 1
+    t_attn = phase["select_attn" if fused else "attention"] * args.steps
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
 
@@ -248,7 +253,8 @@ def main(argv=None) -> int:
     attn_sec = t_attn / args.steps
     value = w.B / sec_per_step
     step_gbps = by["step"] / sec_per_step / 1e9
-    attn_gbps = by["attention"] / attn_sec / 1e9
+    attn_bytes = by["attention"] + (by["scores"] if fused else 0)
+    attn_gbps = attn_bytes / attn_sec / 1e9
 
     cpu = None
     if not args.no_cpu:
@@ -275,10 +281,13 @@ def main(argv=None) -> int:
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
-        "roofline": {"bound": "hbm", "kernel": "kvs_sparse_decode_attn (attn_mfma_kernel + merge_kernel)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("kvs_select_attn (self-selecting attn_mfma_kernel + merge_kernel)" if fused else
+                                "kvs_sparse_decode_attn (attn_mfma_kernel + merge_kernel)"),
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "bytes_per_launch": by["attention"], "us_per_launch": round(attn_sec * 1e6, 3)},
+                     "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": measured_traffic(w.name, "select_attn" if fused else "attention"),
+                     "bytes_per_launch": attn_bytes, "us_per_launch": round(attn_sec * 1e6, 3)},
         "cpu_baseline": cpu,
         "wall_s_timed_region": round(wall_step, 4),
     }
@@ -407,7 +416,8 @@ def bench_hot(args, w, dev) -> int:
     return 0
 
 
-ATTN_SOURCES = ("query_aware_sparse_kvs_amd/csrc/kvs_attn.hip", "query_aware_sparse_kvs_amd/csrc/kvs_internal.h")
+ATTN_SOURCES = ("query_aware_sparse_kvs_amd/csrc/kvs_attn.hip", "query_aware_sparse_kvs_amd/csrc/kvs_internal.h",
+                "query_aware_sparse_kvs_amd/csrc/kvs_topk.h")
 
 
 def attn_source_digest() -> str:
@@ -419,12 +429,13 @@ def attn_source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention call (both kernels) from the counter summary in
-    profiles/, scaled by the copy-kernel calibration recorded there; None when
-    there is none for this workload or the attention sources have changed
-    since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"attention_{workload}_hbm_traffic.txt")
+def measured_traffic(workload: str, call: str):
+    """HBM bytes per call of `call` (attention: kvs_sparse_decode_attn;
+    select_attn: kvs_select_attn; both kernels of the call) from the counter
+    summary in profiles/, scaled by the copy-kernel calibration recorded
+    there; None when there is none for this workload or the attention sources
+    have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{call}_{workload}_hbm_traffic.txt")
     if not os.path.exists(path):
         return None
     rec = {}

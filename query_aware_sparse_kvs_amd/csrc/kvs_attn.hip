@@ -310,18 +310,19 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow
 // row's loads go out beside the scores'.  Returns the selection row (in
 // LDS) after a workgroup barrier; the first split's workgroup also writes
 // it to sel_out.
-constexpr int kSelfSelMax = 2048;               // largest MB and k of the mode
-constexpr int kSelfSelPT = kSelfSelMax / 256;   // score ids per thread
+constexpr int kSelfSelMax = 2048;  // largest MB and k of the mode
 
-template <int NW>
+// SELF: score ids per thread (0 = reads a selection): 2 up to 512 blocks,
+// 8 up to kSelfSelMax
+template <int NW, int SELF>
 __device__ __forceinline__ const int32_t* self_select(const AttnArgs& a, int b, int g, int split, int nb,
                                                       bool staged, int* trow, int32_t* lsel, TopkLds& tk) {
   static_assert(NW * 64 == 256, "the selection runs on 256 threads");
   const long long unit = (long long)b * a.Hkv + g;
-  double wv[kSelfSelPT];
-  load_unit_scores<kSelfSelPT>(a.W + unit * a.MB, a.MB, wv);
+  double wv[SELF];
+  load_unit_scores<SELF>(a.W + unit * a.MB, a.MB, wv);
   if (staged) stage_table_row<64 * NW>(a, b, g, trow);
-  select_unit<kSelfSelPT>(wv, a.MB, nb, a.k, a.recent, lsel, tk);
+  select_unit<SELF>(wv, a.MB, nb, a.k, a.recent, lsel, tk);
   __syncthreads();
   if (split == 0)
     for (int i = threadIdx.x; i < a.k; i += 64 * NW) a.sel_out[unit * a.k + i] = lsel[i];
@@ -387,7 +388,7 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
   }
 }
 
-template <int D, int S, int NW, bool SELF>
+template <int D, int S, int NW, int SELF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CS = D / 32;  // k-steps of the score product
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
@@ -397,7 +398,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   __shared__ long long wl_tile[NW][64];
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
-  __shared__ int32_t lsel[SELF ? kSelfSelMax : 1];
+  __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -442,8 +443,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // table lookups need no further round trip
   int j0, jp0;
   const bool staged = a.MB <= kTabMax;
-  if constexpr (SELF) {
-    srow = self_select<NW>(a, b, g, split, nb, staged, trow, lsel, tk);
+  if constexpr (SELF > 0) {
+    srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
     fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
   } else {
     fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
@@ -653,7 +654,7 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
   }
 }
 
-template <int D, int S, int NW, bool SELF>
+template <int D, int S, int NW, int SELF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a) {
   constexpr int CS = D / 32;
   constexpr int CT = D / 16;
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
   __shared__ __attribute__((aligned(16))) float vsl[NW][S * 8];  // per wavefront: [group][S]
-  __shared__ int32_t lsel[SELF ? kSelfSelMax : 1];
+  __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -709,8 +710,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   // the same two-stage page pipeline as the bf16 kernel
   int j0, jp0;
   const bool staged = a.MB <= kTabMax;
-  if constexpr (SELF) {
-    srow = self_select<NW>(a, b, g, split, nb, staged, trow, lsel, tk);
+  if constexpr (SELF > 0) {
+    srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
     fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
   } else {
     fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
@@ -1157,7 +1158,7 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int D, bool SELF>
+template <int D, int SELF>
 void launch_mfma8_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
   if (a.S == 32)
     hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
@@ -1168,14 +1169,16 @@ void launch_mfma8_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
 template <int D>
 hipError_t launch_mfma8(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.W)
-    launch_mfma8_s<D, true>(a, grid, st);
+  if (!a.W)
+    launch_mfma8_s<D, 0>(a, grid, st);
+  else if (a.MB <= 512)
+    launch_mfma8_s<D, 2>(a, grid, st);
   else
-    launch_mfma8_s<D, false>(a, grid, st);
+    launch_mfma8_s<D, kSelfSelMax / 256>(a, grid, st);
   return hipGetLastError();
 }
 
-template <int D, bool SELF>
+template <int D, int SELF>
 void launch_mfma_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
   if (a.S == 32)
     hipLaunchKernelGGL((attn_mfma_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
@@ -1186,10 +1189,12 @@ void launch_mfma_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
 template <int D>
 hipError_t launch_mfma(const AttnArgs& a, hipStream_t st) {
   const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
-  if (a.W)
-    launch_mfma_s<D, true>(a, grid, st);
+  if (!a.W)
+    launch_mfma_s<D, 0>(a, grid, st);
+  else if (a.MB <= 512)
+    launch_mfma_s<D, 2>(a, grid, st);
   else
-    launch_mfma_s<D, false>(a, grid, st);
+    launch_mfma_s<D, kSelfSelMax / 256>(a, grid, st);
   return hipGetLastError();
 }
 

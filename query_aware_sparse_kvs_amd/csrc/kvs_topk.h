@@ -4,108 +4,66 @@
 // page §2 and "SparDA：把KV選擇提前一層…" §4.2).  Used by topk_kernel and
 // by the attention kernels that select their own blocks.
 //
-// Scores are mapped to order-preserving 64-bit keys.  A most-significant-digit
-// radix select (8-bit digits, LDS histogram) over the high 32 bits, starting
-// at the first bit where the candidates' keys differ, finds the bucket of the
-// (k-1-R)-th largest key among blocks 1..nb-R-1; only when that bucket holds
-// more keys than are needed does a second select run on the low 32 bits of
-// the tied keys.  Ties on the full key go to the lowest block ids, the
-// (W desc, id asc) order.  A block-wide prefix sum writes the chosen ids in
-// ascending order, then -1 padding.
+// The M = k-1-R best candidates (blocks 1..nb-R-1) under (W descending, id
+// ascending) are found by bucket refinement.  Each round takes the still
+// undecided candidates, spreads them over 2048 LDS buckets by the monotone
+// map (w - lo) * 2047 / (hi - lo) (lo, hi: their smallest and largest
+// score), and scans the bucket counts from the top: candidates above the
+// bucket where the count reaches the places left are taken, those below are
+// dropped, and only that bucket's candidates stay undecided.  The rounds end
+// when the undecided candidates exactly fill the places left, or when they
+// all hold one score (then the lowest ids win).  lo and hi always fall into
+// different buckets, so every round decides at least one candidate; with
+// real scores one or two rounds settle the selection.  A block-wide prefix
+// sum then writes the chosen ids in ascending order, then -1 padding.
 #pragma once
 
 #include "kvs_internal.h"
 
 namespace kvs {
 
-// order-preserving map of a double (no NaN) to uint64; -0 and +0 coincide
-__device__ __forceinline__ unsigned long long order_key(double w) {
-  const double z = w + 0.0;  // -0 -> +0
-  const unsigned long long u = (unsigned long long)__double_as_longlong(z);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-
-// Radix select over the active 32-bit keys of a 256-thread workgroup: finds
-// the value T of the rem-th largest active key (rem is 1-based) and how many
-// keys equal to T are needed (*rem_eq).  Keys share the bits above byte
-// `start_byte` (given in `prefix`), so only bytes start_byte..0 are scanned.
-template <int PT>
-__device__ __forceinline__ void radix_select_u32(const unsigned (&key)[PT], const bool (&act)[PT], int rem,
-                                                 int start_byte, unsigned prefix, unsigned* hist,
-                                                 unsigned* sh_T, int* sh_rem, unsigned* T, int* rem_eq) {
-  const int tid = threadIdx.x;
-  unsigned mask = start_byte >= 3 ? 0u : (0xFFFFFFFFu << (8 * (start_byte + 1)));
-  prefix &= mask;
-  for (int pass = start_byte; pass >= 0; --pass) {
-    const int shift = pass * 8;
-    hist[tid] = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < PT; ++i)
-      if (act[i] && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] >> shift) & 255u], 1u);
-    __syncthreads();
-    if (tid < 64) {
-      // lane l owns digits 255-4l .. 252-4l (highest digits first)
-      unsigned c4[4], s = 0u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c4[e] = hist[255 - 4 * tid - e];
-        s += c4[e];
-      }
-      unsigned incl = s;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const unsigned o = __shfl_up(incl, off);
-        if (tid >= off) incl += o;
-      }
-      unsigned above = incl - s;  // keys in higher digits
-      if ((int)above < rem && rem <= (int)incl) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if ((int)(above + c4[e]) >= rem) {
-            *sh_T = prefix | ((unsigned)(255 - 4 * tid - e) << shift);
-            *sh_rem = rem - (int)above;
-            break;
-          }
-          above += c4[e];
-        }
-      }
-    }
-    __syncthreads();
-    prefix = *sh_T;
-    rem = *sh_rem;
-    mask |= 0xFFu << shift;
-  }
-  *T = prefix;
-  *rem_eq = rem;
-}
-
-// block-wide min and max of v over 256 threads (tmp: 8 words of LDS)
-__device__ __forceinline__ void block_min_max_256(unsigned v_min, unsigned v_max, unsigned* tmp, unsigned* mn,
-                                                  unsigned* mx) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    v_min = min(v_min, (unsigned)__shfl_xor((int)v_min, off));
-    v_max = max(v_max, (unsigned)__shfl_xor((int)v_max, off));
-  }
-  if (lane == 0) {
-    tmp[wave] = v_min;
-    tmp[4 + wave] = v_max;
-  }
-  __syncthreads();
-  *mn = min(min(tmp[0], tmp[1]), min(tmp[2], tmp[3]));
-  *mx = max(max(tmp[4], tmp[5]), max(tmp[6], tmp[7]));
-}
+constexpr int kTopkBuckets = 2048;
 
 // LDS of one selection
 struct TopkLds {
-  unsigned hist[256];
-  unsigned mm_tmp[8];
+  unsigned hist[kTopkBuckets];
+  double red_lo[4], red_hi[4];
+  int red_n[4];
   int scan_tmp[4];
-  unsigned sh_T;
-  int sh_rem;
+  int sh_T, sh_rem, sh_all;
 };
+
+// min and max of the active scores and their count, over the 256 threads
+// (one workgroup barrier)
+template <int PT>
+__device__ __forceinline__ void active_range(const double (&wv)[PT], const bool (&act)[PT], TopkLds& sh, double* lo,
+                                             double* hi, int* n) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double l = __builtin_inf(), h = -__builtin_inf();
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+    if (act[i]) {
+      l = fmin(l, wv[i]);
+      h = fmax(h, wv[i]);
+      ++c;
+    }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    l = fmin(l, __shfl_xor(l, off));
+    h = fmax(h, __shfl_xor(h, off));
+    c += __shfl_xor(c, off);
+  }
+  if (lane == 0) {
+    sh.red_lo[wave] = l;
+    sh.red_hi[wave] = h;
+    sh.red_n[wave] = c;
+  }
+  __syncthreads();
+  *lo = fmin(fmin(sh.red_lo[0], sh.red_lo[1]), fmin(sh.red_lo[2], sh.red_lo[3]));
+  *hi = fmax(fmax(sh.red_hi[0], sh.red_hi[1]), fmax(sh.red_hi[2], sh.red_hi[3]));
+  *n = sh.red_n[0] + sh.red_n[1] + sh.red_n[2] + sh.red_n[3];
+}
 
 // A unit's scores W[0..MB): thread t holds ids t*per .. t*per+per-1,
 // per = ceil(MB/256) <= PT.  Ids past the unit's block count are loaded but
@@ -132,104 +90,106 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
     for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
     return;
   }
-  const int M = k - 1 - R;  // free picks among blocks 1..nb-R-1
-
-  bool cand[PT];
-  unsigned hi[PT], lo[PT];
-  unsigned hmin = 0xFFFFFFFFu, hmax = 0u;
+  // nb > k >= R + 1: the sink and the window do not meet
+  bool act[PT], take[PT];
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int j = j0 + i;
-    cand[i] = i < per && j >= 1 && j < nb - R;
-    const unsigned long long key = cand[i] ? order_key(wv[i]) : 0ull;
-    hi[i] = (unsigned)(key >> 32);
-    lo[i] = (unsigned)key;
-    if (cand[i]) {
-      hmin = min(hmin, hi[i]);
-      hmax = max(hmax, hi[i]);
-    }
+    act[i] = i < per && j >= 1 && j < nb - R;  // candidates
+    take[i] = false;
   }
-  // phase 1: threshold on the high 32 bits of the key
-  unsigned T_hi = 0u, T_lo = 0u;
-  int rem_hi = 0, rem_lo = 0, n_eq = 0;
-  bool need_lo = false;
-  bool eqh[PT];
-  if (M > 0) {
-    unsigned mn, mx;
-    block_min_max_256(hmin, hmax, sh.mm_tmp, &mn, &mx);
-    if (mn == mx) {
-      T_hi = mn;
-      rem_hi = M;
-    } else {
-      const int top_bit = 31 - __clz(mn ^ mx);
-      radix_select_u32<PT>(hi, cand, M, top_bit / 8, mn, sh.hist, &sh.sh_T, &sh.sh_rem, &T_hi, &rem_hi);
-    }
-    int cnt = 0;
+  int need = k - 1 - R;  // places left for undecided candidates
+  constexpr int BPT = kTopkBuckets / 256;  // buckets per thread
+  for (;;) {  // every round decides at least one candidate
+    // the round's histogram is cleared here; active_range's barrier orders
+    // the clear before the counting below
 #pragma unroll
-    for (int i = 0; i < PT; ++i) {
-      eqh[i] = cand[i] && hi[i] == T_hi;
-      cnt += eqh[i] ? 1 : 0;
+    for (int q = 0; q < BPT; ++q) sh.hist[q * 256 + tid] = 0u;
+    double lo, hi;
+    int n;
+    active_range<PT>(wv, act, sh, &lo, &hi, &n);
+    // (lo, hi, n and need are the same in every thread: the exits are uniform)
+    if (need == 0) break;
+    if (n <= need) {  // the undecided candidates fill the places left
+#pragma unroll
+      for (int i = 0; i < PT; ++i) take[i] = take[i] || act[i];
+      break;
     }
-    int tot;
-    (void)block_exclusive_scan_256(cnt, sh.scan_tmp, &tot);
-    n_eq = tot;
-    // phase 2 (only when the threshold bucket holds more keys than needed):
-    // threshold on the low 32 bits among the keys tied on the high bits
-    need_lo = rem_hi < n_eq;
-    if (need_lo) {
-      unsigned lmin = 0xFFFFFFFFu, lmax = 0u;
+    if (!(lo < hi)) {  // one score left: the lowest ids win
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) c += act[i] ? 1 : 0;
+      int tot;
+      int before = block_exclusive_scan_256(c, sh.scan_tmp, &tot);
 #pragma unroll
       for (int i = 0; i < PT; ++i)
-        if (eqh[i]) {
-          lmin = min(lmin, lo[i]);
-          lmax = max(lmax, lo[i]);
+        if (act[i]) {
+          take[i] = take[i] || before < need;
+          ++before;
         }
-      unsigned mn2, mx2;
-      block_min_max_256(lmin, lmax, sh.mm_tmp, &mn2, &mx2);
-      if (mn2 == mx2) {
-        T_lo = mn2;
-        rem_lo = rem_hi;
-      } else {
-        const int top_bit = 31 - __clz(mn2 ^ mx2);
-        radix_select_u32<PT>(lo, eqh, rem_hi, top_bit / 8, mn2, sh.hist, &sh.sh_T, &sh.sh_rem, &T_lo, &rem_lo);
+      break;
+    }
+    // bucket of each undecided candidate, nondecreasing in its score: lo in
+    // bucket 0, hi in the last bucket
+    const double scale = (double)(kTopkBuckets - 1) / (hi - lo);
+    int bk[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) {
+      const double x = (wv[i] - lo) * scale;
+      int v = -1;
+      if (act[i]) v = wv[i] == lo ? 0 : (wv[i] == hi || !(x < kTopkBuckets - 1) ? kTopkBuckets - 1 : (int)x);
+      bk[i] = v;
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      if (bk[i] >= 0) atomicAdd(&sh.hist[bk[i]], 1u);
+    __syncthreads();
+    // thread t sums buckets last-BPT*t down to last-BPT*t-(BPT-1) (from the top)
+    unsigned cnt[BPT];
+    int s = 0;
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      cnt[q] = sh.hist[kTopkBuckets - 1 - BPT * tid - q];
+      s += (int)cnt[q];
+    }
+    int tot;
+    int above = block_exclusive_scan_256(s, sh.scan_tmp, &tot);
+    if (above < need && need <= above + s) {  // exactly one thread
+#pragma unroll
+      for (int q = 0; q < BPT; ++q) {
+        if (above + (int)cnt[q] >= need) {
+          sh.sh_T = kTopkBuckets - 1 - BPT * tid - q;
+          sh.sh_rem = need - above;
+          sh.sh_all = above + (int)cnt[q] == need;  // the bucket fills the places exactly
+          break;
+        }
+        above += (int)cnt[q];
       }
     }
-  } else {
+    __syncthreads();
+    const int T = sh.sh_T;
+    need = sh.sh_rem;
+    const bool all = sh.sh_all != 0;
 #pragma unroll
-    for (int i = 0; i < PT; ++i) eqh[i] = false;
+    for (int i = 0; i < PT; ++i) {
+      take[i] = take[i] || bk[i] > T || (all && bk[i] == T);
+      act[i] = act[i] && bk[i] == T;
+    }
+    if (all) break;
   }
-  // ties on the full key go to the lowest block ids
-  int n_tie = 0;
-#pragma unroll
-  for (int i = 0; i < PT; ++i) n_tie += (need_lo && eqh[i] && lo[i] == T_lo) ? 1 : 0;
-  int tot;
-  int tie_before = block_exclusive_scan_256(n_tie, sh.scan_tmp, &tot);
+  // ascending output: the sink, the chosen candidates, the window
   int n_sel = 0;
   unsigned chosen = 0u;  // bit i: id j0+i selected
 #pragma unroll
   for (int i = 0; i < PT; ++i) {
     const int j = j0 + i;
     if (i >= per || j >= nb) continue;
-    bool take;
-    if (j == 0 || j >= nb - R) {
-      take = true;
-    } else if (!cand[i] || M == 0) {
-      take = false;
-    } else if (hi[i] != T_hi) {
-      take = hi[i] > T_hi;
-    } else if (!need_lo) {
-      take = true;  // the whole bucket is needed
-    } else if (lo[i] != T_lo) {
-      take = lo[i] > T_lo;
-    } else {
-      take = tie_before < rem_lo;
-      ++tie_before;
-    }
-    if (take) {
+    if (j == 0 || j >= nb - R || take[i]) {
       chosen |= 1u << i;
       ++n_sel;
     }
   }
+  int tot;
   int pos = block_exclusive_scan_256(n_sel, sh.scan_tmp, &tot);
 #pragma unroll
   for (int i = 0; i < PT; ++i)
