@@ -77,6 +77,9 @@ def main(argv=None) -> int:
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--selection-study", action="store_true",
+                    help="instead of the step benchmark: selection churn and hot-buffer misses over a "
+                         "drifting query, plain / smoothed / recent window / both (one JSON line)")
     ap.add_argument("--separate-topk", action="store_true",
                     help="time the step with the top-k as a launch of its own (kvs_select_topk_ex + "
                          "kvs_sparse_decode_attn) instead of inside the attention launch")
@@ -107,6 +110,8 @@ def main(argv=None) -> int:
         print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
         return 0
     w = synth.WORKLOADS[args.workload]
+    if args.selection_study:
+        return selection_study(args, w, dev)
     if w.hot_slots:
         return bench_hot(args, w, dev)
     code = kvs.DTYPE_CODE
@@ -413,6 +418,79 @@ def bench_hot(args, w, dev) -> int:
         "cpu_baseline": None,
     }
     print(json.dumps(result), flush=True)
+    return 0
+
+
+def selection_study(args, w, dev) -> int:
+    """How stable the selection is from one decode step to the next ("SparDA…"
+    §6.1 smooths the scores so that the mask stops jumping; §4.2 keeps a
+    recent window), and what that does to a hot buffer of k slots per unit
+    ("KV 稀疏化" §7): every block that enters the selection is a miss copied
+    in over the host link.  The query drifts as a seeded random walk
+    q <- rho*q + sqrt(1-rho^2)*noise (rho = 0.95), the stand-in for a
+    decode's successive queries; the cache is the workload's first layer.
+    For each variant the steps run eagerly: kvs_select_topk_ex (exact
+    scores, smoothing state kept across steps), kvs_hot_lookup_swapin,
+    attention through the hot table."""
+    import torch
+
+    from query_aware_sparse_kvs_amd import kvs, synth
+    from query_aware_sparse_kvs_amd.step import HotBufferStep, SparseDecodeStep
+
+    code = kvs.DTYPE_CODE
+    L = kvs.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code[w.q_dtype], code[w.kv_dtype],
+                   w.quant_group)
+    inp = synth.make_inputs(w, dev, layer=0)
+    st = SparseDecodeStep(L, w.k, dev)
+    summ = st.new_summaries(dev)
+    st.prefill_summaries(inp["k_pool"], inp["k_scales"], inp["block_table"], inp["seq_lens"], summ)
+    pages = inp["block_table"].long().cpu()
+    host = [None if inp[n] is None else inp[n].cpu()[pages].transpose(1, 2).contiguous().pin_memory()
+            for n in ("k_pool", "v_pool", "k_scales", "v_scales")]
+    steps, rho = 64, 0.95
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed * 7919 + 11)
+    qs = [inp["q"].float()]
+    for _ in range(steps):
+        noise = torch.randn(qs[-1].shape, generator=g, device=dev)
+        qs.append(rho * qs[-1] + math.sqrt(1.0 - rho * rho) * noise)
+    qs = [x.to(inp["q"].dtype).contiguous() for x in qs]
+    variants = {"plain": (1, False), "ema0.7": (1, True), "window8": (8, False), "window8+ema0.7": (8, True)}
+    units = w.B * w.Hkv
+    kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    tile = w.S * w.D * kv_elem + (w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0)
+    res = {}
+    for name, (recent, ema) in variants.items():
+        state = torch.full((w.B, w.Hkv, w.nb), float("nan"), dtype=torch.float64, device=dev)
+        opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None)
+        hs = HotBufferStep(L, w.k, w.k, dev)
+        misses = []
+        t_sel = t_swap = t_attn = 0.0
+        for t, q in enumerate(qs):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            kvs.kvs_select_topk_ex(L, q, summ, inp["seq_lens"], w.k, opts, None, st.sel, None, st.select_ws)
+            ev[1].record()
+            hs.swap_in(t, st.sel, *host)
+            ev[2].record()
+            hs.attend(q, st.sel, inp["seq_lens"])
+            ev[3].record()
+            torch.cuda.synchronize()
+            if t > 0:  # step 0 fills the empty buffer
+                misses.append(int(hs.miss_count.sum().item()))
+                t_sel += ev[0].elapsed_time(ev[1]) / 1e3
+                t_swap += ev[1].elapsed_time(ev[2]) / 1e3
+                t_attn += ev[2].elapsed_time(ev[3]) / 1e3
+        n = len(misses)
+        res[name] = {"misses_per_step": round(sum(misses) / n, 2),
+                     "misses_per_unit_step": round(sum(misses) / n / units, 3),
+                     "host_link_bytes_per_step": int(sum(misses) / n * 2 * tile),
+                     "select_us": round(t_sel / n * 1e6, 2), "swap_in_us": round(t_swap / n * 1e6, 2),
+                     "attention_us": round(t_attn / n * 1e6, 2)}
+    assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
+    print(json.dumps({"study": "selection stability over a drifting query", "workload": w.name,
+                      "steps": steps, "rho": rho, "k": w.k, "hot_slots_per_unit": w.k, "units": units,
+                      "launch": "eager, per call HIP events", "variants": res}), flush=True)
     return 0
 
 
