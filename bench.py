@@ -77,6 +77,9 @@ def main(argv=None) -> int:
                     help="only run a plain device copy of MIB MiB five times (the reference kernel "
                          "for scaling HBM byte counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--prefetch", action="store_true",
+                    help="hot-buffer workload: swap in the next layer's misses on a second stream while the "
+                         "current layer attends (selections known one layer ahead)")
     ap.add_argument("--selection-study", action="store_true",
                     help="instead of the step benchmark: selection churn and hot-buffer misses over a "
                          "drifting query, plain / smoothed / recent window / both (one JSON line)")
@@ -326,7 +329,7 @@ def bench_hot(args, w, dev) -> int:
     kvs.kvs_select_topk(L, inp["q"], summ, inp["seq_lens"], w.k, st.sel, None, st.select_ws)
     sel0 = st.sel.cpu().numpy()
     per_phase = (args.warmup + args.steps) // n_layers + 2
-    stream = synth.drift_selections(sel0, w.nb, 3 * per_phase, w.drift, seed=w.seed)
+    stream = synth.drift_selections(sel0, w.nb, 4 * per_phase, w.drift, seed=w.seed)
     sels = torch.from_numpy(stream).to(dev)
     # host tier [B][Hkv][MB][S][D] (V tiles [D][S]), pinned and shared by the layer instances
     pages = inp["block_table"].long().cpu()
@@ -373,6 +376,30 @@ def bench_hot(args, w, dev) -> int:
     t_step = timed(step)
     t_swap = timed(only_swap)
     t_attn = timed(only_attend)
+    t_pipe = None
+    if args.prefetch:
+        from query_aware_sparse_kvs_amd.step import HotPrefetchPipeline
+        pipe = HotPrefetchPipeline(hs, dev)
+        nxt = {"i": 0}
+
+        def prefetch(i):
+            h_i = i % n_layers
+            t = m[h_i]
+            pipe.prefetch(h_i, t, sels[t], *host)
+
+        def piped(i):  # layer i attends while layer i+1's misses come in
+            if nxt["i"] <= i:
+                prefetch(i)
+                nxt["i"] = i + 1
+            prefetch(i + 1)
+            nxt["i"] = i + 2
+            h_i = i % n_layers
+            t = m[h_i]
+            pipe.attend(h_i, inp["q"], sels[t], inp["seq_lens"])
+            m[h_i] += 1
+
+        t_pipe = timed(piped)
+        torch.cuda.synchronize()
     miss = hs[0].miss_count.sum().item()
     assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
     # pinned host -> device copy rate of the runtime, for reference
@@ -394,19 +421,22 @@ def bench_hot(args, w, dev) -> int:
     units = w.B * w.Hkv
     attn_bytes = units * w.k * 2 * tile + w.B * w.Hq * w.D * (2 + 4)
     link_gbps = link_bytes / t_swap / 1e9
+    t_best = t_pipe if t_pipe is not None else t_step
     result = {
         "metric": METRIC,
-        "value": round(w.B / t_step, 1),
+        "value": round(w.B / t_best, 1),
         "unit": "query-tokens/s/layer",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(t_step * 1e3, 5),
+        "ms_per_step": round(t_best * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
                    "context": w.L, "block": w.S, "top_k_blocks": w.k, "hot_slots": w.hot_slots,
                    "drift_per_step": w.drift, "kv_storage": w.kv_dtype, "layer_instances": n_layers,
-                   "graph_replay": False},
-        "phase_us": {"swap_in": round(t_swap * 1e6, 3), "attention": round(t_attn * 1e6, 3)},
+                   "graph_replay": False, "prefetch_next_layer": bool(args.prefetch)},
+        "phase_us": {"swap_in": round(t_swap * 1e6, 3), "attention": round(t_attn * 1e6, 3),
+                     "sequential_step": round(t_step * 1e6, 3),
+                     "prefetched_step": None if t_pipe is None else round(t_pipe * 1e6, 3)},
         "misses_per_step": int(miss),
         "roofline": {"bound": "host-link", "kernel": "kvs_hot_lookup_swapin",
                      "achieved": round(link_gbps, 2), "peak": 64.0, "unit": "GB/s",

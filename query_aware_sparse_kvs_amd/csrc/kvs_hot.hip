@@ -14,10 +14,10 @@
 //      sort in LDS orders them, so the r-th smallest is the r-th victim;
 //   4. the r-th miss takes the r-th victim (old owner unmapped).
 //   Integer work only; latency-bound.
-// swapin_copy_kernel: one workgroup per (miss slot r, unit); the workgroup
-//   of a real miss copies that block's K and V tiles (and fp8 scales) from
-//   pinned host memory into its hot slot with 16-byte loads, all issued
-//   before the stores.  Bound by the host link.
+// swapin_copy_kernel: two workgroups per unit, each copying every other
+//   miss's K and V tiles (and fp8 scales) from pinned host memory into its
+//   hot slot with 16-byte loads, a tile's loads all issued before its
+//   stores.  Bound by the host link.
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -145,55 +145,63 @@ __global__ __launch_bounds__(256) void hot_lookup_kernel(HotArgs a) {
   }
 }
 
+// Copy workgroups per unit: each takes every kCopyGroups-th miss of its unit.
+// Few workgroups suffice to keep the host link busy (two tiles of 16 KiB per
+// workgroup in flight), and they leave most SIMDs free for kernels that run
+// beside the copy (the attention of another layer).
+constexpr int kCopyGroups = 2;
+
 __global__ __launch_bounds__(256) void swapin_copy_kernel(HotArgs a) {
-  const int r = blockIdx.x, u = blockIdx.y, tid = threadIdx.x;
-  const int m = a.miss_count[u];
-  if (r >= m) return;
-  const int j = a.miss_list[(long long)u * a.k + r];
-  if (j < 0 || j >= a.MB) return;
-  const int slot = a.pt[(long long)u * a.MB + j];
-  if (slot < u * a.ns || slot >= (u + 1) * a.ns) {
-    if (tid == 0) raise_flag(a.err, 0x2u);
-    return;
-  }
+  const int u = blockIdx.y, tid = threadIdx.x;
+  int m = a.miss_count[u];
+  m = m < 0 ? 0 : (m > a.k ? a.k : m);  // miss_list holds k entries per unit
   const long long tile_bytes = (long long)a.S * a.D * a.elem_bytes;
-  const long long src_off = ((long long)u * a.MB + j) * tile_bytes;
-  const long long dst_off = (long long)slot * tile_bytes;
   const int n16 = (int)(tile_bytes / 16);
-  const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_k) + src_off);
-  const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_v) + src_off);
-  u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_k) + dst_off);
-  u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_v) + dst_off);
   constexpr int kMaxPer = 8;  // 16-byte vectors per thread per round
-  for (int x0 = 0; x0 < n16; x0 += 256 * kMaxPer) {
-    u32x4 bk[kMaxPer], bv[kMaxPer];
+  for (int r = blockIdx.x; r < m; r += kCopyGroups) {  // m is uniform over the workgroup
+    const int j = a.miss_list[(long long)u * a.k + r];
+    if (j < 0 || j >= a.MB) continue;
+    const int slot = a.pt[(long long)u * a.MB + j];
+    if (slot < u * a.ns || slot >= (u + 1) * a.ns) {
+      if (tid == 0) raise_flag(a.err, 0x2u);
+      continue;
+    }
+    const long long src_off = ((long long)u * a.MB + j) * tile_bytes;
+    const long long dst_off = (long long)slot * tile_bytes;
+    const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_k) + src_off);
+    const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_v) + src_off);
+    u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_k) + dst_off);
+    u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_v) + dst_off);
+    for (int x0 = 0; x0 < n16; x0 += 256 * kMaxPer) {
+      u32x4 bk[kMaxPer], bv[kMaxPer];
 #pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-      const int x = x0 + q * 256 + tid;
-      bk[q] = bv[q] = u32x4{0u, 0u, 0u, 0u};
-      if (x < n16) {
-        bk[q] = sk[x];
-        bv[q] = sv[x];
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int x = x0 + q * 256 + tid;
+        bk[q] = bv[q] = u32x4{0u, 0u, 0u, 0u};
+        if (x < n16) {
+          bk[q] = sk[x];
+          bv[q] = sv[x];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kMaxPer; ++q) {
+        const int x = x0 + q * 256 + tid;
+        if (x < n16) {
+          dk[x] = bk[q];
+          dv[x] = bv[q];
+        }
       }
     }
-#pragma unroll
-    for (int q = 0; q < kMaxPer; ++q) {
-      const int x = x0 + q * 256 + tid;
-      if (x < n16) {
-        dk[x] = bk[q];
-        dv[x] = bv[q];
+    if (a.qg > 0) {
+      const int ns_per_tile = a.S * (a.D / a.qg);
+      const float* ssk = a.host_ks + ((long long)u * a.MB + j) * ns_per_tile;
+      const float* ssv = a.host_vs + ((long long)u * a.MB + j) * ns_per_tile;
+      float* dsk = a.hot_ks + (long long)slot * ns_per_tile;
+      float* dsv = a.hot_vs + (long long)slot * ns_per_tile;
+      for (int x = tid; x < ns_per_tile; x += 256) {
+        dsk[x] = ssk[x];
+        dsv[x] = ssv[x];
       }
-    }
-  }
-  if (a.qg > 0) {
-    const int ns_per_tile = a.S * (a.D / a.qg);
-    const float* ssk = a.host_ks + ((long long)u * a.MB + j) * ns_per_tile;
-    const float* ssv = a.host_vs + ((long long)u * a.MB + j) * ns_per_tile;
-    float* dsk = a.hot_ks + (long long)slot * ns_per_tile;
-    float* dsv = a.hot_vs + (long long)slot * ns_per_tile;
-    for (int x = tid; x < ns_per_tile; x += 256) {
-      dsk[x] = ssk[x];
-      dsv[x] = ssv[x];
     }
   }
 }
@@ -207,7 +215,7 @@ hipError_t launch_hot(const HotArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(hot_lookup_kernel, dim3((unsigned)units), dim3(256), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(swapin_copy_kernel, dim3((unsigned)a.k, (unsigned)units), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(swapin_copy_kernel, dim3((unsigned)kCopyGroups, (unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -171,3 +171,44 @@ class HotBufferStep:
     def run(self, step, sel, q, seq_lens, host_k, host_v, host_ks=None, host_vs=None, stream=None):
         self.swap_in(step, sel, host_k, host_v, host_ks, host_vs, stream)
         return self.attend(q, sel, seq_lens, stream)
+
+
+class HotPrefetchPipeline:
+    """Hot-buffer decode steps over several layers whose selections are known
+    one layer ahead (the premise of selecting KV a layer early, "SparDA…"
+    §3–4): the swap-in of layer i+1's misses runs on a second stream while
+    layer i attends, so the host-link copies leave the decode critical path
+    ("KV 稀疏化" §7 names misses on that path as the cost of the hot buffer).
+
+    Each layer has its own HotBufferStep.  Layer i's attention waits for its
+    own swap-in (an event on the copy stream); a swap-in into layer i's
+    buffer waits for the previous attention that read it (an event on the
+    compute stream).  Both streams keep the default priority."""
+
+    def __init__(self, steps: list, device="cuda"):
+        self.hs = steps
+        dev = torch.device(device)
+        self.copy_stream = torch.cuda.Stream(device=dev)
+        self.ready = [torch.cuda.Event() for _ in steps]
+        self.done = [torch.cuda.Event() for _ in steps]
+        self.used = [False for _ in steps]
+
+    def prefetch(self, i, step, sel, host_k, host_v, host_ks=None, host_vs=None):
+        """Enqueues layer i's swap-in on the copy stream."""
+        cur = torch.cuda.current_stream()
+        s = self.copy_stream
+        s.wait_stream(cur)  # sel and everything before it are ready
+        if self.used[i]:
+            s.wait_event(self.done[i])  # the buffer's last attention has read its slots
+        with torch.cuda.stream(s):
+            self.hs[i].swap_in(step, sel, host_k, host_v, host_ks, host_vs)
+        self.ready[i].record(s)
+
+    def attend(self, i, q, sel, seq_lens) -> torch.Tensor:
+        """Layer i's attention on the current stream, after its swap-in."""
+        cur = torch.cuda.current_stream()
+        cur.wait_event(self.ready[i])
+        out = self.hs[i].attend(q, sel, seq_lens)
+        self.done[i].record(cur)
+        self.used[i] = True
+        return out

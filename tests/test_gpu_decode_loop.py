@@ -363,3 +363,43 @@ def test_score_blocks_then_select_attn(env, case):
         err, rel = check_attn(out, o_out)
         p.inp["q"] = _drift_q(env, p.inp["q"], rng)
     print(f"[score+select-attn {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
+
+
+def test_prefetch_pipeline_matches_sequential_hot_steps(env):
+    """Layers' swap-ins issued one layer ahead on a second stream (the copy
+    for layer i+1 while layer i attends) give exactly the outputs, page
+    tables and slot states of the same steps run one after another."""
+    torch, kvs, synth = env.torch, env.kvs, env.synth
+    from query_aware_sparse_kvs_amd.step import HotBufferStep, HotPrefetchPipeline
+    w = synth.scaled(synth.WORKLOADS["llama8b"], B=2, L=64 * 40, Hkv=2, Hq=8, layers=1, k=10)
+    p = Problem(env, w)
+    L = p.L
+    n_layers, steps = 3, 7
+    print(f"[prefetch] {n_layers} layers x {steps} steps, units {L.num_seqs * L.num_kv_heads}, k {w.k}",
+          flush=True)
+    sel0 = synth.random_selection(w, p.h["lens"], w.k, seed=4)
+    stream = synth.drift_selections(sel0, w.nb, n_layers * steps + 2, 3, seed=5)
+    sels = torch.from_numpy(stream).to(env.dev)
+    pages = p.inp["block_table"].long().cpu()
+    host = [p.inp[n].cpu()[pages].transpose(1, 2).contiguous().pin_memory() for n in ("k_pool", "v_pool")]
+    seq = [HotBufferStep(L, w.k, w.k, env.dev) for _ in range(n_layers)]
+    pip = [HotBufferStep(L, w.k, w.k, env.dev) for _ in range(n_layers)]
+    pipe = HotPrefetchPipeline(pip, env.dev)
+    outs_seq, outs_pip = [], []
+    t_of = lambda i: 1 + i  # stream entry of step i (entry 0 is the warm start)
+    for h in seq + pip:
+        h.run(0, sels[0], p.inp["q"], p.inp["seq_lens"], *host)
+    for i in range(n_layers * steps):
+        outs_seq.append(seq[i % n_layers].run(t_of(i), sels[t_of(i)], p.inp["q"], p.inp["seq_lens"], *host).clone())
+    pipe.prefetch(0, t_of(0), sels[t_of(0)], *host)
+    for i in range(n_layers * steps):
+        if i + 1 < n_layers * steps:
+            pipe.prefetch((i + 1) % n_layers, t_of(i + 1), sels[t_of(i + 1)], *host)
+        outs_pip.append(pipe.attend(i % n_layers, p.inp["q"], sels[t_of(i)], p.inp["seq_lens"]).clone())
+    torch.cuda.synchronize()
+    no_device_errors(env)
+    for i, (a, b) in enumerate(zip(outs_seq, outs_pip)):
+        assert torch.equal(a, b), f"step {i}: outputs differ"
+    for a, b in zip(seq, pip):
+        for n in ("page_table", "slot_owner", "slot_stamp", "hot_k", "hot_v"):
+            assert torch.equal(getattr(a, n), getattr(b, n)), f"{n} differs"
