@@ -65,6 +65,8 @@ def lib():
             "or_select_window": (ctypes.c_int, [LP, P, P, i32, i32, P]),
             "or_ema_scores": (ctypes.c_int, [LP, P, P, f64, P, P]),
             "or_append_token": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+            "or_summaries_mean": (ctypes.c_int, [LP, P, P, P, P, P, i32, P]),
+            "or_mean_scores": (ctypes.c_int, [LP, P, P, P, P, P]),
             "or_sparse_attn": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, i32, f64, P]),
             "or_dense_attn": (ctypes.c_int, [LP, P, P, P, P, P, P, P, f64, P]),
             "or_hot_step": (ctypes.c_int, [i32, i32, i32, i64, i32, P, P, P, P, P, P]),
@@ -158,6 +160,36 @@ def bounds(L: Layout, q, summ, seq_lens, want_u=False):
     U = np.empty((L.B, L.Hq, L.max_blocks), dtype=np.float64) if want_u else None
     _check(lib().or_bounds(ctypes.byref(L.c()), _ptr(q), _ptr(summ), _ptr(sl), _ptr(U), _ptr(W)),
            "or_bounds")
+    return (W, U) if want_u else W
+
+
+def summaries_mean(L: Layout, k_pool, k_scales, block_table, seq_lens, first_block=None,
+                   num_rebuild=None, out=None):
+    """Returns (or fills) the [B][Hkv][max_blocks][D] fp32 mean table."""
+    kp = _pool(L, k_pool)
+    ks = _c(k_scales, np.float32)
+    bt = _c(block_table, np.int32)
+    sl = _c(seq_lens, np.int32)
+    fb = _c(first_block, np.int32)
+    if num_rebuild is None:
+        num_rebuild = L.max_blocks
+    if out is None:
+        out = np.full((L.B, L.Hkv, L.max_blocks, L.D), np.nan, dtype=np.float32)
+    assert out.dtype == np.float32 and out.flags.c_contiguous
+    _check(lib().or_summaries_mean(ctypes.byref(L.c()), _ptr(kp), _ptr(ks), _ptr(bt), _ptr(sl), _ptr(fb),
+                                   num_rebuild, _ptr(out)), "or_summaries_mean")
+    return out
+
+
+def mean_scores(L: Layout, q, mean, seq_lens, want_u=False):
+    """Returns W [B][Hkv][max_blocks] (and U [B][Hq][max_blocks] if asked)."""
+    q = _c(q, np.float64)
+    mean = _c(mean, np.float32)
+    sl = _c(seq_lens, np.int32)
+    W = np.empty((L.B, L.Hkv, L.max_blocks), dtype=np.float64)
+    U = np.empty((L.B, L.Hq, L.max_blocks), dtype=np.float64) if want_u else None
+    _check(lib().or_mean_scores(ctypes.byref(L.c()), _ptr(q), _ptr(mean), _ptr(sl), _ptr(U), _ptr(W)),
+           "or_mean_scores")
     return (W, U) if want_u else W
 
 

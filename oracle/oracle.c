@@ -602,3 +602,74 @@ int or_append_token(const or_layout* L, const void* k_new, const void* v_new,
   }
   return OR_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* mean summaries                                                      */
+/* ------------------------------------------------------------------ */
+
+int or_summaries_mean(const or_layout* L, const void* k_pool, const float* k_scales,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* first_block, int32_t num_rebuild, float* out) {
+  if (!layout_ok(L) || !k_pool || !block_table || !seq_lens || !out) return OR_EARG;
+  if (L->kv_dtype == 2 && !k_scales) return OR_EARG;
+  if (num_rebuild < 0) return OR_EARG;
+  for (int32_t b = 0; b < L->B; ++b) {
+    int32_t len = seq_lens[b];
+    if (!len_ok(L, len)) return OR_ERANGE;
+    int32_t nb = num_blocks(L, len);
+    int32_t j0 = first_block ? first_block[b] : 0;
+    if (j0 < 0) return OR_ERANGE;
+    int64_t j1 = (int64_t)j0 + num_rebuild;
+    if (j1 > nb) j1 = nb;
+    for (int32_t j = j0; j < j1; ++j) {
+      int32_t page = block_table[(int64_t)b * L->max_blocks + j];
+      if (page < 0 || page >= L->num_pages) return OR_ERANGE;
+      int32_t t_end = (j + 1) * L->S < len ? (j + 1) * L->S : len;
+      int32_t n = t_end - j * L->S;
+      for (int32_t g = 0; g < L->Hkv; ++g) {
+        float* m = out + (((int64_t)b * L->Hkv + g) * L->max_blocks + j) * L->D;
+        for (int32_t c = 0; c < L->D; ++c) {
+          double sum = 0.0;
+          for (int32_t t = j * L->S; t < t_end; ++t)
+            sum = sum + kv_value(L, k_pool, k_scales, page, g, t - j * L->S, c);
+          double mean = sum / (double)n;
+          m[c] = (float)mean;
+        }
+      }
+    }
+  }
+  return OR_OK;
+}
+
+int or_mean_scores(const or_layout* L, const double* q, const float* mean,
+                   const int32_t* seq_lens, double* U, double* W) {
+  if (!layout_ok(L) || !q || !mean || !seq_lens || !W) return OR_EARG;
+  int32_t G = L->Hq / L->Hkv;
+  for (int32_t b = 0; b < L->B; ++b) {
+    int32_t len = seq_lens[b];
+    if (!len_ok(L, len)) return OR_ERANGE;
+    int32_t nb = num_blocks(L, len);
+    for (int32_t g = 0; g < L->Hkv; ++g) {
+      double* w = W + ((int64_t)b * L->Hkv + g) * L->max_blocks;
+      for (int32_t j = 0; j < L->max_blocks; ++j) w[j] = -INFINITY;
+    }
+    for (int32_t h = 0; h < L->Hq; ++h) {
+      int32_t g = h / G;
+      const double* qh = q + ((int64_t)b * L->Hq + h) * L->D;
+      double* w = W + ((int64_t)b * L->Hkv + g) * L->max_blocks;
+      double* u = U ? U + ((int64_t)b * L->Hq + h) * L->max_blocks : NULL;
+      for (int32_t j = 0; j < L->max_blocks; ++j) {
+        if (j >= nb) {
+          if (u) u[j] = -INFINITY;
+          continue;
+        }
+        const float* m = mean + (((int64_t)b * L->Hkv + g) * L->max_blocks + j) * L->D;
+        double acc = 0.0;
+        for (int32_t c = 0; c < L->D; ++c) acc = acc + qh[c] * (double)m[c];
+        if (u) u[j] = acc;
+        if (acc > w[j]) w[j] = acc;
+      }
+    }
+  }
+  return OR_OK;
+}

@@ -181,6 +181,22 @@ int or_append_token(const or_layout* L, const void* k_new, const void* v_new,
                     double* summ, void* host_k, void* host_v,
                     float* host_k_scales, float* host_v_scales);
 
+/* Mean summaries ("KV 稀疏化" §5 lists the mean beside min and max as a
+ * block summary): per block and channel, the mean of K over the block's
+ * valid tokens, mean = fp32(sum / n) with the sum in fp64 over ascending
+ * token positions and the division in fp64.  out is
+ * [B][Hkv][max_blocks][D] fp32; block range as for or_summaries. */
+int or_summaries_mean(const or_layout* L, const void* k_pool, const float* k_scales,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      const int32_t* first_block, int32_t num_rebuild, float* out);
+
+/* Score of a block from its mean: U[b][h][j] = sum_{c=0}^{D-1} q[b][h][c] *
+ * mean[c] in fp64, ascending c (an estimate of the block's typical q.k, not
+ * a bound); W[b][g][j] = max over the group's heads; -inf for j >= nb_b.
+ * U may be NULL. */
+int or_mean_scores(const or_layout* L, const double* q, const float* mean,
+                   const int32_t* seq_lens, double* U, double* W);
+
 #ifdef __cplusplus
 }
 #endif

@@ -271,3 +271,80 @@ def test_ema_limits_and_new_blocks(orc):
     assert out[1, 0, 2] == W[1, 0, 2]  # no history yet: the score itself
     with pytest.raises(orc.OracleError):
         orc.ema_scores(L, W, lens, 1.5, state)
+
+
+# ---------------------------------------------------------------------------
+# mean summaries
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype,qg,S", [(1, 0, 4), (1, 0, 16), (0, 0, 4), (2, 4, 4)])
+def test_mean_summaries_are_the_mean_of_the_valid_tokens(orc, kv_dtype, qg, S):
+    lens = (3 * S + 1, S, 2 * S - 1)
+    c = _appended_cache(orc, kv_dtype, qg, S, lens, seed=51 + S)
+    L = c["L"]
+    m = orc.summaries_mean(L, c["kp"], c["ks"], c["pages"], np.asarray(lens, np.int32))
+    for b, n in enumerate(lens):
+        for j in range((n + S - 1) // S):
+            blk = c["valk"][b, :, j * S: min((j + 1) * S, n)]  # [Hkv][t][D]
+            # fp64 sums of these values are exact (bf16 / small fp8 values), so
+            # numpy's summation order gives the same double; one fp32 rounding
+            if kv_dtype != orc.KV_F32:
+                want = (blk.sum(axis=1) / blk.shape[1]).astype(np.float32)
+                assert np.array_equal(m[b, :, j], want)
+            else:  # fp32 values: compare with the ascending-order fp64 sum
+                acc = np.zeros(blk.shape[::2])
+                for t in range(blk.shape[1]):
+                    acc = acc + blk[:, t, :]
+                assert np.array_equal(m[b, :, j], (acc / blk.shape[1]).astype(np.float32))
+            # the mean lies inside the block's min/max box
+            assert (m[b, :, j] >= c["summ"][b, :, j, 0]).all() and (m[b, :, j] <= c["summ"][b, :, j, 1]).all()
+        assert np.isnan(m[b, :, (n + S - 1) // S:]).all()
+
+
+def test_mean_of_a_single_token_block_is_the_key_and_its_score_the_dot_product(orc):
+    rng = np.random.default_rng(61)
+    B, Hkv, Hq, D, MB = 2, 2, 4, 16, 5
+    L = orc.Layout(B, Hq, Hkv, D, 1, MB, B * MB, orc.KV_BF16, 0)
+    x = torch.from_numpy(rng.standard_normal((B * MB, Hkv, 1, D)).astype(np.float32)).to(torch.bfloat16)
+    kp = x.view(torch.int16).numpy().view(np.uint16).copy()
+    table = np.arange(B * MB, dtype=np.int32).reshape(B, MB)
+    lens = np.array([MB, 3], np.int32)
+    m = orc.summaries_mean(L, kp, None, table, lens)
+    kv = x.double().numpy()
+    for b in range(B):
+        for j in range(lens[b]):
+            assert np.array_equal(m[b, :, j], kv[table[b, j], :, 0].astype(np.float32))
+    q = rng.standard_normal((B, Hq, D))
+    W, U = orc.mean_scores(L, q, m, lens, want_u=True)
+    summ = orc.summaries(L, kp, None, table, lens)
+    Wb, Ub = orc.bounds(L, q, summ, lens, want_u=True)  # S = 1: the box bound is q.k too
+    for b in range(B):
+        assert np.array_equal(U[b, :, :lens[b]], Ub[b, :, :lens[b]])
+        assert np.array_equal(W[b, :, :lens[b]], Wb[b, :, :lens[b]])
+        assert np.isneginf(W[b, :, lens[b]:]).all()
+
+
+def test_mean_score_never_exceeds_the_box_bound(orc):
+    """mean lies in [min, max] per channel, so each term q*mean <= max(q*min,
+    q*max) and, summed in the same order, the mean score <= the bound
+    (exactly, by monotone rounding)."""
+    S = 8
+    lens = (5 * S - 3, 2 * S, S + 1)
+    c = _appended_cache(orc, orc.KV_BF16, 0, S, lens, seed=71, MB=6)
+    L = c["L"]
+    ln = np.asarray(lens, np.int32)
+    m = orc.summaries_mean(L, c["kp"], None, c["pages"], ln)
+    q = c["rng"].standard_normal((L.B, L.Hq, L.D))
+    Wm, Um = orc.mean_scores(L, q, m, ln, want_u=True)
+    Wb, Ub = orc.bounds(L, q, c["summ"], ln, want_u=True)
+    for b, n in enumerate(lens):
+        nb = (n + S - 1) // S
+        assert (Um[b, :, :nb] <= Ub[b, :, :nb]).all()
+        assert (Wm[b, :, :nb] <= Wb[b, :, :nb]).all()
+        # and it is the dot product with the mean of the block's keys
+        G = L.Hq // L.Hkv
+        for h in range(L.Hq):
+            for j in range(nb):
+                blk = c["valk"][b, h // G, j * S: min((j + 1) * S, n)]
+                est = q[b, h] @ blk.mean(axis=0)
+                assert abs(Um[b, h, j] - est) <= 1e-6 * (1 + abs(est))
