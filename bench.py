@@ -136,7 +136,10 @@ def main(argv=None) -> int:
                              v_new_scales=nt["v_new_scales"], block_table=inp["block_table"],
                              k_pool=inp["k_pool"], v_pool=inp["v_pool"], k_scales=inp["k_scales"],
                              v_scales=inp["v_scales"])
-        layers.append(dict(inp=inp, summ=summ, newest=newest, tok=tok, nt=nt))
+        mean = torch.empty((w.B, w.Hkv, w.nb, w.D), dtype=torch.float32, device=dev)
+        kvs.kvs_build_summaries_ex(L, kvs.KVS_SUMM_MEAN, inp["k_pool"], inp["k_scales"], inp["block_table"],
+                                   inp["seq_lens"], None, L.max_blocks, mean)
+        layers.append(dict(inp=inp, summ=summ, newest=newest, tok=tok, nt=nt, mean=mean))
         steps.append(st)
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0
@@ -180,6 +183,16 @@ def main(argv=None) -> int:
         d, st = layers[i], steps[i]
         inp = d["inp"]
         kvs.kvs_score_blocks(L, inp["q"], d["summ"], inp["seq_lens"], None, d["tok"], st.scores, None)
+
+    mean_opts = kvs.SelectOpts(summary_kind=kvs.KVS_SUMM_MEAN)
+
+    def run_score_mean(i):
+        d, st = layers[i], steps[i]
+        inp = d["inp"]
+        kvs.kvs_score_blocks(L, inp["q"], d["mean"], inp["seq_lens"], mean_opts, None, st.scores, None)
+        kvs.kvs_select_attn(L, inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"],
+                            inp["block_table"], inp["seq_lens"], st.scores, w.k, 1, st.sel, st.sm_scale, st.out,
+                            st.attn_ws)
 
     def run_select_attn(i):
         d, st = layers[i], steps[i]
@@ -242,6 +255,7 @@ def main(argv=None) -> int:
     # rebuild of the newest block's summary from its K tile instead
     phase = {}
     for name, fn in (("score_blocks", run_score), ("select_attn", run_select_attn),
+                     ("mean_summaries_step", run_score_mean),
                      ("append_select", run_append_select), ("select_topk_only", run_select),
                      ("select_topk_rebuild", run_select_append), ("attention", run_attn)):
         t, _ = timed(capture(fn), args.steps, args.warmup)
@@ -485,21 +499,28 @@ def selection_study(args, w, dev) -> int:
         noise = torch.randn(qs[-1].shape, generator=g, device=dev)
         qs.append(rho * qs[-1] + math.sqrt(1.0 - rho * rho) * noise)
     qs = [x.to(inp["q"].dtype).contiguous() for x in qs]
-    variants = {"plain": (1, False), "ema0.7": (1, True), "window8": (8, False), "window8+ema0.7": (8, True)}
+    variants = {"plain": (1, False), "ema0.7": (1, True), "window8": (8, False), "window8+ema0.7": (8, True),
+                "mean-summaries": (1, False)}
+    mean = torch.empty((w.B, w.Hkv, w.nb, w.D), dtype=torch.float32, device=dev)
+    kvs.kvs_build_summaries_ex(L, kvs.KVS_SUMM_MEAN, inp["k_pool"], inp["k_scales"], inp["block_table"],
+                               inp["seq_lens"], None, L.max_blocks, mean)
     units = w.B * w.Hkv
     kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
     tile = w.S * w.D * kv_elem + (w.S * (w.D // w.quant_group) * 4 if w.quant_group else 0)
     res = {}
     for name, (recent, ema) in variants.items():
         state = torch.full((w.B, w.Hkv, w.nb), float("nan"), dtype=torch.float64, device=dev)
-        opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None)
+        kind = kvs.KVS_SUMM_MEAN if name == "mean-summaries" else kvs.KVS_SUMM_MINMAX
+        opts = kvs.SelectOpts(recent_blocks=recent, use_ema=ema, ema_alpha=0.7, ema_state=state if ema else None,
+                              summary_kind=kind)
+        table = mean if kind == kvs.KVS_SUMM_MEAN else summ
         hs = HotBufferStep(L, w.k, w.k, dev)
         misses = []
         t_sel = t_swap = t_attn = 0.0
         for t, q in enumerate(qs):
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
-            kvs.kvs_select_topk_ex(L, q, summ, inp["seq_lens"], w.k, opts, None, st.sel, None, st.select_ws)
+            kvs.kvs_select_topk_ex(L, q, table, inp["seq_lens"], w.k, opts, None, st.sel, None, st.select_ws)
             ev[1].record()
             hs.swap_in(t, st.sel, *host)
             ev[2].record()

@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 2
+#define KVS_ABI_VERSION 3
 
 typedef enum kvs_status {
   KVS_OK = 0,
@@ -148,6 +148,24 @@ kvs_status kvs_build_summaries(const kvs_layout* layout, const void* k_pool,
                                const float* k_scales, const int32_t* block_table,
                                const int32_t* seq_lens, const int32_t* first_block,
                                int32_t num_rebuild, void* summaries, void* stream);
+
+/* Summary kinds ("KV 稀疏化", §5 names min/max and mean as block summaries). */
+#define KVS_SUMM_MINMAX 0
+#define KVS_SUMM_MEAN   1
+
+/* ------------------------------------------------------------------------
+ * kvs_build_summaries_ex -- kvs_build_summaries for either summary kind
+ *
+ * KVS_SUMM_MINMAX: exactly kvs_build_summaries.  KVS_SUMM_MEAN: per rebuilt
+ * block and channel, mean = fp32(sum / n) of K over the block's n valid
+ * tokens, the sum in fp64 over ascending token positions and the division
+ * in fp64 (fp8 elements dequantised first); summaries is
+ * [B][Hkv][MB][D] fp32.  Other arguments and errors as kvs_build_summaries.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_build_summaries_ex(const kvs_layout* layout, int32_t summary_kind, const void* k_pool,
+                                  const float* k_scales, const int32_t* block_table,
+                                  const int32_t* seq_lens, const int32_t* first_block,
+                                  int32_t num_rebuild, void* summaries, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_select_topk -- query-aware block scores and top-k selection
@@ -286,7 +304,14 @@ kvs_status kvs_append_token(const kvs_layout* layout, const kvs_append_args* app
  *               [B][Hkv][MB] fp64 in/out (NaN = no history; reset a row when
  *               its sequence slot is reused); entries j >= nb(b) are left
  *               untouched.  0 <= alpha <= 1.
- *  opts = NULL  R = 1, no smoothing.
+ *  opts->summary_kind  KVS_SUMM_MINMAX: blocks are scored by the box bound
+ *               W on min/max summaries; KVS_SUMM_MEAN: by the mean score
+ *               max over the group's heads of sum_c q_c * mean_c (fp64,
+ *               ascending c) on mean summaries (kvs_build_summaries_ex).  With
+ *               mean summaries an append writes the token and then rebuilds
+ *               its block's mean from the pool (a launch each), and scoring is
+ *               always the exact path.
+ *  opts = NULL  R = 1, no smoothing, min/max summaries.
  *  append       NULL, or the token append of kvs_append_token (same
  *               arguments), done before the blocks are scored.  Without
  *               bounds_out and smoothing it runs inside the scoring launch,
@@ -304,6 +329,7 @@ typedef struct kvs_select_opts {
   int32_t use_ema;
   double ema_alpha;
   double* ema_state;
+  int32_t summary_kind;  /* KVS_SUMM_MINMAX (the box bound) or KVS_SUMM_MEAN */
 } kvs_select_opts;
 
 kvs_status kvs_select_topk_ex(const kvs_layout* layout, const void* q, void* summaries,

@@ -186,6 +186,16 @@ kvs_status kvs_build_summaries(const kvs_layout* L, const void* k_pool, const fl
                                const int32_t* block_table, const int32_t* seq_lens,
                                const int32_t* first_block, int32_t num_rebuild, void* summaries,
                                void* stream) {
+  return kvs_build_summaries_ex(L, KVS_SUMM_MINMAX, k_pool, k_scales, block_table, seq_lens, first_block,
+                                num_rebuild, summaries, stream);
+}
+
+kvs_status kvs_build_summaries_ex(const kvs_layout* L, int32_t summary_kind, const void* k_pool,
+                                  const float* k_scales, const int32_t* block_table, const int32_t* seq_lens,
+                                  const int32_t* first_block, int32_t num_rebuild, void* summaries,
+                                  void* stream) {
+  if (summary_kind != KVS_SUMM_MINMAX && summary_kind != KVS_SUMM_MEAN)
+    return fail(KVS_ERR_INVALID_ARG, "unknown summary_kind");
   kvs_status st = check_layout(L, false);
   if (st != KVS_OK) return st;
   if (!k_pool || !block_table || !seq_lens || !summaries)
@@ -213,6 +223,7 @@ kvs_status kvs_build_summaries(const kvs_layout* L, const void* k_pool, const fl
   a.P = L->num_pages;
   a.qg = L->quant_group;
   a.num_rebuild = num_rebuild;
+  a.mean = summary_kind == KVS_SUMM_MEAN ? 1 : 0;
   return hip_status(kvs::launch_summaries(a, kind_of(L->kv_dtype), static_cast<hipStream_t>(stream)),
                     "summaries launch");
 }
@@ -282,7 +293,20 @@ struct SelectOpts {
   bool ema = false;
   double alpha = 1.0;
   double* state = nullptr;
+  int kind = KVS_SUMM_MINMAX;
 };
+
+SelectOpts opts_of(const kvs_select_opts* opts) {
+  SelectOpts o;
+  if (opts) {
+    o.recent = opts->recent_blocks;
+    o.ema = opts->use_ema != 0;
+    o.alpha = opts->ema_alpha;
+    o.state = opts->ema_state;
+    o.kind = opts->summary_kind;
+  }
+  return o;
+}
 
 // kvs_select_topk's checks and launches.  With `app`, each sequence's newest
 // block summary is also rebuilt from K; with `tok`, the decode token is
@@ -309,6 +333,10 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   }
   if (opt.ema && (!opt.state || !aligned(opt.state, 8) || !(opt.alpha >= 0.0 && opt.alpha <= 1.0)))
     return fail(KVS_ERR_INVALID_ARG, "smoothing needs an 8-byte aligned ema_state and 0 <= ema_alpha <= 1");
+  if (opt.kind != KVS_SUMM_MINMAX && opt.kind != KVS_SUMM_MEAN)
+    return fail(KVS_ERR_INVALID_ARG, "unknown summary_kind");
+  const bool mean = opt.kind == KVS_SUMM_MEAN;
+  if (mean && app) return fail(KVS_ERR_UNSUPPORTED, "the newest-block rebuild call keeps min/max summaries");
   if (!aligned(summaries, 16) || (workspace && !aligned(workspace, 16)) || (bounds_out && !aligned(bounds_out, 8)))
     return fail(KVS_ERR_INVALID_ARG, "summaries/workspace must be 16-byte aligned, bounds_out 8-byte");
   kvs::AppendArgs tok{};
@@ -317,7 +345,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   if ((st = error_word(&err)) != KVS_OK) return st;
   tok.err = err;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int summ_kind = L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32;
+  const int summ_kind = mean ? kvs::K_MEAN : (L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32);
   const int G = L->num_q_heads / L->num_kv_heads;
   kvs::SummArgs ap{};
   int fuse = 0;  // the scoring launch's extra-workgroup role (BoundArgs::append)
@@ -329,6 +357,31 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
       hipError_t e = kvs::launch_summaries(ap, kind_of(L->kv_dtype), s);
       if (e != hipSuccess) return hip_status(e, "summaries launch");
     }
+  } else if (tok_in && mean) {
+    // a mean cannot be updated in place exactly: write the token, then
+    // rebuild its block's mean from the pool
+    tok.skip_summary = 1;
+    hipError_t e = kvs::launch_append(tok, kind_of(L->kv_dtype), s);
+    if (e != hipSuccess) return hip_status(e, "append launch");
+    kvs::SummArgs ms{};
+    ms.k_pool = tok.k_pool;
+    ms.k_scales = tok.k_scales;
+    ms.block_table = tok.block_table;
+    ms.seq_lens = seq_lens;
+    ms.out = const_cast<void*>(summaries);
+    ms.err = err;
+    ms.B = L->num_seqs;
+    ms.Hkv = L->num_kv_heads;
+    ms.D = L->head_dim;
+    ms.S = L->block_size;
+    ms.MB = L->max_blocks;
+    ms.P = L->num_pages;
+    ms.qg = L->quant_group;
+    ms.num_rebuild = 1;
+    ms.newest = 1;
+    ms.mean = 1;
+    e = kvs::launch_summaries(ms, kind_of(L->kv_dtype), s);
+    if (e != hipSuccess) return hip_status(e, "summaries launch");
   } else if (tok_in) {
     // fused only where the newest block's racing score is never used: it
     // would reach bounds_out, and through smoothing the next steps
@@ -345,7 +398,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   // of thousands of blocks (8 x 4 x 512: 15.0 vs 16.5 us; 256 x 4 x 512:
   // 108 vs 75 us).
   const long long blocks = (long long)L->num_seqs * L->num_kv_heads * L->max_blocks;
-  if (!scores_out && !bounds_out && !opt.ema && blocks >= kSelectMfmaMinBlocks &&
+  if (!scores_out && !bounds_out && !opt.ema && !mean && blocks >= kSelectMfmaMinBlocks &&
       kvs::select_mfma_supported(kind_of(L->q_dtype), summ_kind, L->head_dim, L->max_blocks, G)) {
     kvs::SelMfmaArgs ma{};
     ma.q = q;
@@ -419,15 +472,8 @@ kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summa
 kvs_status kvs_select_topk_ex(const kvs_layout* L, const void* q, void* summaries, const int32_t* seq_lens,
                               int32_t k, const kvs_select_opts* opts, const kvs_append_args* append, int32_t* sel,
                               double* bounds_out, void* workspace, size_t workspace_bytes, void* stream) {
-  SelectOpts o;
-  if (opts) {
-    o.recent = opts->recent_blocks;
-    o.ema = opts->use_ema != 0;
-    o.alpha = opts->ema_alpha;
-    o.state = opts->ema_state;
-  }
-  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr, o,
-                     append);
+  return select_impl(L, q, summaries, seq_lens, k, sel, bounds_out, workspace, workspace_bytes, stream, nullptr,
+                     opts_of(opts), append);
 }
 
 kvs_status kvs_append_token(const kvs_layout* L, const kvs_append_args* append, const int32_t* seq_lens,
@@ -495,12 +541,8 @@ kvs_status kvs_score_blocks(const kvs_layout* L, const void* q, void* summaries,
                             const kvs_select_opts* opts, const kvs_append_args* append, double* scores,
                             double* bounds_out, void* stream) {
   if (!scores) return fail(KVS_ERR_INVALID_ARG, "scores must be non-NULL");
-  SelectOpts o;
-  if (opts) {
-    o.ema = opts->use_ema != 0;
-    o.alpha = opts->ema_alpha;
-    o.state = opts->ema_state;
-  }
+  SelectOpts o = opts_of(opts);
+  o.recent = 1;  // not used here
   return select_impl(L, q, summaries, seq_lens, 0, nullptr, bounds_out, nullptr, 0, stream, nullptr, o, append,
                      scores);
 }

@@ -63,7 +63,7 @@ __device__ __forceinline__ void append_token_unit(const AppendArgs& a, int b, in
   // the block's stored summary (its tokens before t) is read beside the page
   const long long row = (unit * a.MB + j) * 2 * D;  // min at [0, D), max at [D, 2D)
   float old_mn = 0.0f, old_mx = 0.0f;
-  if (s > 0) {
+  if (s > 0 && !a.skip_summary) {
     if constexpr (KVK == K_BF16) {
       const uint16_t* ps = static_cast<const uint16_t*>(a.summ) + row;
       old_mn = bf16_lo(ps[c]);
@@ -82,6 +82,8 @@ __device__ __forceinline__ void append_token_unit(const AppendArgs& a, int b, in
   if (tid < D) {
     static_cast<E*>(a.k_pool)[(tile * S + s) * D + c] = kv;
     static_cast<E*>(a.v_pool)[((tile * (S / T) + s / T) * D + c) * T + s % T] = vv;
+  }
+  if (tid < D && !a.skip_summary) {
     float x;  // the K element's value, as the summaries and attention read it
     if constexpr (KVK == K_F32) {
       x = __uint_as_float(kv);

@@ -8,7 +8,7 @@
 namespace kvs {
 
 // element kinds of q / K / V / summaries
-enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2 };
+enum Kind : int { K_F32 = 0, K_BF16 = 1, K_FP8 = 2, K_MEAN = 3 /* fp32 mean summaries */ };
 
 constexpr int kWave = 64;
 
@@ -124,6 +124,7 @@ struct SummArgs {
   unsigned int* err;
   int32_t B, Hkv, D, S, MB, P, qg, num_rebuild;
   int32_t newest;  // 1: rebuild block nb(b)-1 of every sequence (first_block unused)
+  int32_t mean;    // 1: the fp32 mean table [B][Hkv][MB][D] instead of min/max
 };
 
 // One decode token per sequence written into its page, its block's summary
@@ -146,6 +147,7 @@ struct AppendArgs {
   float* host_vs;
   unsigned int* err;
   int32_t B, Hkv, D, S, MB, P, qg;
+  int32_t skip_summary;  // 1: K/V (and the seal) only; the caller rebuilds the summary
 };
 
 struct BoundArgs {

@@ -36,7 +36,7 @@ constexpr int kBoundBlocks = 64;  // blocks per bounds workgroup (lane = block)
 // (4 with fp32 summaries, whose chunk fills half the LDS)
 template <int G, int SK>
 constexpr int bound_waves() {
-  return G >= 8 && SK == K_BF16 ? 8 : 4;
+  return G >= 8 && (SK == K_BF16 || SK == K_MEAN) ? 8 : 4;
 }
 
 // Score smoothing across decode steps ("SparDA…" §6.1): the score a block is
@@ -62,8 +62,8 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   constexpr int NWB = bound_waves<G, SK>();
   constexpr int NT = 64 * NWB;
   constexpr int NB = kBoundBlocks;
-  constexpr int EB = elem_bytes<SK>();
-  constexpr int ROWB = 2 * D * EB;           // bytes of one block's summary
+  constexpr int EB = SK == K_BF16 ? 2 : 4;   // summary element bytes
+  constexpr int ROWB = (SK == K_MEAN ? 1 : 2) * D * EB;  // bytes of one block's summary
   constexpr int ROWP = ROWB + 16;            // padded LDS row (bank spread)
   constexpr int NV = NB * ROWB / 16;         // 16-byte vectors of the chunk
   constexpr int NPT = NV / NT;
@@ -93,7 +93,7 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
 
   // stage the chunk's summaries: every load issued before any use, and not
   // waiting for seq_lens (blocks past nb are read but never used)
-  const char* src = static_cast<const char*>(a.summ) + ((((long long)b * a.Hkv + g) * a.MB + j0) * 2 * D) * EB;
+  const char* src = static_cast<const char*>(a.summ) + (((long long)b * a.Hkv + g) * a.MB + j0) * ROWB;
   u32x4 raw[NPT];
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   // the decode token is appended by the unit's first workgroup while its
   // chunk loads are in flight (a workgroup of its own would leave some
   // compute units with two scoring workgroups)
-  if (a.append == 2 && blockIdx.x == 0) {
+  if (SK != K_MEAN && a.append == 2 && blockIdx.x == 0) {  // (mean tables are rebuilt instead)
     if constexpr (SK == K_BF16)
       append_token_unit<K_BF16, D, NT>(a.tok, b, g);
     else if (a.app_kv == K_FP8)
@@ -161,11 +161,17 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
 #pragma unroll 1
     for (int c0 = 0; c0 < D; c0 += VEC) {
       const u32x4 vmn = *reinterpret_cast<const u32x4*>(pmn + c0 * EB);
-      const u32x4 vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
+      u32x4 vmx = vmn;
+      if constexpr (SK != K_MEAN) vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
 #pragma unroll
       for (int i = 0; i < HPW; ++i) {
         const int h = wave + NWB * i;
         if (h >= G) break;
+        if constexpr (SK == K_MEAN) {  // score q.mean: the row is the mean itself
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i] = __builtin_fma(qd[h][c0 + e], (double)__uint_as_float(vmn[e]), acc[i]);
+          continue;
+        }
         const u32x4 m = *reinterpret_cast<const u32x4*>(&qm[h][c0 * EB / 4]);
         const u32x4 x = (vmx & m) | (vmn & ~m);
         float xf[VEC];
@@ -254,6 +260,8 @@ hipError_t launch_bounds(const BoundArgs& a, int q_kind, int summ_kind, hipStrea
   const int G = a.Hq / a.Hkv;
   if (q_kind == K_F32 && summ_kind == K_F32) return launch_bounds_d<K_F32, K_F32>(a, G, s);
   if (q_kind == K_BF16 && summ_kind == K_BF16) return launch_bounds_d<K_BF16, K_BF16>(a, G, s);
+  if (summ_kind == K_MEAN)
+    return q_kind == K_F32 ? launch_bounds_d<K_F32, K_MEAN>(a, G, s) : launch_bounds_d<K_BF16, K_MEAN>(a, G, s);
   return launch_bounds_d<K_BF16, K_F32>(a, G, s);
 }
 

@@ -64,6 +64,15 @@ class Layout:
     def summary_dtype(self) -> torch.dtype:
         return torch.bfloat16 if self.kv_dtype == KVS_BF16 else torch.float32
 
+    def summary_dtype_of(self, kind: int) -> torch.dtype:
+        return torch.float32 if kind == KVS_SUMM_MEAN else self.summary_dtype
+
+    def summary_numel(self, kind: int = 0) -> int:
+        """Elements of the summary table: [B][Hkv][MB][2][D] (min/max) or
+        [B][Hkv][MB][D] (mean)."""
+        n = self.num_seqs * self.num_kv_heads * self.max_blocks * self.head_dim
+        return n if kind == KVS_SUMM_MEAN else 2 * n
+
 
 class _CAppendArgs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
@@ -73,7 +82,11 @@ class _CAppendArgs(ctypes.Structure):
 
 class _CSelectOpts(ctypes.Structure):
     _fields_ = [("recent_blocks", ctypes.c_int32), ("use_ema", ctypes.c_int32),
-                ("ema_alpha", ctypes.c_double), ("ema_state", ctypes.c_void_p)]
+                ("ema_alpha", ctypes.c_double), ("ema_state", ctypes.c_void_p),
+                ("summary_kind", ctypes.c_int32)]
+
+
+KVS_SUMM_MINMAX, KVS_SUMM_MEAN = 0, 1
 
 
 @dataclass
@@ -97,11 +110,12 @@ class AppendArgs:
 
 @dataclass
 class SelectOpts:
-    """kvs_select_opts: recent window and score smoothing."""
+    """kvs_select_opts: recent window, score smoothing, summary kind."""
     recent_blocks: int = 1
     use_ema: bool = False
     ema_alpha: float = 0.7
     ema_state: torch.Tensor | None = None
+    summary_kind: int = 0  # KVS_SUMM_MINMAX or KVS_SUMM_MEAN
 
 
 def _load():
@@ -113,6 +127,7 @@ def _load():
     LP = ctypes.POINTER(_CLayout)
     sigs = {
         "kvs_build_summaries": (i32, [LP, P, P, P, P, P, i32, P, P]),
+        "kvs_build_summaries_ex": (i32, [LP, i32, P, P, P, P, P, i32, P, P]),
         "kvs_select_topk": (i32, [LP, P, P, P, i32, P, P, P, sz, P]),
         "kvs_select_topk_append": (i32, [LP, P, P, P, P, P, P, i32, P, P, P, sz, P]),
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
@@ -140,6 +155,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
             "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
+            "kvs_build_summaries_ex",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
 
@@ -203,6 +219,23 @@ def kvs_build_summaries(layout: Layout, k_pool, k_scales, block_table, seq_lens,
         int(num_rebuild),
         _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
         _stream(stream)), "kvs_build_summaries")
+
+
+def kvs_build_summaries_ex(layout: Layout, summary_kind: int, k_pool, k_scales, block_table, seq_lens,
+                           first_block, num_rebuild: int, summaries, stream=None) -> None:
+    L = layout
+    tile = L.num_kv_heads * L.block_size * L.head_dim
+    qg = L.quant_group
+    _check(_lib.kvs_build_summaries_ex(
+        ctypes.byref(L.c()), int(summary_kind),
+        _ptr(k_pool, "k_pool", _pool_dtype(L), L.num_pages * tile),
+        _ptr(k_scales, "k_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(block_table, "block_table", torch.int32, L.num_seqs * L.max_blocks),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        _ptr(first_block, "first_block", torch.int32, L.num_seqs),
+        int(num_rebuild),
+        _ptr(summaries, "summaries", L.summary_dtype_of(summary_kind), L.summary_numel(summary_kind)),
+        _stream(stream)), "kvs_build_summaries_ex")
 
 
 def kvs_select_topk(layout: Layout, q, summaries, seq_lens, k: int, sel, bounds_out, workspace,
@@ -279,17 +312,13 @@ def kvs_append_token(layout: Layout, append: AppendArgs, seq_lens, summaries, st
 def kvs_select_topk_ex(layout: Layout, q, summaries, seq_lens, k: int, opts: SelectOpts | None,
                        append: AppendArgs | None, sel, bounds_out, workspace, stream=None) -> None:
     L = layout
-    co = None
-    if opts is not None:
-        co = _CSelectOpts(int(opts.recent_blocks), 1 if opts.use_ema else 0, float(opts.ema_alpha),
-                          _ptr(opts.ema_state, "ema_state", torch.float64,
-                               L.num_seqs * L.num_kv_heads * L.max_blocks))
+    co = _opts_struct(L, opts)
     ca = _append_struct(L, append) if append is not None else None
     ws = _ptr(workspace, "workspace", torch.uint8)
     _check(_lib.kvs_select_topk_ex(
         ctypes.byref(L.c()),
         _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
-        _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
+        _ptr(summaries, "summaries", L.summary_dtype_of(_kind(opts)), L.summary_numel(_kind(opts))),
         _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
         int(k),
         ctypes.byref(co) if co is not None else None,
@@ -304,7 +333,12 @@ def _opts_struct(L: Layout, opts: SelectOpts | None):
     if opts is None:
         return None
     return _CSelectOpts(int(opts.recent_blocks), 1 if opts.use_ema else 0, float(opts.ema_alpha),
-                        _ptr(opts.ema_state, "ema_state", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks))
+                        _ptr(opts.ema_state, "ema_state", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
+                        int(opts.summary_kind))
+
+
+def _kind(opts: SelectOpts | None) -> int:
+    return 0 if opts is None else int(opts.summary_kind)
 
 
 def kvs_score_blocks(layout: Layout, q, summaries, seq_lens, opts: SelectOpts | None, append: AppendArgs | None,
@@ -316,7 +350,7 @@ def kvs_score_blocks(layout: Layout, q, summaries, seq_lens, opts: SelectOpts | 
     _check(_lib.kvs_score_blocks(
         ctypes.byref(L.c()),
         _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
-        _ptr(summaries, "summaries", L.summary_dtype, n * 2 * L.head_dim),
+        _ptr(summaries, "summaries", L.summary_dtype_of(_kind(opts)), L.summary_numel(_kind(opts))),
         _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
         ctypes.byref(co) if co is not None else None,
         ctypes.byref(ca) if ca is not None else None,

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(kvs):
 
 
 def test_abi_version_and_status_strings(kvs):
-    assert kvs.kvs_abi_version() == 2
+    assert kvs.kvs_abi_version() == 3
     for st in range(5):
         assert kvs.kvs_status_string(st).startswith("KVS_")
     assert "unknown" in kvs.kvs_status_string(99)
@@ -160,8 +160,8 @@ def test_append_and_select_ex_argument_checks(kvs):
     fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
     assert lib.kvs_append_token(ctypes.byref(fp8.c()), ctypes.byref(ok), FAKE, FAKE, None) == 1  # no scales
 
-    def sel_ex(k, recent=1, ema=0, alpha=0.7, state=FAKE.value, app=None):
-        o = kvs._CSelectOpts(recent, ema, alpha, state)
+    def sel_ex(k, recent=1, ema=0, alpha=0.7, state=FAKE.value, app=None, kind=0):
+        o = kvs._CSelectOpts(recent, ema, alpha, state, kind)
         return lib.kvs_select_topk_ex(c, FAKE, FAKE, FAKE, k, ctypes.byref(o),
                                       ctypes.byref(app) if app is not None else None,
                                       FAKE, None, FAKE, 1 << 20, None)
@@ -171,3 +171,5 @@ def test_append_and_select_ex_argument_checks(kvs):
     assert sel_ex(4, ema=1, state=None) == kvs.KVS_ERR_INVALID_ARG
     assert sel_ex(4, ema=1, state=0x100004) == kvs.KVS_ERR_INVALID_ARG  # misaligned state
     assert sel_ex(4, app=_append_args(kvs, v_new=None)) == kvs.KVS_ERR_INVALID_ARG
+    assert sel_ex(4, kind=2) == kvs.KVS_ERR_INVALID_ARG
+    assert lib.kvs_build_summaries_ex(c, 5, FAKE, None, FAKE, FAKE, None, 1, FAKE, None) == kvs.KVS_ERR_INVALID_ARG

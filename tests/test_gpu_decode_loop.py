@@ -403,3 +403,86 @@ def test_prefetch_pipeline_matches_sequential_hot_steps(env):
     for a, b in zip(seq, pip):
         for n in ("page_table", "slot_owner", "slot_stamp", "hot_k", "hot_v"):
             assert torch.equal(getattr(a, n), getattr(b, n)), f"{n} differs"
+
+
+MEAN_CASES = [
+    # (name, workload, overrides, lens0, k, recent, append, bounds)
+    ("bf16-bounds", "llama8b", {"B": 3, "L": 64 * 40, "layers": 1}, [64 * 30 - 1, 64 * 7, 5], 12, 1, False, True),
+    ("bf16-append-window", "llama8b", {"B": 3, "L": 64 * 40, "layers": 1}, [64 * 30 - 1, 64 * 7 + 63, 5], 12, 3,
+     True, False),
+    ("bf16-s32-d64-g4-append", "llama8b", {"B": 2, "L": 32 * 50, "S": 32, "D": 64, "Hq": 16, "layers": 1},
+     [32 * 40 + 3, 32 * 11 - 1], 10, 2, True, True),
+    ("fp8-append", "longfp8", {"B": 2, "L": 64 * 40}, [64 * 30 - 1, 64 * 7], 10, 2, True, False),
+    ("f32-s16-append", "tiny", {"B": 2, "L": 16 * 40}, [16 * 30 - 1, 16 * 7], 10, 1, True, True),
+]
+
+
+@pytest.mark.parametrize("case", MEAN_CASES, ids=[c[0] for c in MEAN_CASES])
+def test_mean_summaries_scores_and_selection(env, case):
+    """Mean summaries (kvs_build_summaries_ex), blocks ranked by q.mean
+    (kvs_select_topk_ex and kvs_score_blocks + kvs_select_attn with
+    summary_kind = mean), with and without the token append: the mean table,
+    the scores and the selections equal the oracle's bit for bit, the
+    attention is within the bars."""
+    from test_gpu_parity import check_attn
+    name, base, over, lens0, k, recent, with_append, with_bounds = case
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    c = Cache(env, w, lens0, seed=21)
+    p, L = c.p, c.p.L
+    print(f"[mean {name}] units {L.num_seqs * L.num_kv_heads} max_blocks {L.max_blocks} k={k} recent={recent} "
+          f"append={with_append} bounds={with_bounds}", flush=True)
+    mean = torch.full((L.num_seqs, L.num_kv_heads, L.max_blocks, L.head_dim), float("nan"), device=env.dev)
+    kvs.kvs_build_summaries_ex(L, kvs.KVS_SUMM_MEAN, p.inp["k_pool"], p.inp["k_scales"], p.inp["block_table"],
+                               p.inp["seq_lens"], None, L.max_blocks, mean)
+    no_device_errors(env)
+    opts = kvs.SelectOpts(recent_blocks=recent, summary_kind=kvs.KVS_SUMM_MEAN)
+    sws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    aws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    scores = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=env.dev)
+    lens = np.asarray(lens0, np.int64)
+    for step in range(3):
+        tok = None
+        if with_append:
+            lens = lens + 1
+            c.set_lens(lens)
+            tok = c.new_token()
+        o_mean = orc.summaries_mean(p.OL, c.o["k_pool"] if with_append else p.h["k_pool"],
+                                    c.o["k_scales"] if with_append else p.h["k_scales"], p.h["table"], p.h["lens"])
+        sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+        W = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64,
+                        device=env.dev) if with_bounds else None
+        kvs.kvs_select_topk_ex(L, p.inp["q"], mean, p.inp["seq_lens"], k, opts,
+                               c.args(tok) if tok is not None else None, sel, W, sws)
+        no_device_errors(env)
+        if tok is not None:
+            c.oracle_append(tok, lens.astype(np.int32))
+            o_mean = orc.summaries_mean(p.OL, c.o["k_pool"], c.o["k_scales"], p.h["table"], p.h["lens"])
+            for n in ("k_pool", "v_pool"):
+                assert np.array_equal(np_pool(p.inp[n]).view(np.uint8), c.o[n].view(np.uint8)), f"{n} differs"
+        gm = mean.cpu().numpy()
+        for b, nb in enumerate(p.nbs):
+            assert np.array_equal(gm[b, :, :nb], o_mean[b, :, :nb]), f"step {step}: mean table differs"
+        o_W = orc.mean_scores(p.OL, p.h["q"], o_mean, p.h["lens"])
+        if with_bounds:
+            gW = W.cpu().numpy()
+            for b, nb in enumerate(p.nbs):
+                assert np.array_equal(gW[b, :, :nb], o_W[b, :, :nb]), f"step {step}: mean scores differ"
+        o_sel = orc.select_window(p.OL, o_W, p.h["lens"], k, recent)
+        assert np.array_equal(sel.cpu().numpy(), o_sel), f"step {step}: selection differs"
+        # the same scores and selection through kvs_score_blocks + kvs_select_attn
+        kvs.kvs_score_blocks(L, p.inp["q"], mean, p.inp["seq_lens"], opts, None, scores, None)
+        out = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=env.dev)
+        sel2 = torch.full_like(sel, -7)
+        kvs.kvs_select_attn(L, p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
+                            p.inp["block_table"], p.inp["seq_lens"], scores, k, recent, sel2, p.sm_scale, out, aws)
+        no_device_errors(env)
+        gs = scores.cpu().numpy()
+        for b, nb in enumerate(p.nbs):
+            assert np.array_equal(gs[b, :, :nb], o_W[b, :, :nb]), f"step {step}: kvs_score_blocks differs"
+        assert torch.equal(sel2, sel), f"step {step}: kvs_select_attn picks other blocks"
+        pools = c.o if with_append else p.h
+        o_out = orc.sparse_attn(p.OL, p.h["q"], pools["k_pool"], pools["v_pool"], pools["k_scales"],
+                                pools["v_scales"], p.h["table"], p.h["lens"], o_sel, p.sm_scale)
+        err, rel = check_attn(out, o_out)
+    print(f"[mean {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
