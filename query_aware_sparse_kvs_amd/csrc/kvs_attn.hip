@@ -1038,101 +1038,68 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   }
 }
 
-// Split merge: one 256-thread workgroup per 2 query heads.  Thread t takes
-// 4 output channels of one head and a quarter of the splits; all of its
-// partial loads (m, acc) are issued together, the quarters are summed in LDS.
-constexpr int kMergeHeads = 2;
+// Split merge: one thread per (query head, 4 output channels), 64 threads
+// per workgroup.  Each thread loads, in one round trip, the head's split
+// maxima and normalisers (the same addresses for the head's threads) and its
+// 4 channels of every split's partial, in batches of kMergeBatch splits, and
+// merges them online in registers:
+//   M = max m_i, L = sum l_i 2^(m_i - M), o = sum acc_i 2^(m_i - M) / L.
+// No cross-lane traffic and no barriers.
 constexpr int kMaxSplits = kComputeUnits;  // attn_num_splits never exceeds it
+constexpr int kMergeThreads = 64;
+constexpr int kMergeBatch = 8;
 
 template <int D>
-__global__ __launch_bounds__(256) void merge_kernel(AttnArgs a) {
-  constexpr int C4 = D / 4;                    // float4 chunks per head
-  constexpr int CH = kMergeHeads * C4;         // chunks per workgroup
-  constexpr int SG = 256 / CH;                 // split groups
-  constexpr int BATCH = 8;                     // partial rows in flight per thread
-  __shared__ float4 red[SG][CH];
-  __shared__ float hm[kMergeHeads], hl[kMergeHeads];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const long long h0 = (long long)blockIdx.x * kMergeHeads;  // first head row (b*Hq + h)
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a) {
+  constexpr int C4 = D / 4;  // float4 chunks per head
+  const long long t = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
   const long long nrows = (long long)a.B * a.Hq;
+  if (t >= nrows * C4) return;
+  const long long row = t / C4;
+  const int c = (int)(t % C4) * 4;
   const int ns = a.nsplit;
-  const int ch = tid % CH, sg = tid / CH;
-  const int hh = ch / C4, c = (ch % C4) * 4;
-  const long long row = h0 + hh;
+  const float* pm = a.part_m + row * ns;
+  const float* pl = a.part_l + row * ns;
+  const float* pa = a.part_acc + row * ns * D + c;
+  float M = -__builtin_inff(), Ls = 0.0f;
   float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  const bool live = row < nrows;
-  float4 v[BATCH];
-  float ms[BATCH];
-  auto load_batch = [&](int s0) {
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float mv[kMergeBatch], lv[kMergeBatch];
+    float4 av[kMergeBatch];
 #pragma unroll
-    for (int x = 0; x < BATCH; ++x) {
-      const int s = s0 + x * SG;
-      v[x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      ms[x] = -__builtin_inff();
-      if (live && s < ns) {
-        v[x] = *reinterpret_cast<const float4*>(a.part_acc + (row * ns + s) * D + c);
-        ms[x] = a.part_m[row * ns + s];
+    for (int x = 0; x < kMergeBatch; ++x) {
+      const int s = s0 + x;
+      mv[x] = -__builtin_inff();
+      lv[x] = 0.0f;
+      av[x] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      if (s < ns) {
+        mv[x] = pm[s];
+        lv[x] = pl[s];
+        av[x] = *reinterpret_cast<const float4*>(pa + (long long)s * D);
       }
     }
-  };
-  auto add_batch = [&](float M) {
+    float Mb = M;
 #pragma unroll
-    for (int x = 0; x < BATCH; ++x) {
-      const float w = ms[x] == -__builtin_inff() ? 0.0f : exp2f(ms[x] - M);
-      acc.x += w * v[x].x;
-      acc.y += w * v[x].y;
-      acc.z += w * v[x].z;
-      acc.w += w * v[x].w;
+    for (int x = 0; x < kMergeBatch; ++x) Mb = fmaxf(Mb, mv[x]);
+    if (Mb == -__builtin_inff()) continue;  // nothing valid yet
+    const float sc = M == -__builtin_inff() ? 0.0f : exp2f(M - Mb);
+    Ls *= sc;
+    acc.x *= sc;
+    acc.y *= sc;
+    acc.z *= sc;
+    acc.w *= sc;
+#pragma unroll
+    for (int x = 0; x < kMergeBatch; ++x) {
+      const float wgt = mv[x] == -__builtin_inff() ? 0.0f : exp2f(mv[x] - Mb);
+      Ls += lv[x] * wgt;
+      acc.x += wgt * av[x].x;
+      acc.y += wgt * av[x].y;
+      acc.z += wgt * av[x].z;
+      acc.w += wgt * av[x].w;
     }
-  };
-  // the first batch of partial rows goes out first; the per-head max and
-  // normaliser are computed while it is in flight (one wavefront per head,
-  // m and l of all splits fetched in one round: ns <= kMaxSplits)
-  load_batch(sg);
-  if (wave < kMergeHeads && h0 + wave < nrows) {
-    const float* pm = a.part_m + (h0 + wave) * ns;
-    const float* pl = a.part_l + (h0 + wave) * ns;
-    float mv[kMaxSplits / kWave], lv[kMaxSplits / kWave];
-#pragma unroll
-    for (int x = 0; x < kMaxSplits / kWave; ++x) {
-      const int s = x * kWave + lane;
-      mv[x] = s < ns ? pm[s] : -__builtin_inff();
-      lv[x] = s < ns ? pl[s] : 0.0f;
-    }
-    float M = mv[0];
-#pragma unroll
-    for (int x = 1; x < kMaxSplits / kWave; ++x) M = fmaxf(M, mv[x]);
-    M = wave_max(M);
-    float L = 0.0f;
-#pragma unroll
-    for (int x = 0; x < kMaxSplits / kWave; ++x) L += mv[x] == -__builtin_inff() ? 0.0f : lv[x] * exp2f(mv[x] - M);
-    L = wave_sum(L);
-    if (lane == 0) {
-      hm[wave] = M;
-      hl[wave] = L;
-    }
+    M = Mb;
   }
-  __syncthreads();
-  // every thread meets the same two barriers
-  const float Mh = live ? hm[hh] : 0.0f;
-  add_batch(Mh);
-  for (int s0 = sg + SG * BATCH; s0 < ns; s0 += SG * BATCH) {
-    load_batch(s0);
-    add_batch(Mh);
-  }
-  red[sg][ch] = acc;
-  __syncthreads();
-  if (sg != 0 || !live) return;
-#pragma unroll
-  for (int q = 1; q < SG; ++q) {
-    const float4 o = red[q][ch];
-    acc.x += o.x;
-    acc.y += o.y;
-    acc.z += o.z;
-    acc.w += o.w;
-  }
-  const float M = hm[hh], L = hl[hh];
-  const float inv = (M != -__builtin_inff() && L > 0.0f) ? 1.0f / L : 0.0f;
+  const float inv = (M != -__builtin_inff() && Ls > 0.0f) ? 1.0f / Ls : 0.0f;
   *reinterpret_cast<float4*>(a.out + row * D + c) = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
 }
 
@@ -1237,12 +1204,12 @@ hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s
   else
     e = a.D == 64 ? launch_valu<K_BF16, K_FP8, 64>(a, st) : launch_valu<K_BF16, K_FP8, 128>(a, st);
   if (e != hipSuccess || a.nsplit == 1) return e;
-  const long long rows = (long long)a.B * a.Hq;
-  const dim3 grid((unsigned)((rows + kMergeHeads - 1) / kMergeHeads));
+  const long long threads = (long long)a.B * a.Hq * (a.D / 4);
+  const dim3 grid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads));
   if (a.D == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, st, a);
   return hipGetLastError();
 }
 
