@@ -150,6 +150,10 @@ def main(argv=None) -> int:
         kvs.kvs_select_topk_append(L, inp["q"], inp["k_pool"], inp["k_scales"], inp["block_table"],
                                    inp["seq_lens"], d["summ"], w.k, st.sel, None, st.select_ws)
 
+    # where the library selects on the matrix cores, the separate selection
+    # launch is the cheaper step (the in-attention top-k needs every exact score)
+    matrix_cores = kvs.kvs_select_uses_matrix_cores(L, w.k)
+
     def run_append_select(i):
         d, st = layers[i], steps[i]
         inp = d["inp"]
@@ -174,7 +178,7 @@ def main(argv=None) -> int:
         if args.parts > 1:  # the summary-rebuild chain, cut into concurrent batch slices
             st.run(inp["q"], inp["k_pool"], inp["v_pool"], inp["k_scales"], inp["v_scales"], inp["block_table"],
                    inp["seq_lens"], d["summ"])
-        elif args.separate_topk:
+        elif args.separate_topk or matrix_cores:
             st.run_decode(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
         else:
             st.run_decode_fused(inp["q"], d["tok"], inp["seq_lens"], d["summ"])
@@ -262,7 +266,7 @@ def main(argv=None) -> int:
         phase[name] = t / args.steps
     # the roofline entry is for the step's dominant call: the attention with
     # its own selection (or, with --separate-topk, the attention alone)
-    fused = not args.separate_topk and args.parts == 1
+    fused = not args.separate_topk and not matrix_cores and args.parts == 1
     t_attn = phase["select_attn" if fused else "attention"] * args.steps
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
@@ -298,7 +302,8 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                    "head_dim": w.D, "context": w.L, "block": w.S, "top_k_blocks": w.k,
                    "kv_storage": w.kv_dtype, "q_storage": w.q_dtype, "layer_instances": n_layers,
-                   "graph_replay": True, "concurrent_batch_slices": len(steps[0].slices)},
+                   "graph_replay": True, "concurrent_batch_slices": len(steps[0].slices),
+                   "topk": "inside the attention launch" if fused else "separate launch"},
         "phase_us": {k: round(v * 1e6, 3) for k, v in phase.items()},
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),

@@ -469,6 +469,14 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, i
 size_t kvs_select_workspace_size(const kvs_layout* layout, int32_t k);
 size_t kvs_attn_workspace_size(const kvs_layout* layout, int32_t k);
 
+/* 1 when kvs_select_topk (no bounds_out; kvs_select_topk_ex with min/max
+ * summaries and no smoothing) scores this layout on the matrix cores and
+ * refines only near the threshold; 0 when it computes every block's exact
+ * score, as kvs_score_blocks always does.  With 1 the separate selection
+ * launch is the cheaper way to select; with 0 kvs_select_attn's in-attention
+ * top-k is.  0 also for an invalid layout. */
+int32_t kvs_select_uses_matrix_cores(const kvs_layout* layout, int32_t k);
+
 /* Number of key splits the attention kernel uses for this layout and k
  * (each (sequence, KV head) unit's k blocks are spread over that many
  * workgroups whose partial results are merged); 0 when invalid. */

@@ -287,6 +287,13 @@ kvs_status make_append(const kvs_layout* L, const kvs_append_args* ap, const int
   return KVS_OK;
 }
 
+// Whether the selection scores on the matrix cores (no bounds requested,
+// min/max summaries, no smoothing).
+bool uses_matrix_cores(const kvs_layout* L, long long blocks, int summ_kind, int G) {
+  return blocks >= kSelectMfmaMinBlocks &&
+         kvs::select_mfma_supported(kind_of(L->q_dtype), summ_kind, L->head_dim, L->max_blocks, G);
+}
+
 // Selection options after validation.
 struct SelectOpts {
   int recent = 1;
@@ -398,8 +405,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   // of thousands of blocks (8 x 4 x 512: 15.0 vs 16.5 us; 256 x 4 x 512:
   // 108 vs 75 us).
   const long long blocks = (long long)L->num_seqs * L->num_kv_heads * L->max_blocks;
-  if (!scores_out && !bounds_out && !opt.ema && !mean && blocks >= kSelectMfmaMinBlocks &&
-      kvs::select_mfma_supported(kind_of(L->q_dtype), summ_kind, L->head_dim, L->max_blocks, G)) {
+  if (!scores_out && !bounds_out && !opt.ema && !mean && uses_matrix_cores(L, blocks, summ_kind, G)) {
     kvs::SelMfmaArgs ma{};
     ma.q = q;
     ma.summ = summaries;
@@ -461,6 +467,13 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
 }  // namespace
 
 extern "C" {
+
+int32_t kvs_select_uses_matrix_cores(const kvs_layout* L, int32_t k) {
+  if (check_layout(L, true) != KVS_OK || k < 2 || k > L->max_blocks) return 0;
+  const int summ_kind = L->kv_dtype == KVS_BF16 ? kvs::K_BF16 : kvs::K_F32;
+  const long long blocks = (long long)L->num_seqs * L->num_kv_heads * L->max_blocks;
+  return uses_matrix_cores(L, blocks, summ_kind, L->num_q_heads / L->num_kv_heads) ? 1 : 0;
+}
 
 kvs_status kvs_select_topk(const kvs_layout* L, const void* q, const void* summaries,
                            const int32_t* seq_lens, int32_t k, int32_t* sel, double* bounds_out,

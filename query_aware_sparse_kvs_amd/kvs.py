@@ -141,6 +141,7 @@ def _load():
         "kvs_select_workspace_size": (sz, [LP, i32]),
         "kvs_attn_workspace_size": (sz, [LP, i32]),
         "kvs_attn_num_splits": (i32, [LP, i32]),
+        "kvs_select_uses_matrix_cores": (i32, [LP, i32]),
         "kvs_device_errors": (i32, [ctypes.POINTER(ctypes.c_uint32), i32, P]),
         "kvs_status_string": (ctypes.c_char_p, [i32]),
         "kvs_last_error": (ctypes.c_char_p, []),
@@ -155,7 +156,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
             "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
-            "kvs_build_summaries_ex",
+            "kvs_build_summaries_ex", "kvs_select_uses_matrix_cores",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
 
@@ -448,6 +449,10 @@ def kvs_select_workspace_size(layout: Layout, k: int) -> int:
 
 def kvs_attn_workspace_size(layout: Layout, k: int) -> int:
     return int(_lib.kvs_attn_workspace_size(ctypes.byref(layout.c()), int(k)))
+
+
+def kvs_select_uses_matrix_cores(layout: Layout, k: int) -> bool:
+    return bool(_lib.kvs_select_uses_matrix_cores(ctypes.byref(layout.c()), int(k)))
 
 
 def kvs_attn_num_splits(layout: Layout, k: int) -> int:

@@ -95,6 +95,15 @@ class SparseDecodeStep:
                             self.scores, k, recent, self.sel, self.sm_scale, self.out, self.attn_ws, stream)
         return self.out
 
+    def run_decode_best(self, q, tok: kvs.AppendArgs, seq_lens, summaries, stream=None) -> torch.Tensor:
+        """The decode layer-step by the cheaper route for this layout: the
+        top-k inside the attention launch (run_decode_fused), unless the
+        library scores this layout on the matrix cores, where the separate
+        selection launch is cheaper (run_decode)."""
+        if kvs.kvs_select_uses_matrix_cores(self.layout, self.k):
+            return self.run_decode(q, tok, seq_lens, summaries, stream=stream)
+        return self.run_decode_fused(q, tok, seq_lens, summaries, stream=stream)
+
     def run(self, q, k_pool, v_pool, k_scales, v_scales, block_table, seq_lens, summaries,
             bounds_out=None, stream=None) -> torch.Tensor:
         """summaries: in/out, every block but the newest already summarised.
