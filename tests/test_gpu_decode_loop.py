@@ -486,3 +486,40 @@ def test_mean_summaries_scores_and_selection(env, case):
                                 pools["v_scales"], p.h["table"], p.h["lens"], o_sel, p.sm_scale)
         err, rel = check_attn(out, o_out)
     print(f"[mean {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
+
+
+@pytest.mark.parametrize("base,over", [("llama8b", {"B": 5, "L": 64 * 20, "layers": 1}),
+                                       ("longfp8", {"B": 5, "L": 64 * 20})],
+                         ids=["bf16", "fp8"])
+def test_select_attn_empty_short_and_all_block_sequences(env, base, over):
+    """kvs_select_attn on ragged lengths: an empty sequence (no blocks: all
+    -1, a zero output row), a one-token and a one-block sequence, one whose
+    blocks all fit in k, and a long one; selections equal the oracle's and
+    attention is within the bars."""
+    from test_gpu_parity import check_attn
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    k = 6
+    lens = [0, 1, 64, 64 * 5 + 7, 64 * 20]
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    p = Problem(env, w, seq_lens=lens, max_blocks=w.nb + 1, extra_pages=2)
+    L = p.L
+    print(f"[edge {base}] lens {lens} k={k} splits={kvs.kvs_attn_num_splits(L, k)}", flush=True)
+    summ = p.gpu_summaries()
+    scores = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=env.dev)
+    kvs.kvs_score_blocks(L, p.inp["q"], summ, p.inp["seq_lens"], None, None, scores, None)
+    sel = torch.full((L.num_seqs, L.num_kv_heads, k), -7, dtype=torch.int32, device=env.dev)
+    out = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=env.dev)
+    aws = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    kvs.kvs_select_attn(L, p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
+                        p.inp["block_table"], p.inp["seq_lens"], scores, k, 2, sel, p.sm_scale, out, aws)
+    no_device_errors(env)
+    o_summ = p.or_summaries()
+    W = p.or_bounds(o_summ)
+    gs = scores.cpu().numpy()
+    for b, nb in enumerate(p.nbs):
+        assert np.array_equal(gs[b, :, :nb], W[b, :, :nb])
+        assert np.isneginf(gs[b, :, nb:]).all()
+    o_sel = orc.select_window(p.OL, W, p.h["lens"], k, 2)
+    assert np.array_equal(sel.cpu().numpy(), o_sel)
+    assert (sel[0] == -1).all() and (out[0] == 0).all()
+    check_attn(out, p.or_attn(o_sel))
