@@ -253,6 +253,19 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
+    # distribution: every layer-step graph replayed alone between two events
+    # (the sweep above is the throughput figure; these include one event
+    # pair per step)
+    single = step_graphs[1]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i, (e0, e1) in enumerate(evs):
+        e0.record()
+        single[i % n_layers].replay()
+        e1.record()
+    torch.cuda.synchronize()
+    per = np.sort(np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
+    pct = {f"p{q}": round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)}
     # per-phase graphs: the dominant kernel (attention) for the roofline entry,
     # the token append with the selection as the step runs it, the selection
     # alone (the append's cost is the difference), and the selection with a
@@ -305,6 +318,7 @@ def main(argv=None) -> int:
                    "graph_replay": True, "concurrent_batch_slices": len(steps[0].slices),
                    "topk": "inside the attention launch" if fused else "separate launch"},
         "phase_us": {k: round(v * 1e6, 3) for k, v in phase.items()},
+        "step_us_percentiles": pct,
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
