@@ -89,7 +89,7 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-steps", type=int, default=6, help="layer-steps in the CPU oracle sample (about 2 s each)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               "multi-GPU path: (sequence, KV head) units are independent, so several GPUs would "
               "each run this same step on their share of the sequences.", file=sys.stderr)
         return 2
