@@ -90,6 +90,9 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j0 = blockIdx.x * NB;
   const int nmem = min(NB, a.MB - j0);  // blocks of this chunk inside the array
+  // the sequence length as a scalar load (no kernel writes it), in flight
+  // beside the vector loads below instead of queued behind them
+  int len = *(const __attribute__((address_space(4))) int32_t*)(a.seq_lens + b);
 
   // stage the chunk's summaries: every load issued before any use, and not
   // waiting for seq_lens (blocks past nb are read but never used)
@@ -123,7 +126,6 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     else
       append_token_unit<K_F32, D, NT>(a.tok, b, g);
   }
-  int len = a.seq_lens[b];
   const int cap = a.MB * a.S;
   if (len < 0 || len > cap) {
     if (tid == 0 && blockIdx.x == 0 && g == 0) raise_flag(a.err, 0x1u);

@@ -105,6 +105,8 @@ def test_decode_step_with_append_graph_replays_match_eager(orc, route):
         torch.cuda.synchronize()
         assert torch.equal(st.sel, eager_sel), f"replay {rep}: selection differs"
         assert torch.equal(st.out, eager_out), f"replay {rep}: output differs"
-        assert torch.equal(summ, eager_summ), f"replay {rep}: summaries changed"
+        # bit patterns: blocks past a sequence's end hold whatever the
+        # allocation held, NaN patterns included
+        assert torch.equal(summ.view(torch.int16), eager_summ.view(torch.int16)), f"replay {rep}: summaries changed"
         del junk
     assert kvs.kvs_device_errors() == 0
