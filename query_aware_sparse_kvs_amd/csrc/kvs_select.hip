@@ -3,8 +3,8 @@
 // summaries, keep the top-k; the sink block and the newest block are always
 // kept, same page §2 and "SparDA：把KV選擇提前一層…" §4.2).
 //
-// bounds_kernel: a workgroup of 4 wavefronts (8 for bf16 summaries and
-// groups of 8 or more query heads, one per head) stages 64 consecutive blocks' summaries in LDS
+// bounds_kernel: a workgroup of 4 wavefronts (8 for groups of 8 or more
+// query heads, one per head) stages 64 consecutive blocks' summaries in LDS
 // with coalesced 16-byte loads; lane = block, wavefront w takes query heads
 // w, w+NW, ...  The block score is
 // U = sum_c max(q_c*mn_c, q_c*mx_c); since mx_c >= mn_c the larger product is
@@ -32,11 +32,13 @@ namespace {
 
 constexpr int kBoundBlocks = 64;  // blocks per bounds workgroup (lane = block)
 
-// wavefronts per bounds workgroup: one per query head of the group, 4 to 8
-// (4 with fp32 summaries, whose chunk fills half the LDS)
+// wavefronts per bounds workgroup: one per query head of the group, 4 to 8.
+// With fp32 summaries the 64-block chunk takes about 77 KB of LDS, so two
+// workgroups (16 wavefronts) still share a compute unit; more wavefronts per
+// workgroup hide more of the dependent fp64 chain's latency.
 template <int G, int SK>
 constexpr int bound_waves() {
-  return G >= 8 && (SK == K_BF16 || SK == K_MEAN) ? 8 : 4;
+  return G >= 8 ? 8 : 4;
 }
 
 // Score smoothing across decode steps ("SparDA…" §6.1): the score a block is
