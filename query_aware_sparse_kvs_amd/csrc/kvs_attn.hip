@@ -40,6 +40,8 @@
 //   issued before any of its arithmetic.
 // Roofline: HBM-bound gather of 2*S*D*elem bytes (+ fp8 scales) per
 // selected block.
+#include <type_traits>
+
 #include "kvs_internal.h"
 #include "kvs_topk.h"
 
@@ -553,6 +555,37 @@ __device__ __forceinline__ void load_page_v8(const uint8_t* vt, const float* vst
   }
 }
 
+// K of one page for quantisation groups of 32 channels or more: the codes as
+// in PageK8, and this lane's share of the page's K scales [S][groups] (as
+// PageV8 holds the V scales), staged in LDS before the score product.
+template <int D, int S>
+struct PageK8G {
+  u32x2 k[S / 32][2][D / 32];
+  float ks[S * 8 / kWave];
+};
+template <int D, int S>
+__device__ __forceinline__ void load_page_k8g(const uint8_t* kt, const float* kst, int groups, int r, int j4,
+                                              int lane, PageK8G<D, S>& K) {
+#pragma unroll
+  for (int h = 0; h < S / 32; ++h)
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      const int row = h * 32 + 8 * (r >> 2) + 4 * tg + (r & 3);  // tau(tg, r)
+#pragma unroll
+      for (int cs = 0; cs < D / 32; ++cs)
+        K.k[h][tg][cs] = *reinterpret_cast<const u32x2*>(kt + row * D + cs * 32 + 8 * j4);
+    }
+#pragma unroll
+  for (int y = 0; y < S * 8 / kWave; ++y) {
+    const int x = y * kWave + lane;
+    K.ks[y] = x < S * groups ? kst[x] : 0.0f;
+  }
+}
+
+template <int D, int S>
+__device__ __forceinline__ void page_softmax8(const float (*s)[2][4], float tmax, float& m_run, float& l_run,
+                                              f32x4_t* o, float (*pf)[8]);
+
 // Scores of one page.  K = fp32(decode(code) * scale) is split into two bf16
 // (hi + lo) for the matrix product, so the scores keep ~16 bits of K.
 // Returns the probabilities of this lane's 8 tokens per sub-tile (tokens
@@ -560,7 +593,7 @@ __device__ __forceinline__ void load_page_v8(const uint8_t* vt, const float* vst
 template <int D, int S>
 __device__ __forceinline__ void page_scores8(const PageK8<D, S>& K, const bf16x8_t* qf, float q_scale, int ntok,
                                              int j4, float& m_run, float& l_run, f32x4_t* o, float (*pf)[8]) {
-  constexpr int NSUB = S / 32, CS = D / 32, CT = D / 16;
+  constexpr int NSUB = S / 32, CS = D / 32;
   float s[NSUB][2][4];
   float tmax = -__builtin_inff();
 #pragma unroll
@@ -587,6 +620,17 @@ __device__ __forceinline__ void page_scores8(const PageK8<D, S>& K, const bf16x8
         tmax = fmaxf(tmax, v);
       }
     }
+  page_softmax8<D, S>(s, tmax, m_run, l_run, o, pf);
+}
+
+// Online-softmax update of one page from its masked base-2 scores s (this
+// lane's 8 tokens per sub-tile) and their lane-local maximum tmax: the new
+// running max and normaliser, the rescaled accumulators, and the
+// probabilities pf for the value product.
+template <int D, int S>
+__device__ __forceinline__ void page_softmax8(const float (*s)[2][4], float tmax, float& m_run, float& l_run,
+                                              f32x4_t* o, float (*pf)[8]) {
+  constexpr int NSUB = S / 32, CT = D / 16;
   tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
   const float m_new = fmaxf(m_run, tmax);
@@ -609,6 +653,47 @@ __device__ __forceinline__ void page_scores8(const PageK8<D, S>& K, const bf16x8
   m_run = m_new;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) o[ct] *= alpha;
+}
+
+// Scores of one page when every 32-channel k-step lies in one quantisation
+// group: the codes decode exactly to bf16, one MFMA per k-step gives the
+// group's partial dot product with q, and the token's group scale multiplies
+// that fp32 partial (score = sum over groups of scale * (codes . q)).  Half
+// the matrix products of page_scores8 and no hi/lo split; every product is
+// exact and the sums are fp32.  ksl: this page's K scales in LDS as
+// [group][S]; kgu[cs]: the group of k-step cs.
+template <int D, int S>
+__device__ __forceinline__ void page_scores8g(const PageK8G<D, S>& K, const bf16x8_t* qf, float q_scale, int ntok,
+                                              int j4, const float* ksl, const int* kgu, float& m_run,
+                                              float& l_run, f32x4_t* o, float (*pf)[8]) {
+  constexpr int NSUB = S / 32, CS = D / 32;
+  float s[NSUB][2][4];
+  float tmax = -__builtin_inff();
+#pragma unroll
+  for (int h = 0; h < NSUB; ++h)
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int cs = 0; cs < CS; ++cs) {
+        float x[8];
+        fp8x8_to_f32(K.k[h][tg][cs], x);
+        const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16_exact(x), qf[cs],
+                                                                     f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        // scales of this lane's 4 output tokens h*32 + 8*j4 + 4*tg + e
+        const f32x4_t ks4 = *reinterpret_cast<const f32x4_t*>(ksl + kgu[cs] * S + h * 32 + 8 * j4 + 4 * tg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[e] = fmaf(part[e], ks4[e], sc[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = h * 32 + 8 * j4 + 4 * tg + e;
+        const float v = tok < ntok ? sc[e] * q_scale : -__builtin_inff();
+        s[h][tg][e] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    }
+  page_softmax8<D, S>(s, tmax, m_run, l_run, o, pf);
 }
 
 // The value product of one page: V codes decode exactly to bf16; the V scale
@@ -654,7 +739,9 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
   }
 }
 
-template <int D, int S, int NW, int SELF>
+// PG: quantisation groups of 32 channels or more (page_scores8g), else the
+// hi/lo score product (page_scores8).
+template <int D, int S, int NW, int SELF, int PG>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a) {
   constexpr int CS = D / 32;
   constexpr int CT = D / 16;
@@ -665,6 +752,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
   __shared__ __attribute__((aligned(16))) float vsl[NW][S * 8];  // per wavefront: [group][S]
+  __shared__ __attribute__((aligned(16))) float ksl[PG ? NW : 1][PG ? S * 8 : 1];  // K scales, same layout
   __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
 
@@ -677,7 +765,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   const int gshift = __builtin_ctz(groups);
   int kgrp[CS], ctgrp[CT];
 #pragma unroll
-  for (int cs = 0; cs < CS; ++cs) kgrp[cs] = (cs * 32 + 8 * j4) / a.qg;
+  for (int cs = 0; cs < CS; ++cs)
+    kgrp[cs] = PG ? __builtin_amdgcn_readfirstlane((cs * 32) / a.qg) : (cs * 32 + 8 * j4) / a.qg;
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) ctgrp[ct] = __builtin_amdgcn_readfirstlane((ct * 16) / a.qg);
 
@@ -706,6 +795,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
   float* vw = vsl[wave];
+  float* kw = ksl[PG ? wave : 0];
 
   // the same two-stage page pipeline as the bf16 kernel
   int j0, jp0;
@@ -724,19 +814,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
     resolve_tiles(a, staged ? trow : nullptr, j, jp, t0 == 0 && lane == 0 && i0 == 0, b, g, nb, len, S,
                   wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
-    PageK8<D, S> K;
+    typename std::conditional<PG != 0, PageK8G<D, S>, PageK8<D, S>>::type K;
     PageV8<D, S> V;
     {
       const long long tile = uniform64(wl_tile[wave][0]);
-      load_page_k8<D, S>(kpool + tile * S * D, a.k_scales + tile * S * groups, groups, kgrp, r, j4, K);
+      if constexpr (PG)
+        load_page_k8g<D, S>(kpool + tile * S * D, a.k_scales + tile * S * groups, groups, r, j4, lane, K);
+      else
+        load_page_k8<D, S>(kpool + tile * S * D, a.k_scales + tile * S * groups, groups, kgrp, r, j4, K);
       load_page_v8<D, S>(vpool + tile * D * S, a.v_scales + tile * S * groups, groups, r, j4, lane, V);
     }
     for (int tt = 0; tt < nt; ++tt) {
       const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
       const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : g));
       float pf[NSUB][8];
-      page_scores8<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, pf);
-      load_page_k8<D, S>(kpool + tnext * S * D, a.k_scales + tnext * S * groups, groups, kgrp, r, j4, K);
+      if constexpr (PG) {
+        // this page's K scales -> LDS as [group][S]
+#pragma unroll
+        for (int y = 0; y < S * 8 / kWave; ++y) {
+          const int x = y * kWave + lane;
+          if (x < S * groups) kw[(x & (groups - 1)) * S + (x >> gshift)] = K.ks[y];
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        page_scores8g<D, S>(K, qf, a.q_scale, ntok, j4, kw, kgrp, m_run, l_run, o, pf);
+        load_page_k8g<D, S>(kpool + tnext * S * D, a.k_scales + tnext * S * groups, groups, r, j4, lane, K);
+      } else {
+        page_scores8<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, pf);
+        load_page_k8<D, S>(kpool + tnext * S * D, a.k_scales + tnext * S * groups, groups, kgrp, r, j4, K);
+      }
       // this page's V scales -> LDS as [group][S]
 #pragma unroll
       for (int y = 0; y < S * 8 / kWave; ++y) {
@@ -1125,12 +1232,19 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int D, int SELF, int PG>
+void launch_mfma8_g(const AttnArgs& a, const dim3& grid, hipStream_t st) {
+  if (a.S == 32)
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves, SELF, PG>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves, SELF, PG>), grid, dim3(64 * kAttnWaves), 0, st, a);
+}
 template <int D, int SELF>
 void launch_mfma8_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
-  if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  if (a.qg >= 32)
+    launch_mfma8_g<D, SELF, 1>(a, grid, st);
   else
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+    launch_mfma8_g<D, SELF, 0>(a, grid, st);
 }
 
 template <int D>

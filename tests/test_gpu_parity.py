@@ -186,6 +186,9 @@ SMALL = [
     ("fp8-one-split", "longfp8", {"B": 2, "L": 3000}, [3000, 100], 0, 3),
     ("fp8-qg32", "longfp8", {"B": 2, "L": 6000}, [6000, 2049], 2, 16),
     ("fp8-qg16-d64", "longfp8", {"B": 2, "L": 3000, "D": 64, "quant_group": 16, "S": 32}, [3000, 100], 0, 9),
+    ("fp8-qg64", "longfp8", {"B": 2, "L": 3000, "quant_group": 64}, [3000, 77], 1, 10),
+    ("fp8-qg128-s32", "longfp8", {"B": 2, "L": 3000, "S": 32, "quant_group": 128}, [3000, 1500], 0, 9),
+    ("fp8-qg32-d64", "longfp8", {"B": 2, "L": 3000, "D": 64}, [2999, 640], 0, 9),
 ]
 
 
