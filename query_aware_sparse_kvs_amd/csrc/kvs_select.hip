@@ -71,6 +71,13 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   constexpr int NPT = NV / NT;
   static_assert(NV % NT == 0, "whole vectors per thread");
   constexpr int VEC = 16 / EB;               // summary elements per 16 bytes
+  constexpr int SEGS = SK == K_MEAN ? 1 : 2;  // rows per block: min and max, or the mean
+  constexpr int SEGV = D * EB / 32;           // 16-byte vectors of half a row
+  constexpr int VPH = SEGS * SEGV;            // vectors of one block's channel half
+  constexpr int NPH = NPT / 2;                // vectors per thread and half
+  static_assert(NPT % 2 == 0 && (D / 2) % VEC == 0, "whole vectors per half");
+  // byte offset in a block's row of vector w (< VPH) of channel half `half`
+  auto half_offset = [](int half, int w) { return (w / SEGV) * (D * EB) + half * (D * EB / 2) + (w % SEGV) * 16; };
   constexpr int WPR = D * EB / 4;            // 32-bit words per half row
   __shared__ __attribute__((aligned(16))) char sm[NB * ROWP];
   __shared__ __attribute__((aligned(16))) double qd[G][D];
@@ -96,26 +103,45 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   // beside the vector loads below instead of queued behind them
   int len = *(const __attribute__((address_space(4))) int32_t*)(a.seq_lens + b);
 
-  // stage the chunk's summaries: every load issued before any use, and not
-  // waiting for seq_lens (blocks past nb are read but never used)
+  // the query first: loads complete in issue order, so the query must not
+  // queue behind the chunk
+  constexpr int QPT = (G * D + NT - 1) / NT;
+  float qv[QPT];
+#pragma unroll
+  for (int y = 0; y < QPT; ++y) {
+    // unconditional loads (index clamped) keep the load counter exact
+    const int i = min(y * NT + tid, G * D - 1);
+    const int h = i / D, c = i % D;
+    const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
+    if constexpr (QK == K_F32)
+      qv[y] = static_cast<const float*>(a.q)[qi];
+    else
+      qv[y] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the query loads stay ahead of the chunk's
+  // stage the chunk's summaries in two channel halves (channels [0, D/2),
+  // then [D/2, D), of the min and the max rows of all NB blocks), every load
+  // issued before any use and not waiting for seq_lens (blocks past nb are
+  // read but never used): the first half's fp64 chains run while the
+  // second half is still arriving
   const char* src = static_cast<const char*>(a.summ) + (((long long)b * a.Hkv + g) * a.MB + j0) * ROWB;
   u32x4 raw[NPT];
 #pragma unroll
   for (int x = 0; x < NPT; ++x) {
-    const int v = x * NT + tid;
-    raw[x] = u32x4{0u, 0u, 0u, 0u};
-    if (v / (ROWB / 16) < nmem) raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)v * 16);
+    if (x == NPH) __builtin_amdgcn_sched_barrier(0);  // the first half's loads go out first
+    const int half = x / NPH, u = (x % NPH) * NT + tid;
+    // blocks past the array read its last block of the chunk instead (their
+    // rows are never used): no branch, so the load counter stays exact and
+    // the first half waits for its own loads only
+    const int blk = min(u / VPH, nmem - 1), off = half_offset(half, u % VPH);
+    raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)blk * ROWB + off);
   }
+  __builtin_amdgcn_sched_barrier(0);
   // the query as fp64, and per head the words' choice of max (mask bits set) or min
-  for (int i = tid; i < G * D; i += NT) {
-    const int h = i / D, c = i % D;
-    const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
-    float v;
-    if constexpr (QK == K_F32)
-      v = static_cast<const float*>(a.q)[qi];
-    else
-      v = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
-    qd[h][c] = (double)v;
+#pragma unroll
+  for (int y = 0; y < QPT; ++y) {
+    const int i = y * NT + tid;
+    if (i < G * D) qd[i / D][i % D] = (double)qv[y];
   }
   // the decode token is appended by the unit's first workgroup while its
   // chunk loads are in flight (a workgroup of its own would leave some
@@ -134,14 +160,16 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     len = len < 0 ? 0 : cap;
   }
   const int nb = (len + a.S - 1) / a.S;
+  // one half of the chunk -> its LDS rows
+  auto stage_half = [&](int half) {
 #pragma unroll
-  for (int x = 0; x < NPT; ++x) {
-    const int v = x * NT + tid;
-    if (v / (ROWB / 16) < nmem) {
-      const int blk = v / (ROWB / 16), off = (v % (ROWB / 16)) * 16;
-      *reinterpret_cast<u32x4*>(sm + blk * ROWP + off) = raw[x];
+    for (int x = half * NPH; x < half * NPH + NPH; ++x) {
+      const int u = (x % NPH) * NT + tid;
+      const int blk = u / VPH;
+      if (blk < nmem) *reinterpret_cast<u32x4*>(sm + blk * ROWP + half_offset(half, u % VPH)) = raw[x];
     }
-  }
+  };
+  stage_half(0);
   __syncthreads();
   for (int i = tid; i < G * WPR; i += NT) {
     const int h = i / WPR, w = i % WPR;
@@ -161,9 +189,14 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   for (int i = 0; i < HPW; ++i) acc[i] = 0.0;
   const char* pmn = sm + lane * ROWP;
   const char* pmx = pmn + D * EB;
-  if (wave < G) {
+  for (int half = 0; half < 2; ++half) {
+    if (half == 1) {
+      stage_half(1);
+      __syncthreads();
+    }
+    if (wave >= G) continue;
 #pragma unroll 1
-    for (int c0 = 0; c0 < D; c0 += VEC) {
+    for (int c0 = half * (D / 2); c0 < half * (D / 2) + D / 2; c0 += VEC) {
       const u32x4 vmn = *reinterpret_cast<const u32x4*>(pmn + c0 * EB);
       u32x4 vmx = vmn;
       if constexpr (SK != K_MEAN) vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
