@@ -551,6 +551,69 @@ def test_full_llama8b_layer(env):
     assert np.array_equal(st.sel.cpu().numpy(), o_sel), "selection without bounds_out differs"
 
 
+
+def _newest_token_append(env, w, inp):
+    """The benchmark's decode token: each sequence's newest K/V appended
+    again, which leaves the cache (pools and min/max summaries) as it is, so
+    the oracle's results on the cache are the expected ones."""
+    nt = env.synth.newest_tokens(w, inp)
+    return env.kvs.AppendArgs(k_new=nt["k_new"], v_new=nt["v_new"], k_new_scales=nt["k_new_scales"],
+                              v_new_scales=nt["v_new_scales"], block_table=inp["block_table"],
+                              k_pool=inp["k_pool"], v_pool=inp["v_pool"], k_scales=inp["k_scales"],
+                              v_scales=inp["v_scales"])
+
+
+def test_full_llama8b_fused_route(env):
+    """The benchmark's timed step at full size (32K context, 8 sequences,
+    k = 128 of 512): kvs_score_blocks with the token append, then
+    kvs_select_attn selecting inside the attention.  Summaries, scores and
+    selection bit-exact, attention within the bars, whole layer."""
+    from query_aware_sparse_kvs_amd.step import SparseDecodeStep
+    w = env.synth.WORKLOADS["llama8b"]
+    p = Problem(env, w, layer=5)
+    st = SparseDecodeStep(p.L, w.k, env.dev)
+    summ = st.new_summaries(env.dev)
+    st.prefill_summaries(p.inp["k_pool"], None, p.inp["block_table"], p.inp["seq_lens"], summ)
+    out = st.run_decode_fused(p.inp["q"], _newest_token_append(env, w, p.inp), p.inp["seq_lens"], summ)
+    no_device_errors(env)
+    check_summaries(p, summ, p.or_summaries())
+    o_sel, ties = check_selection(p, st.sel, st.scores, w.k)
+    err, rel = check_attn(out, p.or_attn(o_sel))
+    print(f"[llama8b fused] near-tie units {ties}; attention max|err| {err:.2e} rel L2 {rel:.2e}")
+
+
+def test_full_longfp8_fused_route(env):
+    """The fp8 workload's timed step at full size (131072 tokens, k = 64 of
+    2048: the attention workgroups select from 2048 scores, and the score
+    product runs per 32-channel quantisation group), two sequences checked
+    against the oracle."""
+    from query_aware_sparse_kvs_amd.step import SparseDecodeStep
+    torch, orc = env.torch, env.orc
+    w = env.synth.WORKLOADS["longfp8"]
+    p = Problem(env, w)
+    st = SparseDecodeStep(p.L, w.k, env.dev)
+    summ = st.new_summaries(env.dev)
+    st.prefill_summaries(p.inp["k_pool"], p.inp["k_scales"], p.inp["block_table"], p.inp["seq_lens"], summ)
+    out = st.run_decode_fused(p.inp["q"], _newest_token_append(env, w, p.inp), p.inp["seq_lens"], summ)
+    no_device_errors(env)
+    seqs = [0, 2]
+    flat = p.inp["block_table"][seqs].long().reshape(-1)
+    sub = lambda n: p.inp[n][flat].cpu().numpy()
+    new_tbl = np.arange(flat.numel(), dtype=np.int32).reshape(len(seqs), -1)
+    lens = p.h["lens"][seqs]
+    OL = orc.Layout(len(seqs), w.Hq, w.Hkv, w.D, w.S, w.nb, flat.numel(), orc.KV_E4M3, w.quant_group)
+    o_summ = orc.summaries(OL, sub("k_pool"), sub("k_scales"), new_tbl, lens)
+    assert np.array_equal(summ[seqs].double().cpu().numpy(), o_summ)
+    o_W = orc.bounds(OL, p.h["q"][seqs], o_summ, lens)
+    assert np.array_equal(st.scores[seqs].cpu().numpy(), o_W)
+    o_sel = orc.select(OL, o_W, lens, w.k)
+    assert np.array_equal(st.sel[seqs].cpu().numpy(), o_sel)
+    o_out = orc.sparse_attn(OL, p.h["q"][seqs], sub("k_pool"), sub("v_pool"), sub("k_scales"), sub("v_scales"),
+                            new_tbl, lens, o_sel, 1 / math.sqrt(w.D))
+    err, rel = check_attn(out[seqs], o_out)
+    print(f"[longfp8 fused] attention max|err| {err:.2e} rel L2 {rel:.2e}")
+
+
 def _compact(p, seqs):
     """A problem holding only sequences `seqs` of p (pages copied, table
     remapped), for oracle runs on a sample of a large workload."""
