@@ -629,7 +629,8 @@ def _compact(p, seqs):
 
 def test_full_highconc_sampled(env):
     """256 sequences at 32K, k = 32, over a 131072-page shared pool: the
-    whole batch runs on the GPU; 4 sampled sequences are checked."""
+    whole batch runs on the GPU; 4 sampled sequences are checked, also
+    through the timed route (token append, matrix-core scores)."""
     from query_aware_sparse_kvs_amd.step import SparseDecodeStep
     torch, orc = env.torch, env.orc
     w = env.synth.WORKLOADS["highconc"]
@@ -668,6 +669,13 @@ def test_full_highconc_sampled(env):
     no_device_errors(env)
     assert torch.equal(summ, exact_summ), "fused newest-block rebuild differs"
     assert torch.equal(st.sel, exact_sel), "selection without bounds_out differs"
+    # the benchmark's timed route for this layout: the token append with the
+    # matrix-core scores and the top-k launch, then the attention
+    out = st.run_decode(p_inp["q"], _newest_token_append(env, w, p_inp), p_inp["seq_lens"], summ)
+    no_device_errors(env)
+    assert torch.equal(summ, exact_summ), "summaries after the token append differ"
+    assert torch.equal(st.sel, exact_sel), "selection of the timed route differs"
+    check_attn(out[seqs], o_out)
 
 
 def test_full_longfp8_sampled(env):
