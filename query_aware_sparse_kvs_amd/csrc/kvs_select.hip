@@ -5,7 +5,8 @@
 //
 // bounds_kernel: a workgroup of 4 wavefronts (8 for groups of 8 or more
 // query heads, one per head) stages 64 consecutive blocks' summaries in LDS
-// with coalesced 16-byte loads; lane = block, wavefront w takes query heads
+// with coalesced 16-byte loads, in two channel halves so that the first
+// half's sums run while the second half arrives; lane = block, wavefront w takes query heads
 // w, w+NW, ...  The block score is
 // U = sum_c max(q_c*mn_c, q_c*mx_c); since mx_c >= mn_c the larger product is
 // q_c*mx_c when q_c >= 0 and q_c*mn_c otherwise.  That choice depends only
