@@ -698,7 +698,9 @@ __device__ __forceinline__ void page_scores8g(const PageK8G<D, S>& K, const bf16
 
 // The value product of one page: V codes decode exactly to bf16; the V scale
 // of (token, channel group) is folded into P per group (P' = p * scale,
-// split hi + lo).  vsl: this page's V scales in LDS as [group][S].
+// split hi + lo).  vsl: this page's V scales in LDS as [group][S].  Slots at
+// or past ntok may hold any bytes, scales included (NaN, Inf): their P' is
+// set to zero by selection, never by multiplying p = 0 with the scale.
 template <int D, int S>
 __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, int j4, const float (*pf)[8],
                                              const float* vsl, const int* ctgrp, f32x4_t* o) {
@@ -721,8 +723,8 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
         float pp[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pp[e] = pf[h][e] * s0[e];
-          pp[4 + e] = pf[h][4 + e] * s1[e];
+          pp[e] = t0 + e < nt ? pf[h][e] * s0[e] : 0.0f;
+          pp[4 + e] = t0 + 4 + e < nt ? pf[h][4 + e] * s1[e] : 0.0f;
         }
         split_bf16(pp, phi, plo);
       }

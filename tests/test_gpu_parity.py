@@ -416,6 +416,70 @@ def test_attention_padding_empty_and_partial(env):
     assert (g[1] == 0).all() and (g[0, 3 * w.G:4 * w.G] == 0).all()
 
 
+POISON = [
+    # (name, workload, overrides, seq_lens, k)
+    ("bf16", "llama8b", {"B": 3, "L": 3000, "layers": 1}, [3000, 1000, 77], 12),
+    ("f32", "tiny", {"B": 2, "L": 1000}, [1000, 999], 8),
+    ("fp8-qg32", "longfp8", {"B": 3, "L": 3000}, [3000, 1001, 70], 12),
+    ("fp8-qg16-s32", "longfp8", {"B": 2, "L": 3000, "S": 32, "quant_group": 16}, [2999, 1000], 9),
+]
+
+
+@pytest.mark.parametrize("case", POISON, ids=[c[0] for c in POISON])
+def test_partial_block_tail_slots_are_never_read(env, case):
+    """Token slots at or past seq_len in each sequence's newest (partial)
+    page hold NaN codes and NaN / Inf scales: summaries, scores, selection
+    and attention (with a given selection and with the in-attention top-k)
+    must equal the oracle's, which never reads those slots."""
+    name, base, over, lens, k = case
+    torch, kvs = env.torch, env.kvs
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    p = Problem(env, w, seq_lens=lens)
+    S, D = w.S, w.D
+    T = min(S, 32)
+    kp, vp = p.inp["k_pool"], p.inp["v_pool"]
+    nan_bits = {torch.bfloat16: 0x7FC0, torch.float32: None, torch.uint8: 0x7F}[kp.dtype]
+    for b, n in enumerate(lens):
+        if n % S == 0:
+            continue
+        page = int(p.inp["block_table"][b, (n - 1) // S])
+        for t in range(n % S, S):
+            if kp.dtype == torch.float32:
+                kp[page, :, t] = float("nan")
+                vp[page, :, t // T, :, t % T] = float("inf")
+            elif kp.dtype == torch.bfloat16:
+                kp[page, :, t].view(torch.int16).fill_(nan_bits)
+                vp[page, :, t // T, :, t % T].view(torch.int16).fill_(nan_bits)
+            else:
+                kp[page, :, t] = nan_bits
+                vp[page, :, t // T, :, t % T] = nan_bits
+                p.inp["k_scales"][page, :, t] = float("nan")
+                p.inp["v_scales"][page, :, t, 0] = float("inf")
+                p.inp["v_scales"][page, :, t, 1:] = float("nan")
+    for n in ("k_pool", "v_pool"):
+        p.h[n] = np_pool(p.inp[n])
+    for n in ("k_scales", "v_scales"):
+        if p.inp[n] is not None:
+            p.h[n] = p.inp[n].cpu().numpy()
+    print(f"[poison {name}] B={w.B} S={S} D={D} lens={lens} k={k} {w.kv_dtype}", flush=True)
+    g_summ = p.gpu_summaries()
+    no_device_errors(env)
+    check_summaries(p, g_summ, p.or_summaries())
+    g_sel, g_W = p.gpu_select(g_summ, k)
+    no_device_errors(env)
+    o_sel, _ = check_selection(p, g_sel, g_W, k)
+    err, rel = check_attn(p.gpu_attn(g_sel, k), p.or_attn(o_sel))
+    sel2 = torch.full_like(g_sel, -7)
+    out2 = torch.full((w.B, w.Hq, D), float("nan"), device=env.dev)
+    ws = torch.zeros(kvs.kvs_attn_workspace_size(p.L, k), dtype=torch.uint8, device=env.dev)
+    kvs.kvs_select_attn(p.L, p.inp["q"], kp, vp, p.inp["k_scales"], p.inp["v_scales"], p.inp["block_table"],
+                        p.inp["seq_lens"], g_W, k, 1, sel2, p.sm_scale, out2, ws)
+    no_device_errors(env)
+    assert np.array_equal(sel2.cpu().numpy(), o_sel), "in-attention selection differs"
+    check_attn(out2, p.or_attn(o_sel))
+    print(f"[poison {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
+
+
 def test_device_error_flags_are_raised_and_work_stays_in_bounds(env):
     torch, kvs = env.torch, env.kvs
     w = env.synth.scaled(env.synth.WORKLOADS["llama8b"], B=2, L=640, layers=1)
@@ -711,10 +775,13 @@ def test_full_longfp8_sampled(env):
     check_attn(out[seqs], o_out)
 
 
-def test_full_hotbuf_steps(env):
-    """Hot-buffer workload at full size: 128 slots per unit (25 % of 512),
-    the selection drifting by 13 blocks a step; tables checked bit-exact for
-    all 32 units, attention for the last step."""
+@pytest.mark.parametrize("ns", [128, 160])
+def test_full_hotbuf_steps(env, ns):
+    """Hot-buffer workload at full size: 128 slots per unit (25 % of 512; and
+    160, more than k, so that the LRU order picks the victims), the selection
+    drifting by 13 blocks a step over 16 steps; page tables, owners, stamps,
+    miss lists and counts bit-exact for all 32 units at every step, attention
+    through the hot table for the last step."""
     from query_aware_sparse_kvs_amd.step import HotBufferStep, SparseDecodeStep
     torch, orc = env.torch, env.orc
     w = env.synth.WORKLOADS["hotbuf"]
@@ -723,23 +790,31 @@ def test_full_hotbuf_steps(env):
     summ = st.new_summaries(env.dev)
     st.prefill_summaries(p.inp["k_pool"], None, p.inp["block_table"], p.inp["seq_lens"], summ)
     sel0, _ = p.gpu_select(summ, w.k)
-    stream = env.synth.drift_selections(sel0.cpu().numpy(), w.nb, 3, w.drift, seed=w.seed)
+    steps = 16
+    stream = env.synth.drift_selections(sel0.cpu().numpy(), w.nb, steps, w.drift, seed=w.seed)
     hk, hv, _, _ = host_tier(p)
-    hs = HotBufferStep(p.L, w.k, w.hot_slots, env.dev)
-    units, ns = w.B * w.Hkv, w.hot_slots
+    hs = HotBufferStep(p.L, w.k, ns, env.dev)
+    units = w.B * w.Hkv
     pt = np.full((units, w.nb), -1, np.int32)
     owner = np.full((units, ns), -1, np.int32)
     stamp = np.full((units, ns), -1, np.int64)
     for t in range(stream.shape[0]):
+        print(f"[hotbuf full ns={ns}] step {t}", flush=True)
         sel = torch.from_numpy(stream[t]).to(env.dev)
         out = hs.run(t, sel, p.inp["q"], p.inp["seq_lens"], hk, hv)
         no_device_errors(env)
-        counts = []
+        misses, counts = [], []
         for u in range(units):
-            _, c = orc.hot_step(w.nb, ns, t, u * ns, stream[t].reshape(units, -1)[u], pt[u], owner[u], stamp[u])
+            m, c = orc.hot_step(w.nb, ns, t, u * ns, stream[t].reshape(units, -1)[u], pt[u], owner[u], stamp[u])
+            misses.append(m)
             counts.append(c)
         assert np.array_equal(hs.page_table.cpu().numpy().reshape(units, -1), pt)
         assert np.array_equal(hs.slot_owner.cpu().numpy().reshape(units, -1), owner)
+        assert np.array_equal(hs.slot_stamp.cpu().numpy().reshape(units, -1), stamp)
+        assert np.array_equal(hs.miss_list.cpu().numpy().reshape(units, -1), np.stack(misses))
         assert np.array_equal(hs.miss_count.cpu().numpy().reshape(-1), np.array(counts))
-        assert all(c == (w.k if t == 0 else w.drift) for c in counts)
+        if ns == w.k:  # every block entering the selection is a miss
+            assert all(c == (w.k if t == 0 else w.drift) for c in counts)
+        else:
+            assert all(c == w.k for c in counts) if t == 0 else all(c <= w.drift for c in counts)
     check_attn(out, p.or_attn(stream[-1]))
