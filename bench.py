@@ -36,6 +36,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -205,10 +207,19 @@ def main(argv=None) -> int:
                             inp["block_table"], inp["seq_lens"], st.scores, w.k, 1, st.sel, st.sm_scale, st.out,
                             st.attn_ws)
 
+    def graph_of(fn, layer_ids):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in layer_ids:
+                fn(i)
+        return g
+
     def capture(fn):
         """One graph over every layer instance in order (as a decoder runs its
-        layers), plus one graph per layer for step counts that are not a
-        multiple of the layer count."""
+        layers) and, when the warm-up or timed step count is not a multiple of
+        the layer count, one graph over the first (count mod layers)
+        instances: any step count then replays whole graphs of the same layer
+        sequence, with no per-step graph launches."""
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -216,24 +227,20 @@ def main(argv=None) -> int:
                 fn(i)  # eager warm-up (also initialises the library's per-device state)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        sweep = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(sweep):
-            for i in range(n_layers):
-                fn(i)
-        single = []
-        for i in range(n_layers):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                fn(i)
-            single.append(g)
-        return sweep, single
+        sweep = graph_of(fn, range(n_layers))
+        part = {}
+        for count in (args.steps, args.warmup):
+            r = count % n_layers
+            if r and r not in part:
+                part[r] = graph_of(fn, range(r))
+        return sweep, part
 
     def replay(graphs, K):
-        sweep, single = graphs
+        sweep, part = graphs
         for _ in range(K // n_layers):
             sweep.replay()
-        for i in range(K % n_layers):
-            single[i].replay()
+        if K % n_layers:
+            part[K % n_layers].replay()
 
     def timed(graphs, K, W):
         replay(graphs, W)
@@ -253,10 +260,10 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
-    # distribution: every layer-step graph replayed alone between two events
-    # (the sweep above is the throughput figure; these include one event
-    # pair per step)
-    single = step_graphs[1]
+    # distribution: every layer-step graph replayed alone between two HIP
+    # events (the sweep above is the throughput figure; these include the
+    # launch of one graph and one event pair per step)
+    single = [graph_of(run_step, [i]) for i in range(n_layers)]
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
     for i, (e0, e1) in enumerate(evs):
@@ -264,6 +271,7 @@ def main(argv=None) -> int:
         single[i % n_layers].replay()
         e1.record()
     torch.cuda.synchronize()
+    del single
     per = np.sort(np.array([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]))
     pct = {f"p{q}": round(float(np.percentile(per, q)), 3) for q in (10, 50, 90)}
     # per-phase graphs: the dominant kernel (attention) for the roofline entry,
@@ -295,9 +303,17 @@ def main(argv=None) -> int:
     attn_bytes = by["attention"] + (by["scores"] if fused else 0)
     attn_gbps = attn_bytes / attn_sec / 1e9
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, layers, args.cpu_steps)
+        # each sampled layer's GPU results from one more step (the phase
+        # graphs above leave other phases' results in the step buffers)
+        gpu_results = []
+        for li in range(min(args.cpu_steps, n_layers)):
+            run_step(li)
+            torch.cuda.synchronize()
+            gpu_results.append((steps[li].sel.cpu().numpy(), steps[li].out.cpu().numpy()))
+        assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
+        cpu, parity = cpu_baseline(w, layers, args.cpu_steps, gpu_results)
 
     result = {
         "metric": METRIC,
@@ -330,6 +346,7 @@ def main(argv=None) -> int:
                      "traffic": measured_traffic(w.name, "select_attn" if fused else "attention"),
                      "bytes_per_launch": attn_bytes, "us_per_launch": round(attn_sec * 1e6, 3)},
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
         "wall_s_timed_region": round(wall_step, 4),
     }
     print(json.dumps(result), flush=True)
@@ -600,77 +617,164 @@ def measured_traffic(workload: str, call: str):
         return None
 
 
-def cpu_baseline(w, layers, n_steps):
+def host_info() -> dict:
+    """The host the CPU baseline runs on: logical CPUs, the ones this process
+    may use, and the CPU model from /proc/cpuinfo."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+
+
+NEAR_TIE = 1e-4  # the acceptance band: (k-2)-th and (k-1)-th free candidate scores
+
+
+def near_tie_units(W, lens, S, k) -> int:
+    """Units whose (k-2)-th and (k-1)-th best free candidates score within
+    NEAR_TIE relative of each other (there a selection may differ)."""
+    n = 0
+    for b, L in enumerate(lens):
+        nb = (int(L) + S - 1) // S
+        if nb <= k or k < 3:
+            continue
+        for g in range(W.shape[1]):
+            c = np.sort(W[b, g, 1:nb - 1])[::-1]
+            a, z = c[k - 3], c[k - 2]
+            if abs(a - z) <= NEAR_TIE * max(abs(a), abs(z)):
+                n += 1
+    return n
+
+
+def cpu_baseline(w, layers, n_steps, gpu_results, max_threads=16):
     """The oracle (fp64, as written) on `n_steps` whole layer-steps of the
     same workload -- decode-token append (with its block's summary), bounds,
     selection, sparse attention -- run once on one thread and once fanned out
-    over the sequences on the host's cores."""
-    import numpy as np
+    over the independent (sequence, KV head) units on up to `max_threads`
+    host cores (the oracle's ctypes calls release the interpreter lock).  The
+    one-thread run's selections and outputs are also compared with the GPU's
+    (`gpu_results`: per sampled layer, its sel and out after one step)."""
+    import concurrent.futures as cf
+
     import torch
 
     import oracle
     code = {"f32": oracle.KV_F32, "bf16": oracle.KV_BF16, "e4m3": oracle.KV_E4M3}[w.kv_dtype]
     OL = oracle.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code, w.quant_group)
     n_steps = max(1, min(n_steps, len(layers)))
+    sm = 1.0 / math.sqrt(w.D)
+
+    def host_np(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
     host = []
     for li in range(n_steps):
         inp = layers[li]["inp"]
-        h = {}
-        for n in ("k_pool", "v_pool"):
-            t = inp[n].cpu()
-            h[n] = t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+        h = {n: host_np(inp[n]) for n in ("k_pool", "v_pool")}
         for n in ("k_scales", "v_scales"):
             h[n] = None if inp[n] is None else inp[n].cpu().numpy()
         h["table"] = inp["block_table"].cpu().numpy()
         h["lens"] = inp["seq_lens"].cpu().numpy()
         h["q"] = inp["q"].double().cpu().numpy()
-        h["newest"] = layers[li]["newest"].cpu().numpy()
         nt = layers[li]["nt"]
         for n in ("k_new", "v_new"):
-            t = nt[n].cpu()
-            h[n] = t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+            h[n] = host_np(nt[n])
         for n in ("k_new_scales", "v_new_scales"):
             h[n] = None if nt[n] is None else nt[n].cpu().numpy()
         # prefill-time summaries of every block, built by the oracle (untimed)
         h["summ"] = oracle.summaries(OL, h["k_pool"], h["k_scales"], h["table"], h["lens"])
+        # per-KV-head copies of the pools for the fan-out (untimed)
+        for n in ("k_pool", "v_pool", "k_scales", "v_scales"):
+            h[n + "_h"] = None if h[n] is None else [np.ascontiguousarray(h[n][:, g:g + 1]) for g in range(w.Hkv)]
+        h["summ_u"] = {(b, g): np.ascontiguousarray(h["summ"][b:b + 1, g:g + 1])
+                       for b in range(w.B) for g in range(w.Hkv)}
         host.append(h)
-    def layer_step(h, b0, b1):
-        """The oracle's layer-step for sequences b0..b1-1 (their own rows of
-        every per-sequence array; the pools are shared)."""
-        Ls = oracle.Layout(b1 - b0, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, code, w.quant_group)
-        r = slice(b0, b1)
-        new_s = [None if h[n] is None else np.ascontiguousarray(h[n][r]) for n in ("k_new_scales", "v_new_scales")]
-        summ = np.ascontiguousarray(h["summ"][r])
-        oracle.append_token(Ls, np.ascontiguousarray(h["k_new"][r]), np.ascontiguousarray(h["v_new"][r]),
-                            new_s[0], new_s[1], h["table"][r], h["lens"][r], h["k_pool"], h["v_pool"],
-                            h["k_scales"], h["v_scales"], summ)
-        W = oracle.bounds(Ls, h["q"][r], summ, h["lens"][r])
-        sel = oracle.select(Ls, W, h["lens"][r], w.k)
-        oracle.sparse_attn(Ls, h["q"][r], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["table"][r],
-                           h["lens"][r], sel, 1.0 / math.sqrt(w.D))
-        h["summ"][r] = summ
+
+    def layer_step(h):
+        """The oracle's layer-step for the whole batch."""
+        oracle.append_token(OL, h["k_new"], h["v_new"], h["k_new_scales"], h["v_new_scales"], h["table"],
+                            h["lens"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["summ"])
+        W = oracle.bounds(OL, h["q"], h["summ"], h["lens"])
+        sel = oracle.select(OL, W, h["lens"], w.k)
+        out = oracle.sparse_attn(OL, h["q"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["table"],
+                                 h["lens"], sel, sm)
+        return W, sel, out
+
+    def unit_step(h, b, g):
+        """The same for one (sequence, KV head) unit, on its head's pools."""
+        Lu = oracle.Layout(1, w.G, 1, w.D, w.S, w.nb, w.B * w.nb, code, w.quant_group)
+        r, hs = slice(b, b + 1), slice(g * w.G, (g + 1) * w.G)
+        pick = lambda n: None if h[n] is None else np.ascontiguousarray(h[n][r, g:g + 1])
+        per = lambda n: None if h[n + "_h"] is None else h[n + "_h"][g]
+        summ = h["summ_u"][(b, g)]
+        oracle.append_token(Lu, pick("k_new"), pick("v_new"), pick("k_new_scales"), pick("v_new_scales"),
+                            h["table"][r], h["lens"][r], per("k_pool"), per("v_pool"), per("k_scales"),
+                            per("v_scales"), summ)
+        q = np.ascontiguousarray(h["q"][r, hs])
+        W = oracle.bounds(Lu, q, summ, h["lens"][r])
+        sel = oracle.select(Lu, W, h["lens"][r], w.k)
+        return sel, oracle.sparse_attn(Lu, q, per("k_pool"), per("v_pool"), per("k_scales"), per("v_scales"),
+                                       h["table"][r], h["lens"][r], sel, sm)
 
     print(f"[bench] CPU oracle on {n_steps} layer-step(s), one thread", file=sys.stderr, flush=True)
+    res = []
     t0 = time.perf_counter()
     for h in host:
-        layer_step(h, 0, w.B)
+        res.append(layer_step(h))
     dt1 = time.perf_counter() - t0
-    # the same oracle code fanned out over the sequences (independent units;
-    # the library's ctypes calls release the interpreter lock)
-    import concurrent.futures as cf
-    threads = min(w.B, len(os.sched_getaffinity(0)))
-    print(f"[bench] CPU oracle on {n_steps} layer-step(s), {threads} threads", file=sys.stderr, flush=True)
+    units = w.B * w.Hkv
+    threads = max(1, min(len(os.sched_getaffinity(0)), max_threads, units))
+    print(f"[bench] CPU oracle on {n_steps} layer-step(s), {units} units per step over {threads} threads",
+          file=sys.stderr, flush=True)
+    tasks = [(li, b, g) for li in range(n_steps) for b in range(w.B) for g in range(w.Hkv)]
     t0 = time.perf_counter()
     with cf.ThreadPoolExecutor(max_workers=threads) as ex:
-        for h in host:
-            list(ex.map(lambda b: layer_step(h, b, b + 1), range(w.B)))
+        fan = list(ex.map(lambda t: unit_step(host[t[0]], t[1], t[2]), tasks))
     dtn = time.perf_counter() - t0
-    return {"value": round(w.B * n_steps / dtn, 3), "unit": "query-tokens/s/layer", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n_steps} full layer-step(s) of {w.name} (all {w.B} sequences, {w.B * w.Hkv} units: "
-                      f"append, bounds, selection, attention), fp64, sequences fanned out over {threads} "
-                      f"threads: {dtn:.2f} s; one thread: {dt1:.2f} s",
-            "single_thread_value": round(w.B * n_steps / dt1, 3)}
+    # the fan-out computes the same thing unit by unit
+    for (li, b, g), (sel_u, out_u) in zip(tasks, fan):
+        assert np.array_equal(sel_u[0, 0], res[li][1][b, g]), "oracle fan-out selection differs"
+        assert np.array_equal(out_u[0], res[li][2][b, g * w.G:(g + 1) * w.G]), "oracle fan-out output differs"
+
+    # parity of the GPU's step against the one-thread oracle run
+    ties = differ = differ_outside = 0
+    err = num = den = 0.0
+    for li, (W, o_sel, o_out) in enumerate(res):
+        g_sel, g_out = gpu_results[li]
+        lens = host[li]["lens"]
+        ties += near_tie_units(W, lens, w.S, w.k)
+        bad = ~np.all(g_sel == o_sel, axis=-1)  # [B][Hkv]
+        differ += int(bad.sum())
+        if bad.any():
+            tie_b = {(b, g) for b in range(w.B) for g in range(w.Hkv)
+                     if near_tie_units(W[b:b + 1, g:g + 1], lens[b:b + 1], w.S, w.k)}
+            differ_outside += sum(1 for b, g in zip(*np.nonzero(bad)) if (b, g) not in tie_b)
+            h = host[li]
+            o_out = oracle.sparse_attn(OL, h["q"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"],
+                                       h["table"], lens, g_sel, sm)  # attention on the GPU's selection
+        d = g_out.astype(np.float64) - o_out
+        err = max(err, float(np.abs(d).max()))
+        num += float((d * d).sum())
+        den += float((o_out * o_out).sum())
+    parity = {"layer_steps": n_steps, "units": n_steps * units, "near_tie_units": ties,
+              "selection_units_differing": differ, "selection_units_differing_outside_near_ties": differ_outside,
+              "attention_max_abs_err": err, "attention_rel_l2": math.sqrt(num / den) if den > 0 else 0.0,
+              "bars": {"selection": "bit-exact outside near ties (1e-4 relative)", "max_abs_err": 1e-2,
+                       "rel_l2": 5e-3}}
+    info = host_info()
+    baseline = {"value": round(w.B * n_steps / dtn, 3), "unit": "query-tokens/s/layer", "cores": threads,
+                "kind": "oracle",
+                "sample": f"{n_steps} full layer-step(s) of {w.name} (all {w.B} sequences, {units} units: "
+                          f"append, bounds, selection, attention), fp64, the (sequence, KV head) units "
+                          f"fanned out over {threads} threads: {dtn:.2f} s; one thread: {dt1:.2f} s",
+                "single_thread_value": round(w.B * n_steps / dt1, 3), **info}
+    return baseline, parity
 
 
 if __name__ == "__main__":
