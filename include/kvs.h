@@ -370,6 +370,33 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* layout, int32_t table_kind,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * kvs_sparse_decode_attn_noalloc -- kvs_sparse_decode_attn with no
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc)
+ *
+ * Same computation, arguments, kernels and results as
+ * kvs_sparse_decode_attn.  The split partials go to a device array the
+ * library holds: KVS_NOALLOC_SCRATCH_BYTES on every GPU it runs on, kept
+ * until the process ends.  The call allocates and frees nothing.  Every call
+ * on one GPU shares that GPU's array, so calls that overlap on one GPU
+ * (concurrent streams, or host threads on the same device) race and give
+ * undefined results; calls on one stream are fine.  No contents need to
+ * survive between calls (each call writes every partial it reads).
+ * Errors: as kvs_sparse_decode_attn, and CAPACITY when the layout's
+ * partials (kvs_attn_workspace_size) exceed KVS_NOALLOC_SCRATCH_BYTES; every
+ * layout the library accepts needs at most 4.25 MiB.
+ * ---------------------------------------------------------------------- */
+#define KVS_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+kvs_status kvs_sparse_decode_attn_noalloc(const kvs_layout* layout, int32_t table_kind,
+                                          const void* q, const void* k_pool, const void* v_pool,
+                                          const float* k_scales, const float* v_scales,
+                                          const int32_t* table, const int32_t* seq_lens,
+                                          const int32_t* sel, int32_t k, float sm_scale, float* out,
+                                          void* stream);
+
+/* ------------------------------------------------------------------------
  * kvs_score_blocks + kvs_select_attn -- the layer-step of kvs_select_topk_ex
  * followed by kvs_sparse_decode_attn, with the top-k done inside the
  * attention launch

@@ -11,6 +11,15 @@
 // OR of KVS_DEVERR_* bits raised by kernels on this device.
 __device__ unsigned int kvs_device_error_word = 0u;
 
+// The allocation-free attention entry point keeps its split partials in
+// this file-scope array, one copy per GPU (the code object is loaded on
+// every device the library runs on) that lives until the process ends.
+// Several splits per (sequence, KV head) only happen while B*Hkv < 256
+// compute units, so B*Hq*nsplit < 16*512 rows of (2 + D) floats: at most
+// 4.25 MiB for D = 128.  Host code uses the per-device address from
+// hipGetSymbolAddress, never the name.
+static __device__ __align__(256) unsigned char scratch[KVS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -122,10 +131,37 @@ int attn_splits(const kvs_layout* L, int32_t k) {
   return kvs::attn_num_splits(L->num_seqs * L->num_kv_heads, k);
 }
 
-// attention workspace: [split m, l][split acc]
+// attention workspace: [split m, l][split acc].  With one split the kernels
+// write the output rows directly and never touch it (256 bytes are still
+// asked for, so that a workspace pointer always exists).
 size_t attn_ws(const kvs_layout* L, int32_t k) {
-  const size_t units = (size_t)L->num_seqs * L->num_q_heads * attn_splits(L, k);
+  const int nsplit = attn_splits(L, k);
+  if (nsplit == 1) return 256;
+  const size_t units = (size_t)L->num_seqs * L->num_q_heads * nsplit;
   return round_up(sizeof(float) * units * 2, 256) + round_up(sizeof(float) * units * L->head_dim, 256);
+}
+
+constexpr size_t kNoAllocScratchBytes = KVS_NOALLOC_SCRATCH_BYTES;
+
+// device address of `scratch`, looked up once per device; the array's name
+// is only a host-side stand-in and is never passed to a kernel
+void* g_scratch[kMaxDevices] = {};
+
+kvs_status scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KVS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVS_ERR_UNSUPPORTED, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_err_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(KVS_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return KVS_OK;
 }
 
 }  // namespace
@@ -536,7 +572,8 @@ namespace {
 kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, const void* k_pool, const void* v_pool,
                      const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
                      const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
-                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent);
+                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent,
+                     bool noalloc = false);
 }  // namespace
 
 extern "C" {
@@ -548,6 +585,15 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attn_impl(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out,
                    workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kvs_status kvs_sparse_decode_attn_noalloc(const kvs_layout* L, int32_t table_kind, const void* q,
+                                          const void* k_pool, const void* v_pool, const float* k_scales,
+                                          const float* v_scales, const int32_t* table, const int32_t* seq_lens,
+                                          const int32_t* sel, int32_t k, float sm_scale, float* out,
+                                          void* stream) {
+  return attn_impl(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out,
+                   nullptr, 0, stream, nullptr, 0, /*noalloc=*/true);
 }
 
 kvs_status kvs_score_blocks(const kvs_layout* L, const void* q, void* summaries, const int32_t* seq_lens,
@@ -580,7 +626,10 @@ namespace {
 kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, const void* k_pool, const void* v_pool,
                      const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
                      const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
-                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent) {
+                     size_t workspace_bytes, void* stream, const double* scores, int32_t recent,
+                     bool noalloc) {
+  // noalloc: the split partials go to the library's scratch array instead
+  // of a caller's workspace (workspace and workspace_bytes are ignored)
   kvs_status st = check_layout(L, true);
   if (st != KVS_OK) return st;
   if (table_kind != KVS_TABLE_PAGED && table_kind != KVS_TABLE_HOT)
@@ -592,11 +641,22 @@ kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, con
   if (k < 1 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [1, max_blocks]");
   if (!(sm_scale == sm_scale) || sm_scale == __builtin_inff() || sm_scale == -__builtin_inff())
     return fail(KVS_ERR_INVALID_ARG, "sm_scale must be finite");
-  if (!workspace || workspace_bytes < attn_ws(L, k))
+  if (noalloc) {
+    const size_t need = attn_ws(L, k);
+    if (need > kNoAllocScratchBytes)
+      return fail(KVS_ERR_CAPACITY, "the split partials need " + std::to_string(need) +
+                                        " bytes, more than KVS_NOALLOC_SCRATCH_BYTES (" +
+                                        std::to_string(kNoAllocScratchBytes) + ")");
+  } else if (!workspace || workspace_bytes < attn_ws(L, k)) {
     return fail(KVS_ERR_INVALID_ARG, "workspace missing or smaller than kvs_attn_workspace_size()");
-  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(workspace, 16) || !aligned(q, 4) ||
+  }
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || (!noalloc && !aligned(workspace, 16)) || !aligned(q, 4) ||
       !aligned(out, 4))
     return fail(KVS_ERR_INVALID_ARG, "pools and workspace must be 16-byte aligned");
+  if (noalloc) {
+    if ((st = scratch_ptr(&workspace)) != KVS_OK) return st;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   unsigned int* err = nullptr;
   if ((st = error_word(&err)) != KVS_OK) return st;
   kvs::AttnArgs a{};

@@ -131,6 +131,7 @@ def _load():
         "kvs_select_topk": (i32, [LP, P, P, P, i32, P, P, P, sz, P]),
         "kvs_select_topk_append": (i32, [LP, P, P, P, P, P, P, i32, P, P, P, sz, P]),
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
+        "kvs_sparse_decode_attn_noalloc": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P]),
         "kvs_append_token": (i32, [LP, ctypes.POINTER(_CAppendArgs), P, P, P]),
         "kvs_score_blocks": (i32, [LP, P, P, P, ctypes.POINTER(_CSelectOpts), ctypes.POINTER(_CAppendArgs),
                                    P, P, P]),
@@ -154,7 +155,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn", "kvs_hot_lookup_swapin",
+EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn",
+            "kvs_sparse_decode_attn_noalloc", "kvs_hot_lookup_swapin",
             "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
             "kvs_build_summaries_ex", "kvs_select_uses_matrix_cores",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
@@ -385,10 +387,10 @@ def kvs_select_attn(layout: Layout, q, k_pool, v_pool, k_scales, v_scales, block
         _stream(stream)), "kvs_select_attn")
 
 
-def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,
-                           table, seq_lens, sel, k: int, sm_scale: float, out, workspace,
-                           stream=None) -> None:
-    L = layout
+def _attn_args(L: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k: int,
+               sm_scale: float, out) -> list:
+    """The checked arguments shared by the two attention entry points, from
+    table_kind through out."""
     if table_kind == KVS_TABLE_HOT:
         tile = L.block_size * L.head_dim
         tbl_n = L.num_seqs * L.num_kv_heads * L.max_blocks
@@ -397,21 +399,37 @@ def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k
         tbl_n = L.num_seqs * L.max_blocks
     qg = L.quant_group
     sc_n = L.num_pages * tile // qg if qg else None
+    return [int(table_kind),
+            _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+            _ptr(k_pool, "k_pool", _pool_dtype(L), L.num_pages * tile),
+            _ptr(v_pool, "v_pool", _pool_dtype(L), L.num_pages * tile),
+            _ptr(k_scales, "k_scales", torch.float32, sc_n),
+            _ptr(v_scales, "v_scales", torch.float32, sc_n),
+            _ptr(table, "table", torch.int32, tbl_n),
+            _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+            _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
+            int(k), float(sm_scale),
+            _ptr(out, "out", torch.float32, L.num_seqs * L.num_q_heads * L.head_dim)]
+
+
+def kvs_sparse_decode_attn(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,
+                           table, seq_lens, sel, k: int, sm_scale: float, out, workspace,
+                           stream=None) -> None:
+    L = layout
+    args = _attn_args(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out)
     _check(_lib.kvs_sparse_decode_attn(
-        ctypes.byref(L.c()), int(table_kind),
-        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
-        _ptr(k_pool, "k_pool", _pool_dtype(L), L.num_pages * tile),
-        _ptr(v_pool, "v_pool", _pool_dtype(L), L.num_pages * tile),
-        _ptr(k_scales, "k_scales", torch.float32, sc_n),
-        _ptr(v_scales, "v_scales", torch.float32, sc_n),
-        _ptr(table, "table", torch.int32, tbl_n),
-        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
-        _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
-        int(k), float(sm_scale),
-        _ptr(out, "out", torch.float32, L.num_seqs * L.num_q_heads * L.head_dim),
+        ctypes.byref(L.c()), *args,
         _ptr(workspace, "workspace", torch.uint8),
         workspace.numel() if workspace is not None else 0,
         _stream(stream)), "kvs_sparse_decode_attn")
+
+
+def kvs_sparse_decode_attn_noalloc(layout: Layout, table_kind: int, q, k_pool, v_pool, k_scales, v_scales,
+                                   table, seq_lens, sel, k: int, sm_scale: float, out, stream=None) -> None:
+    L = layout
+    args = _attn_args(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out)
+    _check(_lib.kvs_sparse_decode_attn_noalloc(ctypes.byref(L.c()), *args, _stream(stream)),
+           "kvs_sparse_decode_attn_noalloc")
 
 
 def kvs_hot_lookup_swapin(layout: Layout, sel, k: int, num_slots: int, step: int, page_table,

@@ -173,3 +173,41 @@ def test_append_and_select_ex_argument_checks(kvs):
     assert sel_ex(4, app=_append_args(kvs, v_new=None)) == kvs.KVS_ERR_INVALID_ARG
     assert sel_ex(4, kind=2) == kvs.KVS_ERR_INVALID_ARG
     assert lib.kvs_build_summaries_ex(c, 5, FAKE, None, FAKE, FAKE, None, 1, FAKE, None) == kvs.KVS_ERR_INVALID_ARG
+
+
+def test_noalloc_attention_argument_checks(kvs):
+    """The allocation-free attention entry point validates like the one with
+    a workspace, before it looks up its device array."""
+    lib = kvs.library()
+    L = _layout(kvs)
+    c = ctypes.byref(L.c())
+
+    def na(k=4, kind=0, scale=0.1, out=FAKE, layout=c):
+        return lib.kvs_sparse_decode_attn_noalloc(layout, kind, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                                  k, scale, out, None)
+    assert na(k=0) == kvs.KVS_ERR_INVALID_ARG
+    assert na(k=17) == kvs.KVS_ERR_INVALID_ARG
+    assert na(kind=2) == kvs.KVS_ERR_INVALID_ARG
+    assert na(scale=float("nan")) == kvs.KVS_ERR_INVALID_ARG
+    assert na(out=None) == kvs.KVS_ERR_INVALID_ARG
+    assert na(layout=ctypes.byref(_layout(kvs, head_dim=96).c())) == kvs.KVS_ERR_UNSUPPORTED
+
+
+def test_attention_workspace_bounded_for_every_split_count(kvs):
+    """Several splits per unit only while sequences x KV heads < 256, so the
+    split partials of every accepted layout fit the no-allocation entry
+    point's device array (KVS_NOALLOC_SCRATCH_BYTES = 8 MiB)."""
+    worst = 0
+    for B in (1, 2, 3, 5, 8, 16, 31, 32, 63, 64, 100, 127, 128, 255, 256, 1024):
+        for Hkv in (1, 2, 4, 8):
+            for G in (1, 4, 16):
+                for k in (1, 2, 7, 64, 128, 512):
+                    L = _layout(kvs, num_seqs=B, num_kv_heads=Hkv, num_q_heads=G * Hkv, max_blocks=512)
+                    n = kvs.kvs_attn_num_splits(L, k)
+                    ws = kvs.kvs_attn_workspace_size(L, k)
+                    if n == 1:
+                        assert ws == 256
+                    else:
+                        assert B * Hkv < 256
+                    worst = max(worst, ws)
+    assert worst <= (17 << 18)  # 4.25 MiB
