@@ -27,14 +27,27 @@ class OracleError(RuntimeError):
     pass
 
 
-def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB):
+# A process may load another build of the same source instead (the
+# sanitizer build below), named by this environment variable.
+_LIB_ENV = "ORACLE_LIB"
+
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: str | None = None) -> str:
+    """Compile liboracle.so with gcc (no fast-math, no FP contraction).  With
+    sanitize, an AddressSanitizer + UndefinedBehaviorSanitizer build (same
+    arithmetic flags) goes to `out` instead; a process loads it by naming it
+    in ORACLE_LIB, with gcc's libasan preloaded."""
+    target = out if out else _LIB
+    if force or not os.path.exists(target):
         cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-Wall", "-Wextra", "-o", _LIB + ".tmp", _SRC, "-lm"]
+               "-fno-fast-math", "-Wall", "-Wextra", *(SANITIZE_FLAGS if sanitize else []),
+               "-o", target + ".tmp", _SRC, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+        os.replace(target + ".tmp", target)
+    return target
 
 
 class _Layout(ctypes.Structure):
@@ -48,9 +61,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        path = os.environ.get(_LIB_ENV) or _LIB
+        if path == _LIB and not os.path.exists(_LIB):
             build()
-        L = ctypes.CDLL(_LIB)
+        L = ctypes.CDLL(path)
         P = ctypes.c_void_p
         i32, i64, f64 = ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         LP = ctypes.POINTER(_Layout)
