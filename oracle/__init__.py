@@ -78,6 +78,7 @@ def lib():
             "or_select": (ctypes.c_int, [LP, P, P, i32, P]),
             "or_select_window": (ctypes.c_int, [LP, P, P, i32, i32, P]),
             "or_ema_scores": (ctypes.c_int, [LP, P, P, f64, P, P]),
+            "or_fuse_scores": (ctypes.c_int, [LP, P, i32, P, P]),
             "or_append_token": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
             "or_summaries_mean": (ctypes.c_int, [LP, P, P, P, P, P, i32, P]),
             "or_mean_scores": (ctypes.c_int, [LP, P, P, P, P, P]),
@@ -233,6 +234,19 @@ def ema_scores(L: Layout, W, seq_lens, alpha, state):
     out = np.empty((L.B, L.Hkv, L.max_blocks), dtype=np.float64)
     _check(lib().or_ema_scores(ctypes.byref(L.c()), _ptr(W), _ptr(sl), float(alpha), _ptr(state),
                                _ptr(out)), "or_ema_scores")
+    return out
+
+
+def fuse_scores(L: Layout, W_layers, seq_lens):
+    """Sum of several layers' scores, left to right in fp64 (-inf past each
+    sequence's blocks); W_layers is a list (or [n][B][Hkv][max_blocks]
+    array) of per-layer scores."""
+    arrs = [np.asarray(w, dtype=np.float64) for w in W_layers]
+    W = np.ascontiguousarray(np.stack(arrs)) if arrs else np.zeros((0, L.B, L.Hkv, L.max_blocks))
+    sl = _c(seq_lens, np.int32)
+    out = np.empty((L.B, L.Hkv, L.max_blocks), dtype=np.float64)
+    _check(lib().or_fuse_scores(ctypes.byref(L.c()), _ptr(W), W.shape[0], _ptr(sl), _ptr(out)),
+           "or_fuse_scores")
     return out
 
 

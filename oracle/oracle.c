@@ -307,6 +307,30 @@ int or_ema_scores(const or_layout* L, const double* W, const int32_t* seq_lens,
   return OR_OK;
 }
 
+int or_fuse_scores(const or_layout* L, const double* W, int32_t n_layers,
+                   const int32_t* seq_lens, double* out) {
+  if (!layout_ok(L) || !W || !seq_lens || !out || n_layers < 1) return OR_EARG;
+  const int64_t layer_stride = (int64_t)L->B * L->Hkv * L->max_blocks;
+  for (int32_t b = 0; b < L->B; ++b) {
+    int32_t len = seq_lens[b];
+    if (!len_ok(L, len)) return OR_ERANGE;
+    int32_t nb = num_blocks(L, len);
+    for (int32_t g = 0; g < L->Hkv; ++g) {
+      int64_t row = ((int64_t)b * L->Hkv + g) * L->max_blocks;
+      for (int32_t j = 0; j < L->max_blocks; ++j) {
+        if (j >= nb) {
+          out[row + j] = -INFINITY;
+          continue;
+        }
+        double s = W[row + j];  /* the first layer's score */
+        for (int32_t l = 1; l < n_layers; ++l) s = s + W[l * layer_stride + row + j];
+        out[row + j] = s;
+      }
+    }
+  }
+  return OR_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* attention                                                           */
 /* ------------------------------------------------------------------ */

@@ -125,6 +125,18 @@ int or_select_window(const or_layout* L, const double* W, const int32_t* seq_len
 int or_ema_scores(const or_layout* L, const double* W, const int32_t* seq_lens,
                   double alpha, double* state, double* Wout);
 
+/* Cross-layer score fusion ("SparDA：把KV選擇提前一層…" §3.1 and §4.1: a
+ * few shallow layers score the history, their scores are fused into one
+ * mask, and every deeper layer gathers the K/V that mask names).  The
+ * fused score of (b, g, j) is the sum of the n_layers layers' scores,
+ * added left to right in fp64:
+ *   out[b][g][j] = (...((W[0][b][g][j] + W[1][b][g][j]) + W[2][b][g][j]) ...)
+ * for j < nb_b, -inf beyond.  W is [n_layers][B][Hkv][max_blocks] (each
+ * layer's scores as or_bounds / or_ema_scores / or_mean_scores give them),
+ * out is [B][Hkv][max_blocks]; n_layers >= 1. */
+int or_fuse_scores(const or_layout* L, const double* W, int32_t n_layers,
+                   const int32_t* seq_lens, double* out);
+
 /* Softmax attention of every query head over the tokens of its group's
  * selected blocks (t < len only), two passes (max, then sums):
  *   s_t = sm_scale * q_h . K_t ;  out_h = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m)

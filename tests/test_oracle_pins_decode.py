@@ -348,3 +348,79 @@ def test_mean_score_never_exceeds_the_box_bound(orc):
                 blk = c["valk"][b, h // G, j * S: min((j + 1) * S, n)]
                 est = q[b, h] @ blk.mean(axis=0)
                 assert abs(Um[b, h, j] - est) <= 1e-6 * (1 + abs(est))
+
+
+# ---------------------------------------------------------------------------
+# cross-layer score fusion ("SparDA…" §3.1, §4.1)
+# ---------------------------------------------------------------------------
+
+def _fuse_layout(orc, B=3, Hkv=2, MB=9, S=16):
+    return orc.Layout(B, 2 * Hkv, Hkv, 8, S, MB, B * MB, orc.KV_F32)
+
+
+def test_fused_score_of_integer_multiples_is_their_sum(orc):
+    """Layers whose scores are 1x, 2x and 4x one integer-valued base (all
+    sums exact in fp64) fuse to exactly 7x the base, entry by entry: a
+    dropped or repeated layer, a max instead of a sum, or a wrong layer,
+    sequence or head stride gives another multiple somewhere."""
+    L = _fuse_layout(orc)
+    rng = np.random.default_rng(41)
+    base = rng.integers(-5000, 5000, size=(L.B, L.Hkv, L.max_blocks)).astype(np.float64)
+    lens = np.array([L.max_blocks * L.S, 5 * L.S - 3, 1], np.int32)
+    F = orc.fuse_scores(L, [base, 2 * base, 4 * base], lens)
+    for b, n in enumerate(lens):
+        nb = (int(n) + L.S - 1) // L.S
+        assert np.array_equal(F[b, :, :nb], 7 * base[b, :, :nb])
+        assert np.isneginf(F[b, :, nb:]).all()
+    # one layer: its own scores (up to nb), the selection it gives unchanged
+    F1 = orc.fuse_scores(L, [base], lens)
+    W = base.copy()
+    for b, n in enumerate(lens):
+        W[b, :, (int(n) + L.S - 1) // L.S:] = -np.inf
+    assert np.array_equal(F1, W)
+    assert np.array_equal(orc.select(L, F1, lens, 4), orc.select(L, W, lens, 4))
+
+
+def test_fused_score_adds_left_to_right(orc):
+    """fp64 addition is not associative: with a = 1, b = 2^-53, c = 2^-53 the
+    left-to-right sum (a + b) + c rounds to 1 twice, a + (b + c) does not.
+    The fusion adds the layers in ascending order."""
+    L = _fuse_layout(orc, B=1, Hkv=1, MB=1, S=4)
+    lens = np.array([4], np.int32)
+    one = np.ones((1, 1, 1))
+    tiny = np.full((1, 1, 1), 2.0 ** -53)
+    F = orc.fuse_scores(L, [one, tiny, tiny], lens)
+    assert F[0, 0, 0] == 1.0
+    F = orc.fuse_scores(L, [tiny, tiny, one], lens)
+    assert F[0, 0, 0] == 1.0 + 2.0 ** -52
+
+
+def test_fused_selection_respects_dominance(orc):
+    """A block that scores at least as high as another in every layer is
+    fused at least as high: if it is a free candidate and the other one is
+    selected, it is selected too."""
+    L = _fuse_layout(orc, B=2, Hkv=2, MB=40, S=16)
+    rng = np.random.default_rng(43)
+    lens = np.array([40 * 16, 33 * 16 - 5], np.int32)
+    layers = [rng.normal(size=(L.B, L.Hkv, L.max_blocks)) * 10 for _ in range(3)]
+    # block 7 dominates block 20 in every layer
+    for w in layers:
+        w[:, :, 7] = np.maximum(w[:, :, 7], w[:, :, 20] + 0.5)
+    F = orc.fuse_scores(L, layers, lens)
+    assert (F[:, :, 7] >= F[:, :, 20]).all()
+    for k in range(3, 30):
+        sel = orc.select(L, F, lens, k)
+        for b in range(L.B):
+            for g in range(L.Hkv):
+                s = set(sel[b, g][sel[b, g] >= 0].tolist())
+                if 20 in s:
+                    assert 7 in s
+
+
+def test_fuse_rejects_bad_arguments(orc):
+    L = _fuse_layout(orc)
+    W = np.zeros((1, L.B, L.Hkv, L.max_blocks))
+    with pytest.raises(orc.OracleError):
+        orc.fuse_scores(L, W[:0], np.zeros(L.B, np.int32))  # no layers
+    with pytest.raises(orc.OracleError):
+        orc.fuse_scores(L, W, np.full(L.B, 10 ** 6, np.int32))  # length past the table
