@@ -82,6 +82,8 @@ def main(argv=None) -> int:
     ap.add_argument("--prefetch", action="store_true",
                     help="hot-buffer workload: swap in the next layer's misses on a second stream while the "
                          "current layer attends (selections known one layer ahead)")
+    ap.add_argument("--copy-ahead", type=int, default=2, choices=(1, 2),
+                    help="hot-buffer prefetch: copies issued 1 or 2 layers ahead (page-table steps 2 ahead)")
     ap.add_argument("--selection-study", action="store_true",
                     help="instead of the step benchmark: selection churn and hot-buffer misses over a "
                          "drifting query, plain / smoothed / recent window / both (one JSON line)")
@@ -89,6 +91,9 @@ def main(argv=None) -> int:
                     help="time the step with the top-k as a launch of its own (kvs_select_topk_ex + "
                          "kvs_sparse_decode_attn) instead of inside the attention launch")
     ap.add_argument("--cpu-steps", type=int, default=6, help="layer-steps in the CPU oracle sample (about 2 s each)")
+    ap.add_argument("--reuse", type=int, default=0, metavar="P",
+                    help="also time a decode step over all layer instances that selects once: layers 0..P-1 "
+                         "score (fused) and select, every other layer attends over that selection")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
@@ -260,6 +265,7 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} layer-steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     t_step, wall_step = timed(step_graphs, args.steps, args.warmup)
+    phase = {"step_sweep_us": t_step / args.steps * 1e6}
     # distribution: every layer-step graph replayed alone between two HIP
     # events (the sweep above is the throughput figure; these include the
     # launch of one graph and one event pair per step)
@@ -278,17 +284,19 @@ def main(argv=None) -> int:
     # the token append with the selection as the step runs it, the selection
     # alone (the append's cost is the difference), and the selection with a
     # rebuild of the newest block's summary from its K tile instead
-    phase = {}
     for name, fn in (("score_blocks", run_score), ("select_attn", run_select_attn),
                      ("mean_summaries_step", run_score_mean),
                      ("append_select", run_append_select), ("select_topk_only", run_select),
                      ("select_topk_rebuild", run_select_append), ("attention", run_attn)):
         t, _ = timed(capture(fn), args.steps, args.warmup)
-        phase[name] = t / args.steps
+        phase[name] = t / args.steps * 1e6
+    reuse = None
+    if args.reuse > 0:
+        reuse = time_reuse(args, w, L, layers, steps, n_layers, capture, timed, phase)
     # the roofline entry is for the step's dominant call: the attention with
     # its own selection (or, with --separate-topk, the attention alone)
     fused = not args.separate_topk and not matrix_cores and args.parts == 1
-    t_attn = phase["select_attn" if fused else "attention"] * args.steps
+    t_attn = phase["select_attn" if fused else "attention"] * 1e-6 * args.steps
     torch.cuda.synchronize()
     assert kvs.kvs_device_errors() == 0, "kernels raised device error flags"
 
@@ -333,7 +341,7 @@ def main(argv=None) -> int:
                    "kv_storage": w.kv_dtype, "q_storage": w.q_dtype, "layer_instances": n_layers,
                    "graph_replay": True, "concurrent_batch_slices": len(steps[0].slices),
                    "topk": "inside the attention launch" if fused else "separate launch"},
-        "phase_us": {k: round(v * 1e6, 3) for k, v in phase.items()},
+        "phase_us": {k: round(v, 3) for k, v in phase.items() if k != "step_sweep_us"},
         "step_us_percentiles": pct,
         "step_bytes": by["step"],
         "step_GBps": round(step_gbps, 1),
@@ -347,10 +355,44 @@ def main(argv=None) -> int:
                      "bytes_per_launch": attn_bytes, "us_per_launch": round(attn_sec * 1e6, 3)},
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "cross_layer_reuse": reuse,
         "wall_s_timed_region": round(wall_step, 4),
     }
     print(json.dumps(result), flush=True)
     return 0
+
+
+def time_reuse(args, w, L, layers, steps, n_layers, capture, timed, phase) -> dict:
+    """Cross-layer selection reuse ("SparDA…" §3.1, §4.1): one decode step
+    over all layer instances, in order, where layers 0..P-1 add their block
+    scores into one fused score and attend over its top-k, and every other
+    layer appends its token and attends over that selection without reading
+    its summaries.  Timed as whole model steps (graph sweeps), reported per
+    layer beside the step without reuse."""
+    from query_aware_sparse_kvs_amd.step import CrossLayerDecode
+    P = min(args.reuse, n_layers)
+    cl = CrossLayerDecode(L, w.k, n_layers, P, steps[0].sel.device)
+
+    def run_layer(i):
+        d = layers[i]
+        inp = d["inp"]
+        cl.layer(i, inp["q"], d["tok"], inp["seq_lens"], d["summ"])
+
+    model_steps = max(1, args.steps // n_layers)
+    K, W = model_steps * n_layers, max(1, args.warmup // n_layers) * n_layers
+    t, _ = timed(capture(run_layer), K, W)
+    per_layer = t / K
+    summ_elem = 2 if w.kv_dtype == "bf16" else 4
+    kv_elem = {"f32": 4, "bf16": 2, "e4m3": 1}[w.kv_dtype]
+    by = algorithmic_bytes(w, summ_elem, kv_elem, 4 if w.q_dtype == "f32" else 2)
+    # deeper layers read no summaries
+    model_bytes = n_layers * by["step"] - (n_layers - P) * by["summaries"]
+    full = phase.get("step_sweep_us")
+    return {"predictor_layers": P, "layers": n_layers, "model_steps_timed": model_steps,
+            "us_per_layer": round(per_layer * 1e6, 3),
+            "query_tokens_per_s_per_layer": round(w.B / per_layer, 1),
+            "GBps": round(model_bytes / n_layers / per_layer / 1e9, 1),
+            "us_per_layer_without_reuse": None if full is None else round(full, 3)}
 
 
 def bench_hot(args, w, dev) -> int:
@@ -429,24 +471,14 @@ def bench_hot(args, w, dev) -> int:
     t_pipe = None
     if args.prefetch:
         from query_aware_sparse_kvs_amd.step import HotPrefetchPipeline
-        pipe = HotPrefetchPipeline(hs, dev)
-        nxt = {"i": 0}
-
-        def prefetch(i):
-            h_i = i % n_layers
-            t = m[h_i]
-            pipe.prefetch(h_i, t, sels[t], *host)
+        pipe = HotPrefetchPipeline(hs, dev, copy_ahead=args.copy_ahead)
+        base = list(m)  # each buffer's next stream entry
+        layer_of = lambda i: i % n_layers
+        index_of = lambda i: base[i % n_layers] + i // n_layers
+        lookup_args = lambda i: (index_of(i), sels[index_of(i)])
 
         def piped(i):  # layer i attends while layer i+1's misses come in
-            if nxt["i"] <= i:
-                prefetch(i)
-                nxt["i"] = i + 1
-            prefetch(i + 1)
-            nxt["i"] = i + 2
-            h_i = i % n_layers
-            t = m[h_i]
-            pipe.attend(h_i, inp["q"], sels[t], inp["seq_lens"])
-            m[h_i] += 1
+            pipe.step(i, layer_of, lookup_args, host, inp["q"], sels[index_of(i)], inp["seq_lens"])
 
         t_pipe = timed(piped)
         torch.cuda.synchronize()

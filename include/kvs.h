@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 3
+#define KVS_ABI_VERSION 4
 
 typedef enum kvs_status {
   KVS_OK = 0,
@@ -311,7 +311,11 @@ kvs_status kvs_append_token(const kvs_layout* layout, const kvs_append_args* app
  *               mean summaries an append writes the token and then rebuilds
  *               its block's mean from the pool (a launch each), and scoring is
  *               always the exact path.
- *  opts = NULL  R = 1, no smoothing, min/max summaries.
+ *  opts->accumulate  0, or (kvs_score_blocks only) 1: add this call's
+ *               scores to the ones already in `scores` instead of
+ *               overwriting them (cross-layer fusion, see kvs_score_blocks);
+ *               kvs_select_topk_ex rejects 1 with INVALID_ARG.
+ *  opts = NULL  R = 1, no smoothing, min/max summaries, no accumulation.
  *  append       NULL, or the token append of kvs_append_token (same
  *               arguments), done before the blocks are scored.  Without
  *               bounds_out and smoothing it runs inside the scoring launch,
@@ -330,6 +334,7 @@ typedef struct kvs_select_opts {
   double ema_alpha;
   double* ema_state;
   int32_t summary_kind;  /* KVS_SUMM_MINMAX (the box bound) or KVS_SUMM_MEAN */
+  int32_t accumulate;    /* kvs_score_blocks only; see there */
 } kvs_select_opts;
 
 kvs_status kvs_select_topk_ex(const kvs_layout* layout, const void* q, void* summaries,
@@ -412,6 +417,16 @@ kvs_status kvs_sparse_decode_attn_noalloc(const kvs_layout* layout, int32_t tabl
  * time: that one entry is unspecified (the block is always kept, so no
  * selection reads it).
  *
+ * Cross-layer fusion ("SparDA…" §3.1 and §4.1: a few shallow layers score
+ * the history, their scores are fused into one mask, and every deeper layer
+ * gathers the K/V that mask names): with opts->accumulate = 1,
+ *     scores[b][g][j] = scores[b][g][j] + (this layer's score)
+ * for j < nb(b) (one fp64 add, after the smoothing when that is on; -inf
+ * beyond nb(b)), so predictor layers 0..P-1 called with accumulate = 0, 1,
+ * ..., 1 leave the sum of their scores, added in layer order.  Deeper
+ * layers skip scoring: kvs_select_attn on that sum selects once, and
+ * kvs_sparse_decode_attn reuses the selection in every further layer.
+ *
  * kvs_select_attn selects, per (b, g), the blocks kvs_select_topk_ex would
  * select from those scores (sink, the recent_blocks newest blocks, the best
  * of the rest), writes that selection to sel [B][Hkv][k], and returns the
@@ -490,6 +505,40 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, i
                                  const float* host_v_scales, void* hot_k, void* hot_v,
                                  float* hot_k_scales, float* hot_v_scales, int32_t* miss_list,
                                  int32_t* miss_count, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_hot_lookup + kvs_hot_swapin -- the two halves of kvs_hot_lookup_swapin
+ *
+ * Same page ("KV 稀疏化", §7 "HiSparse"): the table also notes that misses
+ * land on the decode critical path.  Split in two so that a caller can take
+ * the page-table step (steps 1-3 above: hits, the miss list, LRU victims)
+ * for one layer's hot buffer and run the host-link copy (step 4) on
+ * another stream, overlapped with other work ("分块稀疏注意力与KV Cache量化…"
+ * §5.3: wider prefetch during decode).  kvs_hot_lookup followed by
+ * kvs_hot_swapin with the same page_table, miss_list and miss_count gives
+ * exactly kvs_hot_lookup_swapin.
+ *
+ * kvs_hot_lookup: arguments as kvs_hot_lookup_swapin without the pools; it
+ *   leaves page_table, slot_owner, slot_stamp, miss_list and miss_count as
+ *   kvs_hot_lookup_swapin does.
+ * kvs_hot_swapin: copies, for every unit u, the first miss_count[u] blocks
+ *   of miss_list[u] from the host tier into the slot page_table[u][j] gives
+ *   them (K and V tiles and fp8 scales, byte for byte).  A listed block
+ *   whose page-table entry is not one of the unit's slots is skipped with
+ *   KVS_DEVERR_TABLE; counts are clamped to [0, k].  It must run after the
+ *   kvs_hot_lookup that wrote the list and before anything changes the page
+ *   table, and before the attention that reads the slots.
+ * Errors: as kvs_hot_lookup_swapin.
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_hot_lookup(const kvs_layout* layout, const int32_t* sel, int32_t k, int32_t num_slots,
+                          int64_t step, int32_t* page_table, int32_t* slot_owner, int64_t* slot_stamp,
+                          int32_t* miss_list, int32_t* miss_count, void* stream);
+
+kvs_status kvs_hot_swapin(const kvs_layout* layout, int32_t k, int32_t num_slots,
+                          const int32_t* page_table, const int32_t* miss_list,
+                          const int32_t* miss_count, const void* host_k, const void* host_v,
+                          const float* host_k_scales, const float* host_v_scales, void* hot_k,
+                          void* hot_v, float* hot_k_scales, float* hot_v_scales, void* stream);
 
 /* Workspace bytes needed by kvs_select_topk / kvs_sparse_decode_attn for this
  * layout and k; 0 when the layout or k is invalid. */

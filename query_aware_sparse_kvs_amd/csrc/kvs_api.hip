@@ -337,6 +337,7 @@ struct SelectOpts {
   double alpha = 1.0;
   double* state = nullptr;
   int kind = KVS_SUMM_MINMAX;
+  bool accumulate = false;
 };
 
 SelectOpts opts_of(const kvs_select_opts* opts) {
@@ -347,6 +348,7 @@ SelectOpts opts_of(const kvs_select_opts* opts) {
     o.alpha = opts->ema_alpha;
     o.state = opts->ema_state;
     o.kind = opts->summary_kind;
+    o.accumulate = opts->accumulate != 0;
   }
   return o;
 }
@@ -378,6 +380,8 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
     return fail(KVS_ERR_INVALID_ARG, "smoothing needs an 8-byte aligned ema_state and 0 <= ema_alpha <= 1");
   if (opt.kind != KVS_SUMM_MINMAX && opt.kind != KVS_SUMM_MEAN)
     return fail(KVS_ERR_INVALID_ARG, "unknown summary_kind");
+  if (opt.accumulate && !scores_out)
+    return fail(KVS_ERR_INVALID_ARG, "accumulate applies to kvs_score_blocks only");
   const bool mean = opt.kind == KVS_SUMM_MEAN;
   if (mean && app) return fail(KVS_ERR_UNSUPPORTED, "the newest-block rebuild call keeps min/max summaries");
   if (!aligned(summaries, 16) || (workspace && !aligned(workspace, 16)) || (bounds_out && !aligned(bounds_out, 8)))
@@ -485,6 +489,7 @@ kvs_status select_impl(const kvs_layout* L, const void* q, const void* summaries
   ba.ema_alpha = opt.alpha;
   ba.ema_beta = 1.0 - opt.alpha;
   ba.ema_state = opt.state;
+  ba.accumulate = opt.accumulate ? 1 : 0;
   hipError_t e = kvs::launch_bounds(ba, kind_of(L->q_dtype), summ_kind, s);
   if (e != hipSuccess || scores_out) return hip_status(e, "bounds launch");
   kvs::TopkArgs ta{};
@@ -719,19 +724,26 @@ kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, con
 
 extern "C" {
 
-kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots,
-                                 int64_t step, int32_t* page_table, int32_t* slot_owner,
-                                 int64_t* slot_stamp, const void* host_k, const void* host_v,
-                                 const float* host_k_scales, const float* host_v_scales, void* hot_k,
-                                 void* hot_v, float* hot_k_scales, float* hot_v_scales,
-                                 int32_t* miss_list, int32_t* miss_count, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The hot-buffer calls: `phases` = kvs::kHotLookup (page-table step, miss
+// list) and/or kvs::kHotCopy (copy of the listed misses); the pointers a
+// phase does not use may be NULL.
+kvs_status hot_impl(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots, int64_t step,
+                    int32_t* page_table, int32_t* slot_owner, int64_t* slot_stamp, const void* host_k,
+                    const void* host_v, const float* host_k_scales, const float* host_v_scales, void* hot_k,
+                    void* hot_v, float* hot_k_scales, float* hot_v_scales, int32_t* miss_list,
+                    int32_t* miss_count, void* stream, int phases) {
+  const bool lookup = phases & kvs::kHotLookup, copy = phases & kvs::kHotCopy;
   kvs_status st = check_layout(L, false);
   if (st != KVS_OK) return st;
-  if (!sel || !page_table || !slot_owner || !slot_stamp || !host_k || !host_v || !hot_k || !hot_v ||
-      !miss_list || !miss_count)
+  if (!page_table || !miss_list || !miss_count || (lookup && (!sel || !slot_owner || !slot_stamp)) ||
+      (copy && (!host_k || !host_v || !hot_k || !hot_v)))
     return fail(KVS_ERR_INVALID_ARG, "a required pointer is NULL");
   const bool fp8 = L->kv_dtype == KVS_FP8_E4M3;
-  if (fp8 && (!host_k_scales || !host_v_scales || !hot_k_scales || !hot_v_scales))
+  if (copy && fp8 && (!host_k_scales || !host_v_scales || !hot_k_scales || !hot_v_scales))
     return fail(KVS_ERR_INVALID_ARG, "fp8 pools need host and hot scales");
   if (num_slots < 1 || num_slots > 4096) return fail(KVS_ERR_UNSUPPORTED, "num_slots must be in [1, 4096]");
   if (k < 1 || k > L->max_blocks) return fail(KVS_ERR_INVALID_ARG, "k must be in [1, max_blocks]");
@@ -739,12 +751,12 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_
   if (step < 0 || step >= (1ll << 50)) return fail(KVS_ERR_INVALID_ARG, "step must be in [0, 2^50)");
   if ((long long)L->num_seqs * L->num_kv_heads * num_slots > 0x7FFFFFFFll)
     return fail(KVS_ERR_INVALID_ARG, "total hot slots overflow int32");
-  if (!aligned(host_k, 16) || !aligned(host_v, 16) || !aligned(hot_k, 16) || !aligned(hot_v, 16))
+  if (copy && (!aligned(host_k, 16) || !aligned(host_v, 16) || !aligned(hot_k, 16) || !aligned(hot_v, 16)))
     return fail(KVS_ERR_INVALID_ARG, "host and hot pools must be 16-byte aligned");
   // device aliases of the pinned host tier (hipHostMalloc memory is mapped)
   const void* host_ptrs[4] = {host_k, host_v, host_k_scales, host_v_scales};
   void* dev_ptrs[4] = {nullptr, nullptr, nullptr, nullptr};
-  for (int i = 0; i < (fp8 ? 4 : 2); ++i) {
+  for (int i = 0; copy && i < (fp8 ? 4 : 2); ++i) {
     hipError_t e = hipHostGetDevicePointer(&dev_ptrs[i], const_cast<void*>(host_ptrs[i]), 0);
     if (e != hipSuccess || !dev_ptrs[i]) {
       (void)hipGetLastError();
@@ -782,7 +794,39 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_
   a.n2 = n2 < 2 ? 2 : n2;
   a.qg = fp8 ? L->quant_group : 0;
   a.elem_bytes = (int)elem_size(L->kv_dtype);
-  return hip_status(kvs::launch_hot(a, static_cast<hipStream_t>(stream)), "hot-buffer launch");
+  return hip_status(kvs::launch_hot(a, phases, static_cast<hipStream_t>(stream)), "hot-buffer launch");
+}
+
+
+}  // namespace
+
+extern "C" {
+
+kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots,
+                                 int64_t step, int32_t* page_table, int32_t* slot_owner,
+                                 int64_t* slot_stamp, const void* host_k, const void* host_v,
+                                 const float* host_k_scales, const float* host_v_scales, void* hot_k,
+                                 void* hot_v, float* hot_k_scales, float* hot_v_scales,
+                                 int32_t* miss_list, int32_t* miss_count, void* stream) {
+  return hot_impl(L, sel, k, num_slots, step, page_table, slot_owner, slot_stamp, host_k, host_v, host_k_scales,
+                  host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, miss_list, miss_count, stream,
+                  kvs::kHotLookup | kvs::kHotCopy);
+}
+
+kvs_status kvs_hot_lookup(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t num_slots, int64_t step,
+                          int32_t* page_table, int32_t* slot_owner, int64_t* slot_stamp, int32_t* miss_list,
+                          int32_t* miss_count, void* stream) {
+  return hot_impl(L, sel, k, num_slots, step, page_table, slot_owner, slot_stamp, nullptr, nullptr, nullptr,
+                  nullptr, nullptr, nullptr, nullptr, nullptr, miss_list, miss_count, stream, kvs::kHotLookup);
+}
+
+kvs_status kvs_hot_swapin(const kvs_layout* L, int32_t k, int32_t num_slots, const int32_t* page_table,
+                          const int32_t* miss_list, const int32_t* miss_count, const void* host_k,
+                          const void* host_v, const float* host_k_scales, const float* host_v_scales,
+                          void* hot_k, void* hot_v, float* hot_k_scales, float* hot_v_scales, void* stream) {
+  return hot_impl(L, nullptr, k, num_slots, 0, const_cast<int32_t*>(page_table), nullptr, nullptr, host_k, host_v,
+                  host_k_scales, host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales,
+                  const_cast<int32_t*>(miss_list), const_cast<int32_t*>(miss_count), stream, kvs::kHotCopy);
 }
 
 }  // extern "C"

@@ -208,14 +208,17 @@ __global__ __launch_bounds__(256) void swapin_copy_kernel(HotArgs a) {
 
 }  // namespace
 
-hipError_t launch_hot(const HotArgs& a, hipStream_t s) {
+hipError_t launch_hot(const HotArgs& a, int phases, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
   const int units = a.B * a.Hkv;
-  const size_t lds = sizeof(unsigned long long) * (size_t)a.n2 + sizeof(unsigned int) * (size_t)((a.MB + 31) / 32);
-  hipLaunchKernelGGL(hot_lookup_kernel, dim3((unsigned)units), dim3(256), lds, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(swapin_copy_kernel, dim3((unsigned)kCopyGroups, (unsigned)units), dim3(256), 0, s, a);
+  if (phases & kHotLookup) {
+    const size_t lds = sizeof(unsigned long long) * (size_t)a.n2 + sizeof(unsigned int) * (size_t)((a.MB + 31) / 32);
+    hipLaunchKernelGGL(hot_lookup_kernel, dim3((unsigned)units), dim3(256), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (phases & kHotCopy)
+    hipLaunchKernelGGL(swapin_copy_kernel, dim3((unsigned)kCopyGroups, (unsigned)units), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

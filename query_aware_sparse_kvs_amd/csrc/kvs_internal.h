@@ -168,6 +168,8 @@ struct BoundArgs {
   double ema_alpha;    // weight of this step's score
   double ema_beta;     // 1 - ema_alpha (fp64)
   double* ema_state;   // [B][Hkv][MB] in/out, NaN = no history
+  int32_t accumulate;  // 1: W[j] = W[j] + this launch's score (cross-layer
+                       // fusion), for j < nb; W holds the earlier layers' sum
 };
 
 struct TopkArgs {
@@ -248,7 +250,10 @@ hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s);
 // whether launch_attn can run this shape in self-selecting mode
 bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k);
-hipError_t launch_hot(const HotArgs& a, hipStream_t s);
+// hot-buffer phases: the page-table step (hits, miss list, LRU victims) and
+// the copy of the listed misses from the host tier
+constexpr int kHotLookup = 1, kHotCopy = 2;
+hipError_t launch_hot(const HotArgs& a, int phases, hipStream_t s);
 
 // attention split heuristic shared by the launcher and the workspace query
 int attn_num_splits(int units, int k);

@@ -24,6 +24,9 @@
 //
 // With score smoothing on, the bounds kernel ranks blocks by the smoothed
 // score alpha*W + (1-alpha)*history ("SparDA…" §6.1) instead of W itself.
+// With accumulation on, it adds the (smoothed) score to the sum of earlier
+// layers' scores already in the output ("SparDA…" §3.1, §4.1: a few shallow
+// layers' scores fused into one mask for the deeper layers).
 #include "kvs_append.h"
 #include "kvs_summarize.h"
 #include "kvs_topk.h"
@@ -249,6 +252,7 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     const long long wi = ((long long)b * a.Hkv + g) * a.MB + j0 + lane;
     if (a.bounds_out) a.bounds_out[wi] = w;
     if (a.ema && valid) w = smooth_score(w, a.ema_state + wi, a.ema_alpha, a.ema_beta);
+    if (a.accumulate && valid) w = a.W[wi] + w;  // the earlier layers' sum first
     a.W[wi] = w;
   }
 }

@@ -83,7 +83,7 @@ class _CAppendArgs(ctypes.Structure):
 class _CSelectOpts(ctypes.Structure):
     _fields_ = [("recent_blocks", ctypes.c_int32), ("use_ema", ctypes.c_int32),
                 ("ema_alpha", ctypes.c_double), ("ema_state", ctypes.c_void_p),
-                ("summary_kind", ctypes.c_int32)]
+                ("summary_kind", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
 
 
 KVS_SUMM_MINMAX, KVS_SUMM_MEAN = 0, 1
@@ -110,12 +110,14 @@ class AppendArgs:
 
 @dataclass
 class SelectOpts:
-    """kvs_select_opts: recent window, score smoothing, summary kind."""
+    """kvs_select_opts: recent window, score smoothing, summary kind,
+    cross-layer accumulation (kvs_score_blocks)."""
     recent_blocks: int = 1
     use_ema: bool = False
     ema_alpha: float = 0.7
     ema_state: torch.Tensor | None = None
     summary_kind: int = 0  # KVS_SUMM_MINMAX or KVS_SUMM_MEAN
+    accumulate: bool = False
 
 
 def _load():
@@ -139,6 +141,8 @@ def _load():
         "kvs_select_topk_ex": (i32, [LP, P, P, P, i32, ctypes.POINTER(_CSelectOpts),
                                      ctypes.POINTER(_CAppendArgs), P, P, P, sz, P]),
         "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "kvs_hot_lookup": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P]),
+        "kvs_hot_swapin": (i32, [LP, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvs_select_workspace_size": (sz, [LP, i32]),
         "kvs_attn_workspace_size": (sz, [LP, i32]),
         "kvs_attn_num_splits": (i32, [LP, i32]),
@@ -156,7 +160,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn",
-            "kvs_sparse_decode_attn_noalloc", "kvs_hot_lookup_swapin",
+            "kvs_sparse_decode_attn_noalloc", "kvs_hot_lookup_swapin", "kvs_hot_lookup", "kvs_hot_swapin",
             "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
             "kvs_build_summaries_ex", "kvs_select_uses_matrix_cores",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
@@ -337,7 +341,7 @@ def _opts_struct(L: Layout, opts: SelectOpts | None):
         return None
     return _CSelectOpts(int(opts.recent_blocks), 1 if opts.use_ema else 0, float(opts.ema_alpha),
                         _ptr(opts.ema_state, "ema_state", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
-                        int(opts.summary_kind))
+                        int(opts.summary_kind), 1 if opts.accumulate else 0)
 
 
 def _kind(opts: SelectOpts | None) -> int:
@@ -459,6 +463,45 @@ def kvs_hot_lookup_swapin(layout: Layout, sel, k: int, num_slots: int, step: int
         _ptr(miss_list, "miss_list", torch.int32, units * k),
         _ptr(miss_count, "miss_count", torch.int32, units),
         _stream(stream)), "kvs_hot_lookup_swapin")
+
+
+def kvs_hot_lookup(layout: Layout, sel, k: int, num_slots: int, step: int, page_table, slot_owner, slot_stamp,
+                   miss_list, miss_count, stream=None) -> None:
+    L = layout
+    units = L.num_seqs * L.num_kv_heads
+    _check(_lib.kvs_hot_lookup(
+        ctypes.byref(L.c()),
+        _ptr(sel, "sel", torch.int32, units * k), int(k), int(num_slots), int(step),
+        _ptr(page_table, "page_table", torch.int32, units * L.max_blocks),
+        _ptr(slot_owner, "slot_owner", torch.int32, units * num_slots),
+        _ptr(slot_stamp, "slot_stamp", torch.int64, units * num_slots),
+        _ptr(miss_list, "miss_list", torch.int32, units * k),
+        _ptr(miss_count, "miss_count", torch.int32, units),
+        _stream(stream)), "kvs_hot_lookup")
+
+
+def kvs_hot_swapin(layout: Layout, k: int, num_slots: int, page_table, miss_list, miss_count, host_k, host_v,
+                   host_k_scales, host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, stream=None) -> None:
+    L = layout
+    units = L.num_seqs * L.num_kv_heads
+    tile = L.block_size * L.head_dim
+    qg = L.quant_group
+    host_n = units * L.max_blocks * tile
+    hot_n = units * num_slots * tile
+    _check(_lib.kvs_hot_swapin(
+        ctypes.byref(L.c()), int(k), int(num_slots),
+        _ptr(page_table, "page_table", torch.int32, units * L.max_blocks),
+        _ptr(miss_list, "miss_list", torch.int32, units * k),
+        _ptr(miss_count, "miss_count", torch.int32, units),
+        _ptr(host_k, "host_k", _pool_dtype(L), host_n, device=False, pinned=True),
+        _ptr(host_v, "host_v", _pool_dtype(L), host_n, device=False, pinned=True),
+        _ptr(host_k_scales, "host_k_scales", torch.float32, host_n // qg if qg else None, device=False, pinned=True),
+        _ptr(host_v_scales, "host_v_scales", torch.float32, host_n // qg if qg else None, device=False, pinned=True),
+        _ptr(hot_k, "hot_k", _pool_dtype(L), hot_n),
+        _ptr(hot_v, "hot_v", _pool_dtype(L), hot_n),
+        _ptr(hot_k_scales, "hot_k_scales", torch.float32, hot_n // qg if qg else None),
+        _ptr(hot_v_scales, "hot_v_scales", torch.float32, hot_n // qg if qg else None),
+        _stream(stream)), "kvs_hot_swapin")
 
 
 def kvs_select_workspace_size(layout: Layout, k: int) -> int:

@@ -171,6 +171,17 @@ class HotBufferStep:
                                   self.hot_k, self.hot_v, self.hot_ks, self.hot_vs, self.miss_list,
                                   self.miss_count, stream)
 
+    def lookup(self, step, sel, stream=None):
+        """The page-table step alone (hits, miss list, LRU victims)."""
+        kvs.kvs_hot_lookup(self.host_layout, sel, self.k, self.ns, step, self.page_table, self.slot_owner,
+                           self.slot_stamp, self.miss_list, self.miss_count, stream)
+
+    def copy(self, host_k, host_v, host_ks=None, host_vs=None, stream=None):
+        """The copy of the misses the last lookup listed."""
+        kvs.kvs_hot_swapin(self.host_layout, self.k, self.ns, self.page_table, self.miss_list, self.miss_count,
+                           host_k, host_v, host_ks, host_vs, self.hot_k, self.hot_v, self.hot_ks, self.hot_vs,
+                           stream)
+
     def attend(self, q, sel, seq_lens, stream=None) -> torch.Tensor:
         kvs.kvs_sparse_decode_attn(self.hot_layout, kvs.KVS_TABLE_HOT, q, self.hot_k, self.hot_v,
                                    self.hot_ks, self.hot_vs, self.page_table, seq_lens, sel, self.k,
@@ -184,40 +195,128 @@ class HotBufferStep:
 
 class HotPrefetchPipeline:
     """Hot-buffer decode steps over several layers whose selections are known
-    one layer ahead (the premise of selecting KV a layer early, "SparDA…"
-    §3–4): the swap-in of layer i+1's misses runs on a second stream while
-    layer i attends, so the host-link copies leave the decode critical path
-    ("KV 稀疏化" §7 names misses on that path as the cost of the hot buffer).
+    ahead (the premise of selecting KV early, "SparDA…" §3–4): layer i+1's
+    misses come in over the host link while layer i attends, so the copies
+    leave the decode critical path ("KV 稀疏化" §7 names misses on that path
+    as the cost of the hot buffer; "分块稀疏注意力与KV Cache量化…" §5.3 widens
+    decode prefetch).
 
-    Each layer has its own HotBufferStep.  Layer i's attention waits for its
-    own swap-in (an event on the copy stream); a swap-in into layer i's
-    buffer waits for the previous attention that read it (an event on the
-    compute stream).  Both streams keep the default priority."""
+    Each layer has its own HotBufferStep.  lookup(i) runs layer i's
+    page-table step (kvs_hot_lookup) on the compute stream; swapin(i) runs
+    its copy (kvs_hot_swapin) on a copy stream, after that lookup;
+    attend(i) waits for that copy.  step(i) keeps the lookups two layers
+    ahead and the copies one layer ahead: the lookup (a chain of dependent
+    reads, slow beside the HBM-saturating attention) then runs while an
+    earlier copy is on the host link and is off the path between two
+    copies, and the copy stream carries only copies, back to back.  Every
+    lookup follows, on the compute stream, the earlier attentions of its
+    buffer; with lookups two layers ahead that needs at least three
+    buffers.  Both streams keep the default priority."""
 
-    def __init__(self, steps: list, device="cuda"):
+    def __init__(self, steps: list, device="cuda", copy_ahead: int = 2):
+        if len(steps) < 3:
+            raise ValueError("the pipeline needs at least three hot buffers")
+        if copy_ahead not in (1, 2):
+            raise ValueError("copy_ahead must be 1 or 2")
         self.hs = steps
+        self.copy_ahead = copy_ahead
         dev = torch.device(device)
         self.copy_stream = torch.cuda.Stream(device=dev)
+        self.looked = [torch.cuda.Event() for _ in steps]
         self.ready = [torch.cuda.Event() for _ in steps]
-        self.done = [torch.cuda.Event() for _ in steps]
-        self.used = [False for _ in steps]
+        self.next_lookup = self.next_copy = 0
 
-    def prefetch(self, i, step, sel, host_k, host_v, host_ks=None, host_vs=None):
-        """Enqueues layer i's swap-in on the copy stream."""
-        cur = torch.cuda.current_stream()
+    def lookup(self, i, step, sel):
+        """Buffer i's page-table step on the current stream."""
+        self.hs[i].lookup(step, sel)
+        self.looked[i].record(torch.cuda.current_stream())
+
+    def swapin(self, i, host_k, host_v, host_ks=None, host_vs=None):
+        """Buffer i's copy on the copy stream, after its lookup."""
         s = self.copy_stream
-        s.wait_stream(cur)  # sel and everything before it are ready
-        if self.used[i]:
-            s.wait_event(self.done[i])  # the buffer's last attention has read its slots
+        s.wait_event(self.looked[i])
         with torch.cuda.stream(s):
-            self.hs[i].swap_in(step, sel, host_k, host_v, host_ks, host_vs)
+            self.hs[i].copy(host_k, host_v, host_ks, host_vs)
         self.ready[i].record(s)
 
+    def prefetch(self, i, step, sel, host_k, host_v, host_ks=None, host_vs=None):
+        """Buffer i's lookup and copy, issued now."""
+        self.lookup(i, step, sel)
+        self.swapin(i, host_k, host_v, host_ks, host_vs)
+
     def attend(self, i, q, sel, seq_lens) -> torch.Tensor:
-        """Layer i's attention on the current stream, after its swap-in."""
-        cur = torch.cuda.current_stream()
-        cur.wait_event(self.ready[i])
-        out = self.hs[i].attend(q, sel, seq_lens)
-        self.done[i].record(cur)
-        self.used[i] = True
-        return out
+        """Buffer i's attention on the current stream, after its copy."""
+        torch.cuda.current_stream().wait_event(self.ready[i])
+        return self.hs[i].attend(q, sel, seq_lens)
+
+    def step(self, n, layer_of, lookup_args, host, q, sel, seq_lens) -> torch.Tensor:
+        """Decode layer-step n of a sequence of steps numbered 0, 1, ...:
+        step m runs buffer layer_of(m) with lookup_args(m) = (step, sel)
+        for its lookup.  Issues the lookups up to step n+2 and the copies
+        up to step n+1 that are not issued yet, then step n's attention."""
+        while self.next_lookup <= n + 2:
+            m = self.next_lookup
+            self.lookup(layer_of(m), *lookup_args(m))
+            self.next_lookup += 1
+            # the copy's wait goes in right after the lookup's record: on this
+            # stack a wait on an event can also wait for work the recording
+            # stream received after the record
+            while self.next_copy <= min(m, n + self.copy_ahead):
+                self.swapin(layer_of(self.next_copy), *host)
+                self.next_copy += 1
+        return self.attend(layer_of(n), q, sel, seq_lens)
+
+
+class CrossLayerDecode:
+    """A decode step over a model's layers that selects once
+    ("SparDA：把KV選擇提前一層…" §3.1, §4.1: a few shallow layers score the
+    history, their scores are fused into one mask, and every deeper layer
+    gathers the K/V that mask names, skipping its own selection).
+
+    Predictor layer l < P appends its decode token, adds its exact block
+    scores to the fused score (kvs_score_blocks with accumulate for l > 0,
+    so the fused score is the sum over layers 0..l, added in layer order)
+    and attends over the top-k of that sum (kvs_select_attn).  Every deeper
+    layer appends its token (kvs_append_token: its K/V written, its
+    summary kept current) and attends over the last predictor layer's
+    selection (kvs_sparse_decode_attn): it reads no summaries and scores
+    nothing.  Block ids are logical positions, so each layer gathers its own
+    pages through its own block table.  All layers share seq_lens."""
+
+    def __init__(self, layout: kvs.Layout, k: int, num_layers: int, predictor_layers: int, device="cuda"):
+        if not 1 <= predictor_layers <= num_layers:
+            raise ValueError("need 1 <= predictor_layers <= num_layers")
+        L = self.layout = layout
+        self.k, self.n, self.P = k, num_layers, predictor_layers
+        dev = torch.device(device)
+        self.fused = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=dev)
+        self.sel = torch.empty((L.num_seqs, L.num_kv_heads, k), dtype=torch.int32, device=dev)
+        self.out = torch.empty((num_layers, L.num_seqs, L.num_q_heads, L.head_dim), dtype=torch.float32, device=dev)
+        self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(L, k), 1), dtype=torch.uint8, device=dev)
+        self.sm_scale = 1.0 / math.sqrt(L.head_dim)
+        self._first = kvs.SelectOpts()
+        self._more = kvs.SelectOpts(accumulate=True)
+
+    def layer(self, l: int, q, tok: kvs.AppendArgs, seq_lens, summaries, stream=None) -> torch.Tensor:
+        """Layer l of the step (layers run in order 0, 1, ...); returns its
+        attention output [B][Hq][D]."""
+        L, k = self.layout, self.k
+        if l < self.P:
+            kvs.kvs_score_blocks(L, q, summaries, seq_lens, self._more if l > 0 else self._first, tok, self.fused,
+                                 None, stream)
+            kvs.kvs_select_attn(L, q, tok.k_pool, tok.v_pool, tok.k_scales, tok.v_scales, tok.block_table,
+                                seq_lens, self.fused, k, 1, self.sel, self.sm_scale, self.out[l], self.attn_ws,
+                                stream)
+        else:
+            kvs.kvs_append_token(L, tok, seq_lens, summaries, stream)
+            kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, tok.k_pool, tok.v_pool, tok.k_scales,
+                                       tok.v_scales, tok.block_table, seq_lens, self.sel, k, self.sm_scale,
+                                       self.out[l], self.attn_ws, stream)
+        return self.out[l]
+
+    def run(self, qs, toks, seq_lens, summaries, stream=None) -> torch.Tensor:
+        """The whole step: per-layer queries, token appends and summaries
+        (lists of num_layers); returns out [num_layers][B][Hq][D]."""
+        for l in range(self.n):
+            self.layer(l, qs[l], toks[l], seq_lens, summaries[l], stream)
+        return self.out

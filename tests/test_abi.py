@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(kvs):
 
 
 def test_abi_version_and_status_strings(kvs):
-    assert kvs.kvs_abi_version() == 3
+    assert kvs.kvs_abi_version() == 4
     for st in range(5):
         assert kvs.kvs_status_string(st).startswith("KVS_")
     assert "unknown" in kvs.kvs_status_string(99)
@@ -160,8 +160,8 @@ def test_append_and_select_ex_argument_checks(kvs):
     fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
     assert lib.kvs_append_token(ctypes.byref(fp8.c()), ctypes.byref(ok), FAKE, FAKE, None) == 1  # no scales
 
-    def sel_ex(k, recent=1, ema=0, alpha=0.7, state=FAKE.value, app=None, kind=0):
-        o = kvs._CSelectOpts(recent, ema, alpha, state, kind)
+    def sel_ex(k, recent=1, ema=0, alpha=0.7, state=FAKE.value, app=None, kind=0, acc=0):
+        o = kvs._CSelectOpts(recent, ema, alpha, state, kind, acc)
         return lib.kvs_select_topk_ex(c, FAKE, FAKE, FAKE, k, ctypes.byref(o),
                                       ctypes.byref(app) if app is not None else None,
                                       FAKE, None, FAKE, 1 << 20, None)
@@ -172,6 +172,7 @@ def test_append_and_select_ex_argument_checks(kvs):
     assert sel_ex(4, ema=1, state=0x100004) == kvs.KVS_ERR_INVALID_ARG  # misaligned state
     assert sel_ex(4, app=_append_args(kvs, v_new=None)) == kvs.KVS_ERR_INVALID_ARG
     assert sel_ex(4, kind=2) == kvs.KVS_ERR_INVALID_ARG
+    assert sel_ex(4, acc=1) == kvs.KVS_ERR_INVALID_ARG  # accumulation is for kvs_score_blocks
     assert lib.kvs_build_summaries_ex(c, 5, FAKE, None, FAKE, FAKE, None, 1, FAKE, None) == kvs.KVS_ERR_INVALID_ARG
 
 
@@ -211,3 +212,30 @@ def test_attention_workspace_bounded_for_every_split_count(kvs):
                         assert B * Hkv < 256
                     worst = max(worst, ws)
     assert worst <= (17 << 18)  # 4.25 MiB
+
+
+def test_split_hot_calls_argument_checks(kvs):
+    """kvs_hot_lookup and kvs_hot_swapin validate like kvs_hot_lookup_swapin,
+    each needing only its own half's buffers."""
+    lib = kvs.library()
+    L = _layout(kvs)
+    c = ctypes.byref(L.c())
+
+    def look(k=4, ns=4, step=0, sel=FAKE, owner=FAKE):
+        return lib.kvs_hot_lookup(c, sel, k, ns, step, FAKE, owner, FAKE, FAKE, FAKE, None)
+
+    def copy(k=4, ns=4, host_k=FAKE, hot_v=FAKE, layout=c):
+        return lib.kvs_hot_swapin(layout, k, ns, FAKE, FAKE, FAKE, host_k, FAKE, None, None, FAKE, hot_v,
+                                  None, None, None)
+    assert look(k=8, ns=4) == kvs.KVS_ERR_CAPACITY
+    assert look(ns=5000) == kvs.KVS_ERR_UNSUPPORTED
+    assert look(k=0) == kvs.KVS_ERR_INVALID_ARG
+    assert look(step=-1) == kvs.KVS_ERR_INVALID_ARG
+    assert look(sel=None) == kvs.KVS_ERR_INVALID_ARG
+    assert look(owner=None) == kvs.KVS_ERR_INVALID_ARG
+    assert copy(k=8, ns=4) == kvs.KVS_ERR_CAPACITY
+    assert copy(host_k=None) == kvs.KVS_ERR_INVALID_ARG
+    assert copy(hot_v=None) == kvs.KVS_ERR_INVALID_ARG
+    assert copy(hot_v=0x100004) == kvs.KVS_ERR_INVALID_ARG  # misaligned
+    fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
+    assert copy(layout=ctypes.byref(fp8.c())) == kvs.KVS_ERR_INVALID_ARG  # fp8 without scales

@@ -1,0 +1,141 @@
+"""Cross-layer selection reuse ("SparDA：把KV選擇提前一層…" §3.1, §4.1):
+CrossLayerDecode through the C ABI against the oracle over several layers.
+
+Every layer has its own K/V pools, block table and query; the decode token
+is new (each layer's summaries are built without it, then the step appends
+it).  Predictor layers 0..P-1 add their block scores into one fused score
+and attend over its top-k; deeper layers attend over the last predictor
+layer's selection.  Checked per layer against the oracle: the appended
+pools and summaries (by value), the fused scores (bit-exact, except each
+sequence's newest block, whose score the fused append leaves unspecified),
+the selection (bit-exact) and the attention (max |err| <= 1e-2, relative
+L2 <= 5e-3).
+"""
+import math
+
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ATOL, RTOL_L2 = 1e-2, 5e-3
+
+
+def _np(t):
+    import torch
+    t = t.cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _run(orc, base, over, lens, k, n_layers, P, seqs_checked=None):
+    import torch
+    from query_aware_sparse_kvs_amd import kvs, synth
+    from query_aware_sparse_kvs_amd.step import CrossLayerDecode
+    assert torch.cuda.is_available()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kvs.kvs_device_errors(clear=True)
+    w = synth.scaled(synth.WORKLOADS[base], **over, k=k)
+    code = kvs.DTYPE_CODE
+    P_pages = w.B * w.nb
+    L = kvs.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, P_pages, code[w.q_dtype], code[w.kv_dtype], w.quant_group)
+    OL = orc.Layout(w.B, w.Hq, w.Hkv, w.D, w.S, w.nb, P_pages, code[w.kv_dtype], w.quant_group)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    prev = (lens_t - 1).clamp(min=0)
+    layers, host = [], []
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    for l in range(n_layers):
+        inp = synth.make_inputs(w, dev, layer=l, seq_lens=lens)
+        # a new decode token per sequence (K/V drawn afresh; fp8 quantised)
+        if w.kv_dtype == "e4m3":
+            kq, ks = synth.quantize_e4m3(torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev), w.quant_group)
+            vq, vs = synth.quantize_e4m3(torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev), w.quant_group)
+        else:
+            dt = inp["k_pool"].dtype
+            kq = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(dt)
+            vq = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(dt)
+            ks = vs = None
+        tok = kvs.AppendArgs(k_new=kq, v_new=vq, k_new_scales=ks, v_new_scales=vs, block_table=inp["block_table"],
+                             k_pool=inp["k_pool"], v_pool=inp["v_pool"], k_scales=inp["k_scales"],
+                             v_scales=inp["v_scales"])
+        summ = torch.empty((w.B, w.Hkv, w.nb, 2, w.D), dtype=L.summary_dtype, device=dev)
+        kvs.kvs_build_summaries(L, inp["k_pool"], inp["k_scales"], inp["block_table"], prev, None, w.nb, summ)
+        torch.cuda.synchronize()
+        h = {n: _np(inp[n]) for n in ("k_pool", "v_pool")}
+        for n in ("k_scales", "v_scales"):
+            h[n] = None if inp[n] is None else inp[n].cpu().numpy()
+        h["table"] = inp["block_table"].cpu().numpy()
+        h["q"] = inp["q"].double().cpu().numpy()
+        h["summ"] = orc.summaries(OL, h["k_pool"], h["k_scales"], h["table"], prev.cpu().numpy())
+        orc.append_token(OL, _np(kq), _np(vq), None if ks is None else ks.cpu().numpy(),
+                         None if vs is None else vs.cpu().numpy(), h["table"], np.asarray(lens, np.int32),
+                         h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["summ"])
+        layers.append((inp, tok, summ))
+        host.append(h)
+    step = CrossLayerDecode(L, k, n_layers, P, dev)
+    out = step.run([x[0]["q"] for x in layers], [x[1] for x in layers], lens_t, [x[2] for x in layers])
+    torch.cuda.synchronize()
+    assert kvs.kvs_device_errors(clear=True) == 0
+    h_lens = np.asarray(lens, np.int32)
+    nbs = [(n + w.S - 1) // w.S for n in lens]
+    sm = 1.0 / math.sqrt(w.D)
+    Ws, sel, worst = [], None, (0.0, 0.0)
+    seqs = range(w.B) if seqs_checked is None else seqs_checked
+    for l in range(n_layers):
+        inp, _, summ = layers[l]
+        h = host[l]
+        # the appended cache and its summaries
+        for n in ("k_pool", "v_pool"):
+            assert np.array_equal(_np(inp[n]), h[n]), f"layer {l}: {n} after the append differs"
+        g_summ = summ.double().cpu().numpy()
+        for b in seqs:
+            assert np.array_equal(g_summ[b, :, :nbs[b]], h["summ"][b, :, :nbs[b]]), f"layer {l} summaries"
+        if l < P:
+            Ws.append(orc.bounds(OL, h["q"], h["summ"], h_lens))
+            F = orc.fuse_scores(OL, Ws, h_lens)
+            gF = step.fused.cpu().numpy() if l == P - 1 else None
+            if gF is not None:
+                for b in seqs:
+                    nb = nbs[b]
+                    assert np.array_equal(gF[b, :, :nb - 1], F[b, :, :nb - 1]), f"fused scores, sequence {b}"
+                    assert np.isneginf(gF[b, :, nb:]).all()
+            sel = orc.select(OL, F, h_lens, k)
+        gsel = step.sel.cpu().numpy()
+        if l == n_layers - 1 or l == P - 1:
+            for b in seqs:
+                assert np.array_equal(gsel[b], sel[b]), f"layer {l}: selection of sequence {b} differs"
+        o = orc.sparse_attn(OL, h["q"], h["k_pool"], h["v_pool"], h["k_scales"], h["v_scales"], h["table"], h_lens,
+                            sel, sm)
+        gout = out[l].double().cpu().numpy()
+        for b in seqs:
+            assert np.isfinite(gout[b]).all()
+            err = np.abs(gout[b] - o[b]).max()
+            rel = np.linalg.norm(gout[b] - o[b]) / np.linalg.norm(o[b])
+            assert err <= ATOL and rel <= RTOL_L2, f"layer {l} sequence {b}: max|err| {err:.3e} rel {rel:.3e}"
+            worst = (max(worst[0], err), max(worst[1], rel))
+    print(f"[cross-layer {base} P={P}/{n_layers}] worst max|err| {worst[0]:.2e} rel L2 {worst[1]:.2e}", flush=True)
+
+
+CASES = [
+    # (name, workload, overrides, seq_lens, k, layers, predictor layers)
+    ("bf16-p2", "llama8b", {"B": 3, "L": 5000, "layers": 1}, [5000, 4097, 130], 16, 4, 2),
+    ("bf16-p1", "llama8b", {"B": 2, "L": 3000, "layers": 1}, [3000, 64 * 20], 12, 3, 1),
+    ("fp8-p3", "longfp8", {"B": 2, "L": 6000}, [6000, 2049], 16, 4, 3),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_cross_layer_reuse_matches_oracle(orc, case):
+    name, base, over, lens, k, n, P = case
+    print(f"[cross-layer {name}] lens={lens} k={k} layers={n} predictors={P}", flush=True)
+    _run(orc, base, over, lens, k, n, P)
+
+
+def test_cross_layer_reuse_full_longfp8(orc):
+    """The long fp8 workload at full size (4 sequences of 131072 tokens,
+    k = 64 of 2048), four layers selecting once at the first two."""
+    from query_aware_sparse_kvs_amd import synth
+    w = synth.WORKLOADS["longfp8"]
+    print("[cross-layer longfp8 full] 4 layers, 2 predictors", flush=True)
+    _run(orc, "longfp8", {}, [w.L] * w.B, w.k, 4, 2)

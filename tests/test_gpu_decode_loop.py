@@ -365,44 +365,95 @@ def test_score_blocks_then_select_attn(env, case):
     print(f"[score+select-attn {name}] attention max|err| {err:.2e} rel L2 {rel:.2e}")
 
 
-def test_prefetch_pipeline_matches_sequential_hot_steps(env):
-    """Layers' swap-ins issued one layer ahead on a second stream (the copy
-    for layer i+1 while layer i attends) give exactly the outputs, page
-    tables and slot states of the same steps run one after another."""
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_prefetch_pipeline_matches_oracle_and_sequential_hot_steps(env, kind):
+    """Layers' swap-ins issued ahead (page-table steps two layers ahead on
+    the compute stream, copies one layer ahead on a second stream while
+    layer i attends) give exactly the outputs, page tables and slot states of the
+    same steps run one after another, and match the oracle: every step's
+    miss list and count, the final page tables, owners and stamps bit-exact,
+    every step's attention within the bars."""
     torch, kvs, synth = env.torch, env.kvs, env.synth
     from query_aware_sparse_kvs_amd.step import HotBufferStep, HotPrefetchPipeline
-    w = synth.scaled(synth.WORKLOADS["llama8b"], B=2, L=64 * 40, Hkv=2, Hq=8, layers=1, k=10)
+    from test_gpu_parity import check_attn
+    orc = env.orc
+    if kind == "bf16":
+        w = synth.scaled(synth.WORKLOADS["llama8b"], B=2, L=64 * 40, Hkv=2, Hq=8, layers=1, k=10)
+    else:
+        w = synth.scaled(synth.WORKLOADS["longfp8"], B=2, L=64 * 40 - 9, Hkv=2, Hq=8, k=10)
     p = Problem(env, w)
     L = p.L
-    n_layers, steps = 3, 7
-    print(f"[prefetch] {n_layers} layers x {steps} steps, units {L.num_seqs * L.num_kv_heads}, k {w.k}",
-          flush=True)
+    n_layers, steps, ns = 3, 7, 12
+    units = L.num_seqs * L.num_kv_heads
+    print(f"[prefetch {kind}] {n_layers} layers x {steps} steps, units {units}, k {w.k}, slots {ns}", flush=True)
     sel0 = synth.random_selection(w, p.h["lens"], w.k, seed=4)
     stream = synth.drift_selections(sel0, w.nb, n_layers * steps + 2, 3, seed=5)
     sels = torch.from_numpy(stream).to(env.dev)
     pages = p.inp["block_table"].long().cpu()
-    host = [p.inp[n].cpu()[pages].transpose(1, 2).contiguous().pin_memory() for n in ("k_pool", "v_pool")]
-    seq = [HotBufferStep(L, w.k, w.k, env.dev) for _ in range(n_layers)]
-    pip = [HotBufferStep(L, w.k, w.k, env.dev) for _ in range(n_layers)]
+    host = [None if p.inp[n] is None else p.inp[n].cpu()[pages].transpose(1, 2).contiguous().pin_memory()
+            for n in ("k_pool", "v_pool", "k_scales", "v_scales")]
+    seq = [HotBufferStep(L, w.k, ns, env.dev) for _ in range(n_layers)]
+    pip = [HotBufferStep(L, w.k, ns, env.dev) for _ in range(n_layers)]
     pipe = HotPrefetchPipeline(pip, env.dev)
-    outs_seq, outs_pip = [], []
+    outs_seq, outs_pip, miss_pip = [], [], []
     t_of = lambda i: 1 + i  # stream entry of step i (entry 0 is the warm start)
     for h in seq + pip:
         h.run(0, sels[0], p.inp["q"], p.inp["seq_lens"], *host)
     for i in range(n_layers * steps):
         outs_seq.append(seq[i % n_layers].run(t_of(i), sels[t_of(i)], p.inp["q"], p.inp["seq_lens"], *host).clone())
-    pipe.prefetch(0, t_of(0), sels[t_of(0)], *host)
+    layer_of = lambda i: i % n_layers
+    lookup_args = lambda i: (t_of(i), sels[t_of(i)])
     for i in range(n_layers * steps):
-        if i + 1 < n_layers * steps:
-            pipe.prefetch((i + 1) % n_layers, t_of(i + 1), sels[t_of(i + 1)], *host)
-        outs_pip.append(pipe.attend(i % n_layers, p.inp["q"], sels[t_of(i)], p.inp["seq_lens"]).clone())
+        # lookups two steps ahead, copies one step ahead, then step i's attention
+        out = pipe.step(i, layer_of, lookup_args, host, p.inp["q"], sels[t_of(i)], p.inp["seq_lens"])
+        outs_pip.append(out.clone())
+        # this buffer's next lookup (step i + n_layers) is enqueued later on the same stream
+        miss_pip.append((pip[i % n_layers].miss_list.clone(), pip[i % n_layers].miss_count.clone()))
+    N = n_layers * steps
+    # the pipeline has issued the lookups and copies of the steps after N-1
+    # already: take the sequential buffers to the same point
+    for m in range(N, pipe.next_lookup):
+        seq[layer_of(m)].lookup(*lookup_args(m))
+        if m < pipe.next_copy:
+            seq[layer_of(m)].copy(*host)
     torch.cuda.synchronize()
     no_device_errors(env)
     for i, (a, b) in enumerate(zip(outs_seq, outs_pip)):
         assert torch.equal(a, b), f"step {i}: outputs differ"
     for a, b in zip(seq, pip):
-        for n in ("page_table", "slot_owner", "slot_stamp", "hot_k", "hot_v"):
-            assert torch.equal(getattr(a, n), getattr(b, n)), f"{n} differs"
+        for n in ("page_table", "slot_owner", "slot_stamp", "hot_k", "hot_v", "hot_ks", "hot_vs"):
+            if getattr(a, n) is not None:
+                assert torch.equal(getattr(a, n), getattr(b, n)), f"{n} differs"
+    # the oracle: each buffer's LRU state stepped through its selections
+    pt = np.full((n_layers, units, w.nb), -1, np.int32)
+    owner = np.full((n_layers, units, ns), -1, np.int32)
+    stamp = np.full((n_layers, units, ns), -1, np.int64)
+    for l in range(n_layers):
+        for u in range(units):
+            orc.hot_step(w.nb, ns, 0, u * ns, stream[0].reshape(units, -1)[u], pt[l, u], owner[l, u], stamp[l, u])
+    worst = 0.0
+    for i in range(n_layers * steps):
+        l, t = i % n_layers, t_of(i)
+        ml, mc = [], []
+        for u in range(units):
+            m, c = orc.hot_step(w.nb, ns, t, u * ns, stream[t].reshape(units, -1)[u], pt[l, u], owner[l, u],
+                                stamp[l, u])
+            ml.append(m)
+            mc.append(c)
+        g_ml, g_mc = miss_pip[i]
+        assert np.array_equal(g_ml.cpu().numpy().reshape(units, -1), np.stack(ml)), f"step {i}: miss lists"
+        assert np.array_equal(g_mc.cpu().numpy().reshape(-1), np.array(mc)), f"step {i}: miss counts"
+        err, _ = check_attn(outs_pip[i], p.or_attn(stream[t]))
+        worst = max(worst, err)
+    for m in range(N, pipe.next_lookup):  # the lookups issued ahead
+        for u in range(units):
+            orc.hot_step(w.nb, ns, t_of(m), u * ns, stream[t_of(m)].reshape(units, -1)[u], pt[layer_of(m), u],
+                         owner[layer_of(m), u], stamp[layer_of(m), u])
+    for l in range(n_layers):
+        assert np.array_equal(pip[l].page_table.cpu().numpy().reshape(units, -1), pt[l])
+        assert np.array_equal(pip[l].slot_owner.cpu().numpy().reshape(units, -1), owner[l])
+        assert np.array_equal(pip[l].slot_stamp.cpu().numpy().reshape(units, -1), stamp[l])
+    print(f"[prefetch {kind}] pipelined = sequential; tables and miss lists = oracle; max|err| {worst:.2e}")
 
 
 MEAN_CASES = [
