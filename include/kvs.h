@@ -97,7 +97,8 @@ typedef enum kvs_table_kind {
   /* table = hot page table [B][Hkv][MB] of global hot-slot ids in [0, P)
    * (-1 = not resident); one KV head per slot: K pool [P][S][D], V pool
    * [P][S/T][D][T], scales [P][S][D/quant_group]. P is then the total number of
-   * hot slots. */
+   * hot slots.  Slots hold what kvs_hot_lookup_swapin copied from the host
+   * tier: only blocks that no longer receive tokens (see there). */
   KVS_TABLE_HOT = 1
 } kvs_table_kind;
 
@@ -475,6 +476,16 @@ kvs_status kvs_select_attn(const kvs_layout* layout, const void* q, const void* 
  *      tier into its slot.
  * Blocks in the host tier are immutable once written, so eviction needs no
  * write-back.
+ *
+ * Precondition: every block the hot path serves is final.  A slot is filled
+ * from the host tier and never changed by an append, and kvs_append_token
+ * writes a block to the host tier only when it seals it (full).  So a block
+ * that is still receiving tokens -- a sequence's newest, partial block in a
+ * decode loop that appends -- must not be read through KVS_TABLE_HOT: its
+ * slot would hold a copy without the tokens appended since.  Callers attend
+ * such a block from the paged pool (kvs_sparse_decode_attn with
+ * KVS_TABLE_PAGED) or fill the host tier with its current contents before
+ * each swap-in of it.
  *
  *  layout       num_seqs, num_kv_heads, head_dim, block_size, max_blocks
  *               (page-table row length), kv_dtype, quant_group are used

@@ -19,6 +19,7 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 ATOL, RTOL_L2 = 1e-2, 5e-3
+REG_ATOL, REG_RTOL_L2 = 3e-4, 5e-5  # regression bars (test_gpu_parity.py states their basis)
 
 
 def _np(t):
@@ -113,6 +114,7 @@ def _run(orc, base, over, lens, k, n_layers, P, seqs_checked=None):
             err = np.abs(gout[b] - o[b]).max()
             rel = np.linalg.norm(gout[b] - o[b]) / np.linalg.norm(o[b])
             assert err <= ATOL and rel <= RTOL_L2, f"layer {l} sequence {b}: max|err| {err:.3e} rel {rel:.3e}"
+            assert err <= REG_ATOL and rel <= REG_RTOL_L2, "regression bar: " + f"layer {l} sequence {b}: max|err| {err:.3e} rel {rel:.3e}"
             worst = (max(worst[0], err), max(worst[1], rel))
     print(f"[cross-layer {base} P={P}/{n_layers}] worst max|err| {worst[0]:.2e} rel L2 {worst[1]:.2e}", flush=True)
 

@@ -19,6 +19,13 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 ATOL, RTOL_L2, BAND = 1e-2, 5e-3, 1e-4
+# Regression bars beside the acceptance bars: over every parity case the
+# kernels' attention errors are at most 5.7e-5 (max abs, fp8 with 16-channel
+# scale groups, where K enters the score product as a bf16 hi/lo pair) and
+# 7.4e-6 (relative L2).  These bars sit about 5x above that, so a change that
+# loses an order of magnitude of accuracy fails although the acceptance bars
+# (two orders looser still) would pass it.
+REG_ATOL, REG_RTOL_L2 = 3e-4, 5e-5
 
 
 @pytest.fixture(scope="module")
@@ -159,6 +166,7 @@ def check_attn(g_out, o_out):
     nrm = np.linalg.norm(o_out)
     rel = np.linalg.norm(g - o_out) / nrm if nrm > 0 else np.linalg.norm(g - o_out)
     assert err <= ATOL and rel <= RTOL_L2, f"max|err| {err:.3e}, rel L2 {rel:.3e}"
+    assert err <= REG_ATOL and rel <= REG_RTOL_L2, f"regression bar: max|err| {err:.3e}, rel L2 {rel:.3e}"
     return err, rel
 
 
@@ -649,8 +657,8 @@ def test_full_llama8b_fused_route(env):
 def test_full_longfp8_fused_route(env):
     """The fp8 workload's timed step at full size (131072 tokens, k = 64 of
     2048: the attention workgroups select from 2048 scores, and the score
-    product runs per 32-channel quantisation group), two sequences checked
-    against the oracle."""
+    product runs per 32-channel quantisation group), all four sequences
+    checked against the oracle."""
     from query_aware_sparse_kvs_amd.step import SparseDecodeStep
     torch, orc = env.torch, env.orc
     w = env.synth.WORKLOADS["longfp8"]
@@ -660,7 +668,7 @@ def test_full_longfp8_fused_route(env):
     st.prefill_summaries(p.inp["k_pool"], p.inp["k_scales"], p.inp["block_table"], p.inp["seq_lens"], summ)
     out = st.run_decode_fused(p.inp["q"], _newest_token_append(env, w, p.inp), p.inp["seq_lens"], summ)
     no_device_errors(env)
-    seqs = [0, 2]
+    seqs = [0, 1, 2, 3]
     flat = p.inp["block_table"][seqs].long().reshape(-1)
     sub = lambda n: p.inp[n][flat].cpu().numpy()
     new_tbl = np.arange(flat.numel(), dtype=np.int32).reshape(len(seqs), -1)
@@ -691,10 +699,19 @@ def _compact(p, seqs):
     return sub, new_tbl.numpy()
 
 
-def test_full_highconc_sampled(env):
+def fan_out(fn, items, threads=16):
+    """fn over items on up to `threads` host threads (the oracle's ctypes
+    calls release the interpreter lock)."""
+    import concurrent.futures as cf
+    with cf.ThreadPoolExecutor(max_workers=max(1, min(threads, len(items)))) as ex:
+        return list(ex.map(fn, items))
+
+
+def test_full_highconc(env):
     """256 sequences at 32K, k = 32, over a 131072-page shared pool: the
-    whole batch runs on the GPU; 4 sampled sequences are checked, also
-    through the timed route (token append, matrix-core scores)."""
+    whole batch on the GPU; summaries, bounds and selections of all 256
+    sequences checked against the oracle (bit-exact), attention of 32 of
+    them, also through the timed route (token append, matrix-core scores)."""
     from query_aware_sparse_kvs_amd.step import SparseDecodeStep
     torch, orc = env.torch, env.orc
     w = env.synth.WORKLOADS["highconc"]
@@ -709,22 +726,41 @@ def test_full_highconc_sampled(env):
     out = st.run(p_inp["q"], p_inp["k_pool"], p_inp["v_pool"], None, None, p_inp["block_table"],
                  p_inp["seq_lens"], summ, bounds_out=W)
     no_device_errors(env)
-    seqs = [0, 77, 160, 255]
+    print("[highconc] oracle on all 256 sequences", flush=True)
+    kp = np_pool(p_inp["k_pool"])  # the whole pool, 8 GiB
+    table = p_inp["block_table"].cpu().numpy()
+    lens = p_inp["seq_lens"].cpu().numpy()
+    q_all = p_inp["q"].double().cpu().numpy()
+    g_summ = summ.double().cpu().numpy()
+    g_W = W.cpu().numpy()
+    g_sel = st.sel.cpu().numpy()
+    OL1 = orc.Layout(1, w.Hq, w.Hkv, w.D, w.S, w.nb, w.B * w.nb, orc.KV_BF16)
+
+    def one(b):
+        r = slice(b, b + 1)
+        o_summ = orc.summaries(OL1, kp, None, table[r], lens[r])
+        o_W = orc.bounds(OL1, q_all[r], o_summ, lens[r])
+        o_sel = orc.select(OL1, o_W, lens[r], w.k)
+        ok = (np.array_equal(g_summ[b], o_summ[0]), np.array_equal(g_W[b], o_W[0]),
+              np.array_equal(g_sel[b], o_sel[0]))
+        return ok, near_tie_count(o_W, lens[r], w.S, w.k)
+    res = fan_out(one, list(range(w.B)))
+    for b, (ok, _) in enumerate(res):
+        assert ok[0], f"summaries of sequence {b} differ"
+        assert ok[1], f"bounds of sequence {b} differ"
+        assert ok[2], f"selection of sequence {b} differs"
+    ties = sum(t for _, t in res)
+    del kp
+    seqs = list(range(0, w.B, 8))  # 32 sequences for the attention
     tbl = p_inp["block_table"][seqs].long()
     flat = tbl.reshape(-1)
-    kp, vp = np_pool(p_inp["k_pool"][flat]), np_pool(p_inp["v_pool"][flat])
+    kps, vps = np_pool(p_inp["k_pool"][flat]), np_pool(p_inp["v_pool"][flat])
     new_tbl = np.arange(flat.numel(), dtype=np.int32).reshape(len(seqs), -1)
-    lens = p_inp["seq_lens"][seqs].cpu().numpy()
     OL = orc.Layout(len(seqs), w.Hq, w.Hkv, w.D, w.S, w.nb, flat.numel(), orc.KV_BF16)
-    o_summ = orc.summaries(OL, kp, None, new_tbl, lens)
-    assert np.array_equal(summ[seqs].double().cpu().numpy(), o_summ)
-    q = p_inp["q"][seqs].double().cpu().numpy()
-    o_W = orc.bounds(OL, q, o_summ, lens)
-    assert np.array_equal(W[seqs].cpu().numpy(), o_W)
-    o_sel = orc.select(OL, o_W, lens, w.k)
-    assert np.array_equal(st.sel[seqs].cpu().numpy(), o_sel)
-    o_out = orc.sparse_attn(OL, q, kp, vp, None, None, new_tbl, lens, o_sel, 1 / math.sqrt(w.D))
-    check_attn(out[seqs], o_out)
+    o_out = orc.sparse_attn(OL, q_all[seqs], kps, vps, None, None, new_tbl, lens[seqs], g_sel[seqs], 1 / math.sqrt(w.D))
+    err, rel = check_attn(out[seqs], o_out)
+    print(f"[highconc] 256 sequences bit-exact ({ties} near-tie units); attention on 32: max|err| {err:.2e} "
+          f"rel L2 {rel:.2e}", flush=True)
     exact_sel = st.sel.clone()
     exact_summ = summ.clone()
     stale_newest(summ, p_inp["seq_lens"], w.S)
@@ -742,9 +778,9 @@ def test_full_highconc_sampled(env):
     check_attn(out[seqs], o_out)
 
 
-def test_full_longfp8_sampled(env):
-    """131072-token fp8 sequences, k = 64 of 2048: full batch on the GPU,
-    two sequences checked against the oracle."""
+def test_full_longfp8(env):
+    """131072-token fp8 sequences, k = 64 of 2048: the whole batch on the
+    GPU, all four sequences checked against the oracle."""
     from query_aware_sparse_kvs_amd.step import SparseDecodeStep
     torch, orc = env.torch, env.orc
     w = env.synth.WORKLOADS["longfp8"]
@@ -757,7 +793,7 @@ def test_full_longfp8_sampled(env):
     out = st.run(p.inp["q"], p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
                  p.inp["block_table"], p.inp["seq_lens"], summ, bounds_out=W)
     no_device_errors(env)
-    seqs = [1, 3]
+    seqs = [0, 1, 2, 3]
     flat = p.inp["block_table"][seqs].long().reshape(-1)
     sub = lambda n: p.inp[n][flat].cpu().numpy()
     new_tbl = np.arange(flat.numel(), dtype=np.int32).reshape(len(seqs), -1)
