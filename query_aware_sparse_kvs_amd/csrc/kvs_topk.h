@@ -5,17 +5,25 @@
 // by the attention kernels that select their own blocks.
 //
 // The M = k-1-R best candidates (blocks 1..nb-R-1) under (W descending, id
-// ascending) are found by bucket refinement.  Each round takes the still
+// ascending) are found by bucket refinement.  A round takes the still
 // undecided candidates, spreads them over 2048 LDS buckets by the monotone
 // map (w - lo) * 2047 / (hi - lo) (lo, hi: their smallest and largest
 // score), and scans the bucket counts from the top: candidates above the
 // bucket where the count reaches the places left are taken, those below are
-// dropped, and only that bucket's candidates stay undecided.  The rounds end
-// when the undecided candidates exactly fill the places left, or when they
-// all hold one score (then the lowest ids win).  lo and hi always fall into
-// different buckets, so every round decides at least one candidate; with
-// real scores one or two rounds settle the selection.  A block-wide prefix
-// sum then writes the chosen ids in ascending order, then -1 padding.
+// dropped, and only that bucket's candidates stay undecided.  Those (at
+// most 256 of them, else another round) are then ranked among themselves
+// by (W desc, id asc) from a short LDS list, and the first ones fill the
+// places left.  Rounds also end when the undecided candidates exactly fill
+// the places left, or all hold one score (then the lowest ids win).  lo and
+// hi always fall into different buckets, so every round decides at least
+// one candidate; with real scores one round and the ranking settle the
+// selection.  A block-wide prefix sum then writes the chosen ids in
+// ascending order, then -1 padding.
+//
+// Cross-lane steps avoid LDS round trips: minima and maxima go through DPP
+// row moves and readlane, prefix sums of small counts through one ballot and
+// popcount per bit; only the per-wavefront totals meet in LDS, behind one
+// workgroup barrier each.
 #pragma once
 
 #include "kvs_internal.h"
@@ -23,15 +31,85 @@
 namespace kvs {
 
 constexpr int kTopkBuckets = 2048;
+constexpr int kTopkList = 256;  // threshold-bucket candidates ranked directly
 
 // LDS of one selection
 struct TopkLds {
   unsigned hist[kTopkBuckets];
   double red_lo[4], red_hi[4];
-  int red_n[4];
-  int scan_tmp[4];
-  int sh_T, sh_rem, sh_all;
+  int scan_h[4], scan_c[4], scan_o[4];
+  int sh_T, sh_rem, sh_all, sh_cnt, sh_len;
+  double lw[kTopkList];
+  int lid[kTopkList];
 };
+
+// One 32-bit DPP move inside a 16-lane row (CTRL: a permutation, so every
+// lane has a source and `old` is never used).
+template <int CTRL>
+__device__ __forceinline__ double dpp_row_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)((unsigned long long)b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double x, int lane) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_readlane((int)(unsigned)b, lane);
+  const int hi = __builtin_amdgcn_readlane((int)(unsigned)((unsigned long long)b >> 32), lane);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Minimum (MAX = false) or maximum of x over the 64 lanes, in every lane:
+// within each 16-lane row by DPP (lane pairs i^1, i^2, then the half-row and
+// row mirrors), then the four rows' results by readlane.
+template <bool MAX>
+__device__ __forceinline__ double wave_minmax_f64(double x) {
+  auto op = [](double a, double b) { return MAX ? fmax(a, b) : fmin(a, b); };
+  x = op(x, dpp_row_f64<0xB1>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_row_f64<0x4E>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_row_f64<0x141>(x));  // row_half_mirror
+  x = op(x, dpp_row_f64<0x140>(x));  // row_mirror
+  return op(op(readlane_f64(x, 0), readlane_f64(x, 16)), op(readlane_f64(x, 32), readlane_f64(x, 48)));
+}
+
+// Exclusive prefix over the wavefront of a small non-negative v < 2^BITS,
+// and the wavefront total, from one ballot per bit.
+template <int BITS>
+__device__ __forceinline__ int wave_prefix_small(int v, int* total) {
+  const unsigned long long below = (1ull << (threadIdx.x & 63)) - 1ull;
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __ballot((v >> b) & 1);
+    pre += __popcll(m & below) << b;
+    tot += __popcll(m) << b;
+  }
+  *total = tot;
+  return pre;
+}
+
+// The same over the 256 threads (one workgroup barrier); `tmp` holds 4 ints
+// of LDS that no other call uses before the next barrier.
+template <int BITS>
+__device__ __forceinline__ int block_prefix_small_256(int v, int* tmp, int* total) {
+  const int wave = threadIdx.x >> 6;
+  int wt;
+  const int pre = wave_prefix_small<BITS>(v, &wt);
+  if ((threadIdx.x & 63) == 0) tmp[wave] = wt;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + pre;
+}
+
+constexpr int bits_for(int n) { return n <= 1 ? 1 : 1 + bits_for(n / 2); }  // bits of values 0..n
 
 // min and max of the active scores and their count, over the 256 threads
 // (one workgroup barrier)
@@ -42,27 +120,24 @@ __device__ __forceinline__ void active_range(const double (&wv)[PT], const bool 
   double l = __builtin_inf(), h = -__builtin_inf();
   int c = 0;
 #pragma unroll
-  for (int i = 0; i < PT; ++i)
+  for (int i = 0; i < PT; ++i) {
     if (act[i]) {
       l = fmin(l, wv[i]);
       h = fmax(h, wv[i]);
-      ++c;
     }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    l = fmin(l, __shfl_xor(l, off));
-    h = fmax(h, __shfl_xor(h, off));
-    c += __shfl_xor(c, off);
+    c += __popcll(__ballot(act[i]));  // wavefront-uniform
   }
+  l = wave_minmax_f64<false>(l);
+  h = wave_minmax_f64<true>(h);
   if (lane == 0) {
     sh.red_lo[wave] = l;
     sh.red_hi[wave] = h;
-    sh.red_n[wave] = c;
+    sh.scan_c[wave] = c;
   }
   __syncthreads();
   *lo = fmin(fmin(sh.red_lo[0], sh.red_lo[1]), fmin(sh.red_lo[2], sh.red_lo[3]));
   *hi = fmax(fmax(sh.red_hi[0], sh.red_hi[1]), fmax(sh.red_hi[2], sh.red_hi[3]));
-  *n = sh.red_n[0] + sh.red_n[1] + sh.red_n[2] + sh.red_n[3];
+  *n = sh.scan_c[0] + sh.scan_c[1] + sh.scan_c[2] + sh.scan_c[3];
 }
 
 // A unit's scores W[0..MB): thread t holds ids t*per .. t*per+per-1,
@@ -86,6 +161,7 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
   const int tid = threadIdx.x;
   const int per = (MB + 255) / 256;
   const int j0 = tid * per;
+  constexpr int CB = bits_for(PT);  // bits of a per-thread count 0..PT
   if (nb <= k) {  // every block, then padding
     for (int i = tid; i < k; i += 256) out[i] = i < nb ? i : -1;
     return;
@@ -120,13 +196,14 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
 #pragma unroll
       for (int i = 0; i < PT; ++i) c += act[i] ? 1 : 0;
       int tot;
-      int before = block_exclusive_scan_256(c, sh.scan_tmp, &tot);
+      int before = block_prefix_small_256<CB>(c, sh.scan_o, &tot);
 #pragma unroll
       for (int i = 0; i < PT; ++i)
         if (act[i]) {
           take[i] = take[i] || before < need;
           ++before;
         }
+      __syncthreads();  // scan_o is read again by the output scan below
       break;
     }
     // bucket of each undecided candidate, nondecreasing in its score: lo in
@@ -153,7 +230,7 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
       s += (int)cnt[q];
     }
     int tot;
-    int above = block_exclusive_scan_256(s, sh.scan_tmp, &tot);
+    int above = block_prefix_small_256<bits_for(256 * 32)>(s, sh.scan_h, &tot);
     if (above < need && need <= above + s) {  // exactly one thread
 #pragma unroll
       for (int q = 0; q < BPT; ++q) {
@@ -161,6 +238,8 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
           sh.sh_T = kTopkBuckets - 1 - BPT * tid - q;
           sh.sh_rem = need - above;
           sh.sh_all = above + (int)cnt[q] == need;  // the bucket fills the places exactly
+          sh.sh_cnt = (int)cnt[q];
+          sh.sh_len = 0;
           break;
         }
         above += (int)cnt[q];
@@ -170,12 +249,45 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
     const int T = sh.sh_T;
     need = sh.sh_rem;
     const bool all = sh.sh_all != 0;
+    const int cnt_T = sh.sh_cnt;
 #pragma unroll
     for (int i = 0; i < PT; ++i) {
       take[i] = take[i] || bk[i] > T || (all && bk[i] == T);
       act[i] = act[i] && bk[i] == T;
     }
     if (all) break;
+    if (cnt_T <= kTopkList) {
+      // rank the threshold bucket's candidates among themselves by (W desc,
+      // id asc): the `need` first ones are taken
+#pragma unroll
+      for (int i = 0; i < PT; ++i)
+        if (act[i]) {
+          const int slot = (int)atomicAdd((unsigned*)&sh.sh_len, 1u);
+          if (slot < kTopkList) {  // always: exactly cnt_T candidates append
+            sh.lw[slot] = wv[i];
+            sh.lid[slot] = j0 + i;
+          }
+        }
+      __syncthreads();
+      const int m = min(cnt_T, kTopkList);
+      int rank[PT];
+#pragma unroll
+      for (int i = 0; i < PT; ++i) rank[i] = 0;
+      bool any = false;
+#pragma unroll
+      for (int i = 0; i < PT; ++i) any = any || act[i];
+      if (any) {
+        for (int e = 0; e < m; ++e) {
+          const double w = sh.lw[e];
+          const int id = sh.lid[e];
+#pragma unroll
+          for (int i = 0; i < PT; ++i) rank[i] += (w > wv[i] || (w == wv[i] && id < j0 + i)) ? 1 : 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PT; ++i) take[i] = take[i] || (act[i] && rank[i] < need);
+      break;
+    }
   }
   // ascending output: the sink, the chosen candidates, the window
   int n_sel = 0;
@@ -190,7 +302,7 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
     }
   }
   int tot;
-  int pos = block_exclusive_scan_256(n_sel, sh.scan_tmp, &tot);
+  int pos = block_prefix_small_256<CB>(n_sel, sh.scan_o, &tot);
 #pragma unroll
   for (int i = 0; i < PT; ++i)
     if ((chosen & (1u << i)) && pos < k) out[pos++] = j0 + i;
