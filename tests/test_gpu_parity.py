@@ -854,3 +854,83 @@ def test_full_hotbuf_steps(env, ns):
         else:
             assert all(c == w.k for c in counts) if t == 0 else all(c <= w.drift for c in counts)
     check_attn(out, p.or_attn(stream[-1]))
+
+
+# fp32 summaries with a bf16 query (fp8 K), written directly rather than
+# built from a pool, at every group size: equal heads, heads one bf16 step
+# apart, products far outside fp32's range, denormal summaries, zero and
+# negative-zero query channels, blocks of very different scale.  Scores
+# bit-exact (also accumulated onto earlier layers' scores), selections equal.
+PREFILTER_CASES = ["random", "equal-heads", "one-step", "overflow", "denormal", "zeros", "mixed-scale"]
+
+
+def _prefilter_inputs(case, rng, B, Hq, D):
+    import torch
+    q = rng.standard_normal((B, Hq, D))
+    if case == "equal-heads":
+        q[:] = q[:, :1]
+    elif case == "one-step":
+        q[:] = q[:, :1]
+        qb = torch.tensor(q).to(torch.bfloat16)
+        bits = qb.view(torch.int16)
+        bits[:, 1::2, 5] += 1  # odd heads one bf16 step away in channel 5
+        q = bits.view(torch.bfloat16).double().numpy()
+    elif case == "overflow":
+        q *= 2.0 ** 100
+    elif case == "zeros":
+        q[:, ::2, ::3] = 0.0
+        q[:, 1::2, 1::3] = -0.0
+    elif case == "mixed-scale":
+        q *= 2.0 ** rng.integers(-30, 30, size=(B, Hq, 1))
+    return q
+
+
+@pytest.mark.parametrize("G", [2, 4, 8, 16])
+@pytest.mark.parametrize("case", PREFILTER_CASES)
+def test_fp32_summary_scores_adversarial(env, case, G):
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    rng = np.random.default_rng(1000 * PREFILTER_CASES.index(case) + G)
+    B, Hkv, D, S, MB = 2, 2, 128, 64, 200
+    Hq = G * Hkv
+    q = _prefilter_inputs(case, rng, B, Hq, D)
+    x = rng.standard_normal((B, Hkv, MB, 2, D))
+    if case == "overflow":
+        x *= 2.0 ** 100
+    elif case == "denormal":
+        x *= 2.0 ** -135
+    elif case == "mixed-scale":
+        x *= 2.0 ** rng.integers(-40, 40, size=(B, Hkv, MB, 1, 1))
+    x = x.astype(np.float32)
+    summ = np.stack([np.minimum(x[:, :, :, 0], x[:, :, :, 1]), np.maximum(x[:, :, :, 0], x[:, :, :, 1])], axis=3)
+    qt = torch.tensor(q).to(torch.bfloat16)
+    q64 = qt.double().numpy()
+    lens = np.array([MB * S, MB * S - 70 * S - 5], dtype=np.int32)
+    k = 24
+    L = kvs.Layout(B, Hq, Hkv, D, S, MB, B * MB, kvs.KVS_BF16, kvs.KVS_FP8_E4M3, 32)
+    OL = orc.Layout(B, Hq, Hkv, D, S, MB, B * MB, kvs.KVS_FP8_E4M3, 32)
+    dev = env.dev
+    g_summ = torch.tensor(summ).to(dev)
+    g_q = qt.to(dev)
+    g_lens = torch.tensor(lens).to(dev)
+    sel = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=dev)
+    W = torch.empty((B, Hkv, MB), dtype=torch.float64, device=dev)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=dev)
+    kvs.kvs_select_topk(L, g_q, g_summ, g_lens, k, sel, W, ws)
+    torch.cuda.synchronize()
+    oW = orc.bounds(OL, q64, summ.astype(np.float64), lens)
+    gW = W.cpu().numpy()
+    for b in range(B):
+        nb = (int(lens[b]) + S - 1) // S
+        assert np.array_equal(gW[b, :, :nb], oW[b, :, :nb]), f"{case} G={G}: scores differ (sequence {b})"
+        assert np.all(np.isneginf(gW[b, :, nb:])), "blocks past the sequence score -inf"
+    assert np.array_equal(sel.cpu().numpy(), orc.select(OL, oW, lens, k)), f"{case} G={G}: selection differs"
+    # kvs_score_blocks on the same route, accumulating onto earlier scores
+    base = torch.tensor(rng.standard_normal((B, Hkv, MB)), dtype=torch.float64, device=dev)
+    acc = base.clone()
+    kvs.kvs_score_blocks(L, g_q, g_summ, g_lens, kvs.SelectOpts(accumulate=True), None, acc, None)
+    torch.cuda.synchronize()
+    ga, bb = acc.cpu().numpy(), base.cpu().numpy()
+    for b in range(B):
+        nb = (int(lens[b]) + S - 1) // S
+        assert np.array_equal(ga[b, :, :nb], bb[b, :, :nb] + oW[b, :, :nb]), f"{case} G={G}: accumulated scores"
+    assert kvs.kvs_device_errors(clear=True) == 0
