@@ -97,6 +97,26 @@ __device__ __forceinline__ int tile_entry(const AttnArgs& a, const int32_t* srow
   return entry;
 }
 
+// The (split, KV head, sequence) a workgroup of a (nsplit, Hkv, B) grid
+// works on.  The dispatcher hands workgroups to the eight XCDs in turn
+// (workgroup w, counted x-fastest, runs on XCD w % 8), and each XCD has its
+// own L2.  Numbering the work so that consecutive ids sit on one XCD keeps a
+// unit's splits together: they share its scores, its table row and its
+// query in one L2 instead of fetching them into eight.  The map is a
+// permutation of the grid for any size (a tail of fewer than eight
+// workgroups keeps its own numbers).
+__device__ __forceinline__ void xcd_unit(int& split, int& g, int& b) {
+  const int nx = gridDim.x, ny = gridDim.y;
+  const int n = nx * ny * gridDim.z;
+  const int w = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const int per = n >> 3;  // workgroups per XCD in the whole rounds
+  const int m = w < 8 * per ? (w & 7) * per + (w >> 3) : w;
+  split = m % nx;
+  const int u = m / nx;
+  g = u % ny;
+  b = u / ny;
+}
+
 __device__ __forceinline__ int clamp_len(const AttnArgs& a, int b, bool flag_it) {
   int len = ld_uniform(a.seq_lens + b);
   const int cap = a.MB * a.S;
@@ -403,7 +423,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int split, g, b;
+  xcd_unit(split, g, b);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j4 = lane >> 4;
@@ -758,7 +779,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
 
-  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  int split, g, b;
+  xcd_unit(split, g, b);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j4 = lane >> 4;
