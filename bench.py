@@ -310,6 +310,7 @@ def main(argv=None) -> int:
     step_gbps = by["step"] / sec_per_step / 1e9
     attn_bytes = by["attention"] + (by["scores"] if fused else 0)
     attn_gbps = attn_bytes / attn_sec / 1e9
+    attn_kernel = {"bf16": "attn_mfma_kernel", "e4m3": "attn_mfma8_kernel"}.get(w.kv_dtype, "attn_valu_kernel")
 
     cpu = parity = None
     if not args.no_cpu:
@@ -347,8 +348,11 @@ def main(argv=None) -> int:
         "step_GBps": round(step_gbps, 1),
         "step_hbm_frac": round(step_gbps / PEAK_HBM_GBPS, 4),
         "roofline": {"bound": "hbm",
-                     "kernel": ("kvs_select_attn (self-selecting attn_mfma_kernel + merge_kernel)" if fused else
-                                "kvs_sparse_decode_attn (attn_mfma_kernel + merge_kernel)"),
+                     "kernel": ((f"kvs_select_attn (self-selecting {attn_kernel} + merge_kernel)" if fused else
+                                 f"kvs_sparse_decode_attn ({attn_kernel} + merge_kernel)")
+                                if kvs.kvs_attn_num_splits(L, w.k) > 1 else
+                                (f"kvs_select_attn (self-selecting {attn_kernel})" if fused else
+                                 f"kvs_sparse_decode_attn ({attn_kernel})")),
                      "achieved": round(attn_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(attn_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": measured_traffic(w.name, "select_attn" if fused else "attention"),
