@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 4
+#define KVS_ABI_VERSION 5
 
 typedef enum kvs_status {
   KVS_OK = 0,
@@ -455,6 +455,20 @@ kvs_status kvs_select_attn(const kvs_layout* layout, const void* q, const void* 
                            float sm_scale, float* out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* The paged device cache a sequence's newest block is copied from by the
+ * hot-buffer swap-in (kvs_hot_lookup_swapin, kvs_hot_swapin) when the
+ * caller passes one: the same pool, scales and block table the decode-token
+ * append writes (kvs_append_token), and the sequence lengths after it.  The
+ * pool holds layout->num_pages pages. */
+typedef struct {
+  const void* k_pool;          /* [P][Hkv][S][D] kv_dtype */
+  const void* v_pool;          /* [P][Hkv][S/T][D][T] kv_dtype */
+  const float* k_scales;       /* [P][Hkv][S][D/qg] fp32, fp8 only (else NULL) */
+  const float* v_scales;
+  const int32_t* block_table;  /* [B][MB] page ids */
+  const int32_t* seq_lens;     /* [B], the appended tokens included */
+} kvs_hot_live;
+
 /* ------------------------------------------------------------------------
  * kvs_hot_lookup_swapin -- hot-buffer page-table step and swap-in copy
  *
@@ -477,15 +491,19 @@ kvs_status kvs_select_attn(const kvs_layout* layout, const void* q, const void* 
  * Blocks in the host tier are immutable once written, so eviction needs no
  * write-back.
  *
- * Precondition: every block the hot path serves is final.  A slot is filled
- * from the host tier and never changed by an append, and kvs_append_token
- * writes a block to the host tier only when it seals it (full).  So a block
- * that is still receiving tokens -- a sequence's newest, partial block in a
- * decode loop that appends -- must not be read through KVS_TABLE_HOT: its
- * slot would hold a copy without the tokens appended since.  Callers attend
- * such a block from the paged pool (kvs_sparse_decode_attn with
- * KVS_TABLE_PAGED) or fill the host tier with its current contents before
- * each swap-in of it.
+ * The growing block.  kvs_append_token writes a block to the host tier only
+ * when it seals it (full), and a hit is never copied again, so a slot copied
+ * from the host tier cannot follow a block that is still receiving tokens
+ * (a sequence's newest block in a decode loop that appends).  With `live`
+ * non-NULL the swap-in therefore takes each unit's newest block
+ * j = (seq_lens[b] - 1) / S from the paged device cache instead: as a miss
+ * it is copied from there, and as a hit that is still resident it is copied
+ * again, at every call.  A decode step that appends, selects, then calls
+ * this and attends through KVS_TABLE_HOT reads every token appended so far;
+ * once the block fills, the last such copy holds it whole, as the host tier
+ * then does.  Page table, owners, stamps and miss lists are the same as
+ * without `live`.  With `live` NULL every block the hot path serves must be
+ * final (sealed); the newest block of an appending sequence is not.
  *
  *  layout       num_seqs, num_kv_heads, head_dim, block_size, max_blocks
  *               (page-table row length), kv_dtype, quant_group are used
@@ -504,10 +522,15 @@ kvs_status kvs_select_attn(const kvs_layout* layout, const void* q, const void* 
  *               kv_dtype (the KVS_TABLE_HOT pools)
  *  hot_k_scales/hot_v_scales  [B*Hkv*num_slots][S][D/qg] fp32 (fp8 only)
  *  miss_list    [B][Hkv][k] int32 output;  miss_count [B][Hkv] int32 output
+ *  live         NULL, or the paged cache the newest blocks are copied from
+ *               (all its pointers device memory, 16-byte aligned pools; its
+ *               pages counted by layout->num_pages)
  * Initial state of a fresh buffer: page_table, slot_owner, slot_stamp all -1.
  * Errors: INVALID_ARG (also when a host pool is not pinned), CAPACITY
  * (k > num_slots), UNSUPPORTED, HIP.  Device flags: KVS_DEVERR_SEL,
- * KVS_DEVERR_TABLE (inconsistent page table / owner state: unit skipped).
+ * KVS_DEVERR_TABLE (inconsistent page table / owner state, or a live page
+ * id out of range: that block skipped), KVS_DEVERR_SEQLEN (a live length out of
+ * [0, MB*S], clamped).
  * ---------------------------------------------------------------------- */
 kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, int32_t k,
                                  int32_t num_slots, int64_t step, int32_t* page_table,
@@ -515,7 +538,7 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, i
                                  const void* host_v, const float* host_k_scales,
                                  const float* host_v_scales, void* hot_k, void* hot_v,
                                  float* hot_k_scales, float* hot_v_scales, int32_t* miss_list,
-                                 int32_t* miss_count, void* stream);
+                                 int32_t* miss_count, const kvs_hot_live* live, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_hot_lookup + kvs_hot_swapin -- the two halves of kvs_hot_lookup_swapin
@@ -534,11 +557,13 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* layout, const int32_t* sel, i
  *   kvs_hot_lookup_swapin does.
  * kvs_hot_swapin: copies, for every unit u, the first miss_count[u] blocks
  *   of miss_list[u] from the host tier into the slot page_table[u][j] gives
- *   them (K and V tiles and fp8 scales, byte for byte).  A listed block
- *   whose page-table entry is not one of the unit's slots is skipped with
- *   KVS_DEVERR_TABLE; counts are clamped to [0, k].  It must run after the
- *   kvs_hot_lookup that wrote the list and before anything changes the page
- *   table, and before the attention that reads the slots.
+ *   them (K and V tiles and fp8 scales, byte for byte), and with `live` the
+ *   unit's newest block from the paged cache as described above.  A listed
+ *   block whose page-table entry is not one of the unit's slots is skipped
+ *   with KVS_DEVERR_TABLE; counts are clamped to [0, k].  It must run after
+ *   the kvs_hot_lookup that wrote the list and before anything changes the
+ *   page table, after the appends whose tokens it is to carry, and before
+ *   the attention that reads the slots.
  * Errors: as kvs_hot_lookup_swapin.
  * ---------------------------------------------------------------------- */
 kvs_status kvs_hot_lookup(const kvs_layout* layout, const int32_t* sel, int32_t k, int32_t num_slots,
@@ -549,7 +574,8 @@ kvs_status kvs_hot_swapin(const kvs_layout* layout, int32_t k, int32_t num_slots
                           const int32_t* page_table, const int32_t* miss_list,
                           const int32_t* miss_count, const void* host_k, const void* host_v,
                           const float* host_k_scales, const float* host_v_scales, void* hot_k,
-                          void* hot_v, float* hot_k_scales, float* hot_v_scales, void* stream);
+                          void* hot_v, float* hot_k_scales, float* hot_v_scales,
+                          const kvs_hot_live* live, void* stream);
 
 /* Workspace bytes needed by kvs_select_topk / kvs_sparse_decode_attn for this
  * layout and k; 0 when the layout or k is invalid. */

@@ -735,7 +735,7 @@ kvs_status hot_impl(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t 
                     int32_t* page_table, int32_t* slot_owner, int64_t* slot_stamp, const void* host_k,
                     const void* host_v, const float* host_k_scales, const float* host_v_scales, void* hot_k,
                     void* hot_v, float* hot_k_scales, float* hot_v_scales, int32_t* miss_list,
-                    int32_t* miss_count, void* stream, int phases) {
+                    int32_t* miss_count, const kvs_hot_live* live, void* stream, int phases) {
   const bool lookup = phases & kvs::kHotLookup, copy = phases & kvs::kHotCopy;
   kvs_status st = check_layout(L, false);
   if (st != KVS_OK) return st;
@@ -753,6 +753,13 @@ kvs_status hot_impl(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t 
     return fail(KVS_ERR_INVALID_ARG, "total hot slots overflow int32");
   if (copy && (!aligned(host_k, 16) || !aligned(host_v, 16) || !aligned(hot_k, 16) || !aligned(hot_v, 16)))
     return fail(KVS_ERR_INVALID_ARG, "host and hot pools must be 16-byte aligned");
+  if (copy && live) {
+    if (!live->k_pool || !live->v_pool || !live->block_table || !live->seq_lens ||
+        (fp8 && (!live->k_scales || !live->v_scales)))
+      return fail(KVS_ERR_INVALID_ARG, "live: pools, block_table and seq_lens (and fp8 scales) must be non-NULL");
+    if (!aligned(live->k_pool, 16) || !aligned(live->v_pool, 16))
+      return fail(KVS_ERR_INVALID_ARG, "live pools must be 16-byte aligned");
+  }
   // device aliases of the pinned host tier (hipHostMalloc memory is mapped)
   const void* host_ptrs[4] = {host_k, host_v, host_k_scales, host_v_scales};
   void* dev_ptrs[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -766,6 +773,15 @@ kvs_status hot_impl(const kvs_layout* L, const int32_t* sel, int32_t k, int32_t 
   unsigned int* err = nullptr;
   if ((st = error_word(&err)) != KVS_OK) return st;
   kvs::HotArgs a{};
+  if (copy && live) {
+    a.live_k = live->k_pool;
+    a.live_v = live->v_pool;
+    a.live_ks = fp8 ? live->k_scales : nullptr;
+    a.live_vs = fp8 ? live->v_scales : nullptr;
+    a.live_table = live->block_table;
+    a.live_lens = live->seq_lens;
+    a.P = L->num_pages;
+  }
   a.sel = sel;
   a.pt = page_table;
   a.owner = slot_owner;
@@ -807,9 +823,10 @@ kvs_status kvs_hot_lookup_swapin(const kvs_layout* L, const int32_t* sel, int32_
                                  int64_t* slot_stamp, const void* host_k, const void* host_v,
                                  const float* host_k_scales, const float* host_v_scales, void* hot_k,
                                  void* hot_v, float* hot_k_scales, float* hot_v_scales,
-                                 int32_t* miss_list, int32_t* miss_count, void* stream) {
+                                 int32_t* miss_list, int32_t* miss_count, const kvs_hot_live* live,
+                                 void* stream) {
   return hot_impl(L, sel, k, num_slots, step, page_table, slot_owner, slot_stamp, host_k, host_v, host_k_scales,
-                  host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, miss_list, miss_count, stream,
+                  host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, miss_list, miss_count, live, stream,
                   kvs::kHotLookup | kvs::kHotCopy);
 }
 
@@ -817,16 +834,18 @@ kvs_status kvs_hot_lookup(const kvs_layout* L, const int32_t* sel, int32_t k, in
                           int32_t* page_table, int32_t* slot_owner, int64_t* slot_stamp, int32_t* miss_list,
                           int32_t* miss_count, void* stream) {
   return hot_impl(L, sel, k, num_slots, step, page_table, slot_owner, slot_stamp, nullptr, nullptr, nullptr,
-                  nullptr, nullptr, nullptr, nullptr, nullptr, miss_list, miss_count, stream, kvs::kHotLookup);
+                  nullptr, nullptr, nullptr, nullptr, nullptr, miss_list, miss_count, nullptr, stream,
+                  kvs::kHotLookup);
 }
 
 kvs_status kvs_hot_swapin(const kvs_layout* L, int32_t k, int32_t num_slots, const int32_t* page_table,
                           const int32_t* miss_list, const int32_t* miss_count, const void* host_k,
                           const void* host_v, const float* host_k_scales, const float* host_v_scales,
-                          void* hot_k, void* hot_v, float* hot_k_scales, float* hot_v_scales, void* stream) {
+                          void* hot_k, void* hot_v, float* hot_k_scales, float* hot_v_scales,
+                          const kvs_hot_live* live, void* stream) {
   return hot_impl(L, nullptr, k, num_slots, 0, const_cast<int32_t*>(page_table), nullptr, nullptr, host_k, host_v,
                   host_k_scales, host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales,
-                  const_cast<int32_t*>(miss_list), const_cast<int32_t*>(miss_count), stream, kvs::kHotCopy);
+                  const_cast<int32_t*>(miss_list), const_cast<int32_t*>(miss_count), live, stream, kvs::kHotCopy);
 }
 
 }  // extern "C"

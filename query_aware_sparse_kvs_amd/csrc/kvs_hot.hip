@@ -17,7 +17,9 @@
 // swapin_copy_kernel: two workgroups per unit, each copying every other
 //   miss's K and V tiles (and fp8 scales) from pinned host memory into its
 //   hot slot with 16-byte loads, a tile's loads all issued before its
-//   stores.  Bound by the host link.
+//   stores; with a live cache, the unit's newest block (still receiving
+//   tokens, never in the host tier whole) comes from the device pool, hit
+//   or miss.  Bound by the host link.
 #include "kvs_internal.h"
 
 namespace kvs {
@@ -145,63 +147,102 @@ __global__ __launch_bounds__(256) void hot_lookup_kernel(HotArgs a) {
   }
 }
 
-// Copy workgroups per unit: each takes every kCopyGroups-th miss of its unit.
+// Copy workgroups per unit: each takes every kCopyGroups-th block to copy.
 // Few workgroups suffice to keep the host link busy (two tiles of 16 KiB per
 // workgroup in flight), and they leave most SIMDs free for kernels that run
 // beside the copy (the attention of another layer).
 constexpr int kCopyGroups = 2;
 
+// One tile (K, V, and fp8 scales) copied by a workgroup, 16-byte vectors.
+__device__ __forceinline__ void copy_tile(const HotArgs& a, const char* sk, const char* sv, const float* ssk,
+                                          const float* ssv, long long slot, long long tile_bytes) {
+  const int tid = threadIdx.x;
+  const int n16 = (int)(tile_bytes / 16);
+  constexpr int kMaxPer = 8;  // 16-byte vectors per thread per round
+  const u32x4* k16 = reinterpret_cast<const u32x4*>(sk);
+  const u32x4* v16 = reinterpret_cast<const u32x4*>(sv);
+  u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_k) + slot * tile_bytes);
+  u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_v) + slot * tile_bytes);
+  for (int x0 = 0; x0 < n16; x0 += 256 * kMaxPer) {
+    u32x4 bk[kMaxPer], bv[kMaxPer];
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int x = x0 + q * 256 + tid;
+      bk[q] = bv[q] = u32x4{0u, 0u, 0u, 0u};
+      if (x < n16) {
+        bk[q] = k16[x];
+        bv[q] = v16[x];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxPer; ++q) {
+      const int x = x0 + q * 256 + tid;
+      if (x < n16) {
+        dk[x] = bk[q];
+        dv[x] = bv[q];
+      }
+    }
+  }
+  if (a.qg > 0) {
+    const int ns_per_tile = a.S * (a.D / a.qg);
+    float* dsk = a.hot_ks + slot * ns_per_tile;
+    float* dsv = a.hot_vs + slot * ns_per_tile;
+    for (int x = tid; x < ns_per_tile; x += 256) {
+      dsk[x] = ssk[x];
+      dsv[x] = ssv[x];
+    }
+  }
+}
+
+// The unit's misses, in list order, come from the host tier.  With a live
+// cache the unit's newest block comes from it instead: as a miss (then it is
+// the list's last entry, misses being ascending and the newest block the
+// highest id a selection holds) or, when it is resident anyway, as one more
+// item.  (A selection holding ids past the sequence can list it earlier; it
+// is then copied twice, from the same source.)
 __global__ __launch_bounds__(256) void swapin_copy_kernel(HotArgs a) {
   const int u = blockIdx.y, tid = threadIdx.x;
   int m = a.miss_count[u];
   m = m < 0 ? 0 : (m > a.k ? a.k : m);  // miss_list holds k entries per unit
   const long long tile_bytes = (long long)a.S * a.D * a.elem_bytes;
-  const int n16 = (int)(tile_bytes / 16);
-  constexpr int kMaxPer = 8;  // 16-byte vectors per thread per round
-  for (int r = blockIdx.x; r < m; r += kCopyGroups) {  // m is uniform over the workgroup
-    const int j = a.miss_list[(long long)u * a.k + r];
+  const int ns_per_tile = a.qg > 0 ? a.S * (a.D / a.qg) : 0;
+  const int b = u / a.Hkv, g = u % a.Hkv;
+  int newest = -1;  // the unit's newest block, taken from the live cache
+  int items = m;
+  if (a.live_k) {
+    int len = a.live_lens[b];
+    const int cap = a.MB * a.S;
+    if (len < 0 || len > cap) {
+      if (tid == 0 && blockIdx.x == 0 && g == 0) raise_flag(a.err, 0x1u);
+      len = len < 0 ? 0 : cap;
+    }
+    newest = len > 0 ? (len - 1) / a.S : -1;
+    const bool listed = m > 0 && a.miss_list[(long long)u * a.k + m - 1] == newest;
+    if (newest >= 0 && !listed && a.pt[(long long)u * a.MB + newest] >= 0) items = m + 1;
+  }
+  for (int r = blockIdx.x; r < items; r += kCopyGroups) {  // items is uniform over the workgroup
+    const int j = r < m ? a.miss_list[(long long)u * a.k + r] : newest;
     if (j < 0 || j >= a.MB) continue;
     const int slot = a.pt[(long long)u * a.MB + j];
     if (slot < u * a.ns || slot >= (u + 1) * a.ns) {
       if (tid == 0) raise_flag(a.err, 0x2u);
       continue;
     }
-    const long long src_off = ((long long)u * a.MB + j) * tile_bytes;
-    const long long dst_off = (long long)slot * tile_bytes;
-    const u32x4* sk = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_k) + src_off);
-    const u32x4* sv = reinterpret_cast<const u32x4*>(static_cast<const char*>(a.host_v) + src_off);
-    u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_k) + dst_off);
-    u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.hot_v) + dst_off);
-    for (int x0 = 0; x0 < n16; x0 += 256 * kMaxPer) {
-      u32x4 bk[kMaxPer], bv[kMaxPer];
-#pragma unroll
-      for (int q = 0; q < kMaxPer; ++q) {
-        const int x = x0 + q * 256 + tid;
-        bk[q] = bv[q] = u32x4{0u, 0u, 0u, 0u};
-        if (x < n16) {
-          bk[q] = sk[x];
-          bv[q] = sv[x];
-        }
+    if (j == newest) {  // from the live cache
+      const int page = a.live_table[(long long)b * a.MB + j];
+      if (page < 0 || page >= a.P) {
+        if (tid == 0) raise_flag(a.err, 0x2u);
+        continue;
       }
-#pragma unroll
-      for (int q = 0; q < kMaxPer; ++q) {
-        const int x = x0 + q * 256 + tid;
-        if (x < n16) {
-          dk[x] = bk[q];
-          dv[x] = bv[q];
-        }
-      }
-    }
-    if (a.qg > 0) {
-      const int ns_per_tile = a.S * (a.D / a.qg);
-      const float* ssk = a.host_ks + ((long long)u * a.MB + j) * ns_per_tile;
-      const float* ssv = a.host_vs + ((long long)u * a.MB + j) * ns_per_tile;
-      float* dsk = a.hot_ks + (long long)slot * ns_per_tile;
-      float* dsv = a.hot_vs + (long long)slot * ns_per_tile;
-      for (int x = tid; x < ns_per_tile; x += 256) {
-        dsk[x] = ssk[x];
-        dsv[x] = ssv[x];
-      }
+      const long long t = (long long)page * a.Hkv + g;
+      copy_tile(a, static_cast<const char*>(a.live_k) + t * tile_bytes,
+                static_cast<const char*>(a.live_v) + t * tile_bytes, a.live_ks + t * ns_per_tile,
+                a.live_vs + t * ns_per_tile, slot, tile_bytes);
+    } else {  // from the host tier
+      const long long t = (long long)u * a.MB + j;
+      copy_tile(a, static_cast<const char*>(a.host_k) + t * tile_bytes,
+                static_cast<const char*>(a.host_v) + t * tile_bytes, a.host_ks + t * ns_per_tile,
+                a.host_vs + t * ns_per_tile, slot, tile_bytes);
     }
   }
 }

@@ -237,6 +237,15 @@ struct HotArgs {
   unsigned int* err;
   int64_t step;
   int32_t B, Hkv, D, S, MB, k, ns, n2, qg, elem_bytes;
+  // the paged cache each unit's newest block is copied from (live_k null:
+  // every block comes from the host tier)
+  const void* live_k;
+  const void* live_v;
+  const float* live_ks;
+  const float* live_vs;
+  const int32_t* live_table;  // [B][MB]
+  const int32_t* live_lens;   // [B]
+  int32_t P;                  // pages of that cache
 };
 
 // launchers (return the launch status); kinds/shapes are validated by the

@@ -80,6 +80,11 @@ class _CAppendArgs(ctypes.Structure):
         "k_scales", "v_scales", "host_k", "host_v", "host_k_scales", "host_v_scales")]
 
 
+class _CHotLive(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "k_pool", "v_pool", "k_scales", "v_scales", "block_table", "seq_lens")]
+
+
 class _CSelectOpts(ctypes.Structure):
     _fields_ = [("recent_blocks", ctypes.c_int32), ("use_ema", ctypes.c_int32),
                 ("ema_alpha", ctypes.c_double), ("ema_state", ctypes.c_void_p),
@@ -106,6 +111,18 @@ class AppendArgs:
     host_v: torch.Tensor | None = None
     host_k_scales: torch.Tensor | None = None
     host_v_scales: torch.Tensor | None = None
+
+
+@dataclass
+class HotLive:
+    """Tensors of kvs_hot_live (include/kvs.h): the paged device cache the
+    hot-buffer swap-in copies each sequence's newest block from."""
+    k_pool: torch.Tensor
+    v_pool: torch.Tensor
+    k_scales: torch.Tensor | None
+    v_scales: torch.Tensor | None
+    block_table: torch.Tensor
+    seq_lens: torch.Tensor
 
 
 @dataclass
@@ -140,9 +157,9 @@ def _load():
         "kvs_select_attn": (i32, [LP, P, P, P, P, P, P, P, P, i32, i32, P, ctypes.c_float, P, P, sz, P]),
         "kvs_select_topk_ex": (i32, [LP, P, P, P, i32, ctypes.POINTER(_CSelectOpts),
                                      ctypes.POINTER(_CAppendArgs), P, P, P, sz, P]),
-        "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "kvs_hot_lookup_swapin": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvs_hot_lookup": (i32, [LP, P, i32, i32, i64, P, P, P, P, P, P]),
-        "kvs_hot_swapin": (i32, [LP, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P]),
+        "kvs_hot_swapin": (i32, [LP, i32, i32, P, P, P, P, P, P, P, P, P, P, P, P, P]),
         "kvs_select_workspace_size": (sz, [LP, i32]),
         "kvs_attn_workspace_size": (sz, [LP, i32]),
         "kvs_attn_num_splits": (i32, [LP, i32]),
@@ -280,6 +297,21 @@ def kvs_select_topk_append(layout: Layout, q, k_pool, k_scales, block_table, seq
         _ptr(bounds_out, "bounds_out", torch.float64, L.num_seqs * L.num_kv_heads * L.max_blocks),
         ws, workspace.numel() if workspace is not None else 0,
         _stream(stream)), "kvs_select_topk_append")
+
+
+def _live_struct(L: Layout, a: HotLive | None):
+    if a is None:
+        return None
+    tile = L.num_kv_heads * L.block_size * L.head_dim
+    qg = L.quant_group
+    dt = _pool_dtype(L)
+    return ctypes.byref(_CHotLive(
+        _ptr(a.k_pool, "live k_pool", dt, L.num_pages * tile),
+        _ptr(a.v_pool, "live v_pool", dt, L.num_pages * tile),
+        _ptr(a.k_scales, "live k_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(a.v_scales, "live v_scales", torch.float32, L.num_pages * tile // qg if qg else None),
+        _ptr(a.block_table, "live block_table", torch.int32, L.num_seqs * L.max_blocks),
+        _ptr(a.seq_lens, "live seq_lens", torch.int32, L.num_seqs)))
 
 
 def _append_struct(L: Layout, a: AppendArgs) -> _CAppendArgs:
@@ -439,7 +471,7 @@ def kvs_sparse_decode_attn_noalloc(layout: Layout, table_kind: int, q, k_pool, v
 def kvs_hot_lookup_swapin(layout: Layout, sel, k: int, num_slots: int, step: int, page_table,
                           slot_owner, slot_stamp, host_k, host_v, host_k_scales, host_v_scales,
                           hot_k, hot_v, hot_k_scales, hot_v_scales, miss_list, miss_count,
-                          stream=None) -> None:
+                          stream=None, live: HotLive | None = None) -> None:
     L = layout
     units = L.num_seqs * L.num_kv_heads
     tile = L.block_size * L.head_dim
@@ -462,6 +494,7 @@ def kvs_hot_lookup_swapin(layout: Layout, sel, k: int, num_slots: int, step: int
         _ptr(hot_v_scales, "hot_v_scales", torch.float32, hot_n // qg if qg else None),
         _ptr(miss_list, "miss_list", torch.int32, units * k),
         _ptr(miss_count, "miss_count", torch.int32, units),
+        _live_struct(L, live),
         _stream(stream)), "kvs_hot_lookup_swapin")
 
 
@@ -481,7 +514,8 @@ def kvs_hot_lookup(layout: Layout, sel, k: int, num_slots: int, step: int, page_
 
 
 def kvs_hot_swapin(layout: Layout, k: int, num_slots: int, page_table, miss_list, miss_count, host_k, host_v,
-                   host_k_scales, host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, stream=None) -> None:
+                   host_k_scales, host_v_scales, hot_k, hot_v, hot_k_scales, hot_v_scales, stream=None,
+                   live: HotLive | None = None) -> None:
     L = layout
     units = L.num_seqs * L.num_kv_heads
     tile = L.block_size * L.head_dim
@@ -501,6 +535,7 @@ def kvs_hot_swapin(layout: Layout, k: int, num_slots: int, page_table, miss_list
         _ptr(hot_v, "hot_v", _pool_dtype(L), hot_n),
         _ptr(hot_k_scales, "hot_k_scales", torch.float32, hot_n // qg if qg else None),
         _ptr(hot_v_scales, "hot_v_scales", torch.float32, hot_n // qg if qg else None),
+        _live_struct(L, live),
         _stream(stream)), "kvs_hot_swapin")
 
 

@@ -135,7 +135,10 @@ class HotBufferStep:
     """One layer's decode step with a hot device buffer over a pinned host
     tier (page "KV 稀疏化", §7 "HiSparse"): page-table lookup, LRU slot
     assignment and swap-in of the missed blocks, then attention through the
-    hot page table.  State starts empty (every entry -1)."""
+    hot page table.  State starts empty (every entry -1).  In a decode loop
+    that appends tokens, pass `live` (the paged cache the append writes) to
+    the swap-in, after the append: each sequence's newest block, which the
+    host tier does not hold until it is sealed, is then copied from there."""
 
     def __init__(self, layout: kvs.Layout, k: int, num_slots: int, device="cuda"):
         L = layout
@@ -165,22 +168,24 @@ class HotBufferStep:
         self.attn_ws = torch.zeros(max(kvs.kvs_attn_workspace_size(self.hot_layout, k), 1), dtype=torch.uint8, device=dev)
         self.sm_scale = 1.0 / math.sqrt(L.head_dim)
 
-    def swap_in(self, step, sel, host_k, host_v, host_ks=None, host_vs=None, stream=None):
+    def swap_in(self, step, sel, host_k, host_v, host_ks=None, host_vs=None, stream=None,
+                live: kvs.HotLive | None = None):
         kvs.kvs_hot_lookup_swapin(self.host_layout, sel, self.k, self.ns, step, self.page_table,
                                   self.slot_owner, self.slot_stamp, host_k, host_v, host_ks, host_vs,
                                   self.hot_k, self.hot_v, self.hot_ks, self.hot_vs, self.miss_list,
-                                  self.miss_count, stream)
+                                  self.miss_count, stream, live=live)
 
     def lookup(self, step, sel, stream=None):
         """The page-table step alone (hits, miss list, LRU victims)."""
         kvs.kvs_hot_lookup(self.host_layout, sel, self.k, self.ns, step, self.page_table, self.slot_owner,
                            self.slot_stamp, self.miss_list, self.miss_count, stream)
 
-    def copy(self, host_k, host_v, host_ks=None, host_vs=None, stream=None):
-        """The copy of the misses the last lookup listed."""
+    def copy(self, host_k, host_v, host_ks=None, host_vs=None, stream=None, live: kvs.HotLive | None = None):
+        """The copy of the misses the last lookup listed (and, with `live`,
+        of each sequence's newest block from the paged cache)."""
         kvs.kvs_hot_swapin(self.host_layout, self.k, self.ns, self.page_table, self.miss_list, self.miss_count,
                            host_k, host_v, host_ks, host_vs, self.hot_k, self.hot_v, self.hot_ks, self.hot_vs,
-                           stream)
+                           stream, live=live)
 
     def attend(self, q, sel, seq_lens, stream=None) -> torch.Tensor:
         kvs.kvs_sparse_decode_attn(self.hot_layout, kvs.KVS_TABLE_HOT, q, self.hot_k, self.hot_v,
@@ -188,8 +193,9 @@ class HotBufferStep:
                                    self.sm_scale, self.out, self.attn_ws, stream)
         return self.out
 
-    def run(self, step, sel, q, seq_lens, host_k, host_v, host_ks=None, host_vs=None, stream=None):
-        self.swap_in(step, sel, host_k, host_v, host_ks, host_vs, stream)
+    def run(self, step, sel, q, seq_lens, host_k, host_v, host_ks=None, host_vs=None, stream=None,
+            live: kvs.HotLive | None = None):
+        self.swap_in(step, sel, host_k, host_v, host_ks, host_vs, stream, live=live)
         return self.attend(q, sel, seq_lens, stream)
 
 
@@ -211,7 +217,10 @@ class HotPrefetchPipeline:
     copies, and the copy stream carries only copies, back to back.  Every
     lookup follows, on the compute stream, the earlier attentions of its
     buffer; with lookups two layers ahead that needs at least three
-    buffers.  Both streams keep the default priority."""
+    buffers.  Both streams keep the default priority.  The copies run ahead
+    of their layers' steps, so they take every block from the host tier: a
+    decode loop that appends tokens (whose newest blocks the host tier does
+    not hold yet) uses HotBufferStep with a live source instead."""
 
     def __init__(self, steps: list, device="cuda", copy_ahead: int = 2):
         if len(steps) < 3:

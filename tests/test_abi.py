@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(kvs):
 
 
 def test_abi_version_and_status_strings(kvs):
-    assert kvs.kvs_abi_version() == 4
+    assert kvs.kvs_abi_version() == 5
     for st in range(5):
         assert kvs.kvs_status_string(st).startswith("KVS_")
     assert "unknown" in kvs.kvs_status_string(99)
@@ -132,7 +132,7 @@ def test_summaries_and_hot_argument_checks(kvs):
 
     def hot(k, ns, step=0):
         return lib.kvs_hot_lookup_swapin(c, FAKE, k, ns, step, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
-                                         FAKE, FAKE, None, None, FAKE, FAKE, None)
+                                         FAKE, FAKE, None, None, FAKE, FAKE, None, None)
     assert hot(8, 4) == kvs.KVS_ERR_CAPACITY
     assert hot(4, 5000) == kvs.KVS_ERR_UNSUPPORTED
     assert hot(0, 4) == kvs.KVS_ERR_INVALID_ARG
@@ -224,9 +224,9 @@ def test_split_hot_calls_argument_checks(kvs):
     def look(k=4, ns=4, step=0, sel=FAKE, owner=FAKE):
         return lib.kvs_hot_lookup(c, sel, k, ns, step, FAKE, owner, FAKE, FAKE, FAKE, None)
 
-    def copy(k=4, ns=4, host_k=FAKE, hot_v=FAKE, layout=c):
+    def copy(k=4, ns=4, host_k=FAKE, hot_v=FAKE, layout=c, live=None):
         return lib.kvs_hot_swapin(layout, k, ns, FAKE, FAKE, FAKE, host_k, FAKE, None, None, FAKE, hot_v,
-                                  None, None, None)
+                                  None, None, live, None)
     assert look(k=8, ns=4) == kvs.KVS_ERR_CAPACITY
     assert look(ns=5000) == kvs.KVS_ERR_UNSUPPORTED
     assert look(k=0) == kvs.KVS_ERR_INVALID_ARG
@@ -239,3 +239,17 @@ def test_split_hot_calls_argument_checks(kvs):
     assert copy(hot_v=0x100004) == kvs.KVS_ERR_INVALID_ARG  # misaligned
     fp8 = _layout(kvs, kv_dtype=kvs.KVS_FP8_E4M3, quant_group=32)
     assert copy(layout=ctypes.byref(fp8.c())) == kvs.KVS_ERR_INVALID_ARG  # fp8 without scales
+
+    # the live cache the newest blocks come from: every pointer, aligned pools, fp8 scales
+    def live(**kw):
+        f = {n: FAKE.value for n, _ in kvs._CHotLive._fields_}
+        f.update(k_scales=None, v_scales=None)
+        f.update(kw)
+        return ctypes.byref(kvs._CHotLive(**f))
+    for bad in (live(k_pool=None), live(v_pool=None), live(block_table=None), live(seq_lens=None),
+                live(v_pool=0x100004)):
+        assert copy(live=bad) == kvs.KVS_ERR_INVALID_ARG
+        assert "live" in kvs.kvs_last_error()
+    fp8_hot = lambda lv: lib.kvs_hot_swapin(ctypes.byref(fp8.c()), 4, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, FAKE, FAKE, lv, None)
+    assert fp8_hot(live()) == kvs.KVS_ERR_INVALID_ARG and "live" in kvs.kvs_last_error()

@@ -574,3 +574,109 @@ def test_select_attn_empty_short_and_all_block_sequences(env, base, over):
     assert np.array_equal(sel.cpu().numpy(), o_sel)
     assert (sel[0] == -1).all() and (out[0] == 0).all()
     check_attn(out, p.or_attn(o_sel))
+
+
+HOT_APPEND_CASES = [
+    # (name, workload, overrides, first lengths, steps, k, hot slots per unit)
+    ("bf16-s16-d64", "llama8b", {"B": 2, "L": 16 * 12, "S": 16, "D": 64, "Hq": 8, "Hkv": 2, "layers": 1,
+                                 "heavy": "none"}, [16 * 4 - 3, 16 * 2 + 5], 36, 5, 7),
+    ("fp8-s32-qg32", "longfp8", {"B": 2, "L": 32 * 8, "S": 32}, [32 * 3 - 2, 40], 40, 4, 6),
+]
+
+
+@pytest.mark.parametrize("case", HOT_APPEND_CASES, ids=[c[0] for c in HOT_APPEND_CASES])
+def test_hot_buffer_decode_loop_with_appends(env, case):
+    """A decode loop over the hot buffer (page "KV 稀疏化", §7) that appends a
+    token every step, across block boundaries: kvs_append_token (full blocks
+    sealed to the host tier), the selection on the updated summaries, the
+    swap-in with the paged cache as the live source of each sequence's
+    newest block, and the attention through the hot table.  Every step
+    against the oracle: pools, host tier and summaries, the selection, page
+    table, owners, stamps, miss lists and counts bit-exact; every resident
+    slot byte-equal to its block in the host tier, the newest block's to the
+    paged cache; attention within the bars.  Without the live source the
+    newest block's slot would miss the tokens appended after its copy."""
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    from query_aware_sparse_kvs_amd.step import HotBufferStep
+    from test_gpu_parity import check_attn
+    name, base, over, lens0, steps, k, ns = case
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    c = Cache(env, w, lens0, seed=31)
+    p, L = c.p, c.p.L
+    S, Hkv, MB = L.block_size, L.num_kv_heads, L.max_blocks
+    units = L.num_seqs * Hkv
+    # the blocks already full before the loop are in the host tier, as their
+    # seal would have put them
+    table = p.h["table"]
+    per_tile = {"k": S * L.head_dim, "s": S * (L.head_dim // L.quant_group) if c.fp8 else 0}
+    for b, n in enumerate(lens0):
+        for j in range(n // S):
+            for g in range(Hkv):
+                u, t = b * Hkv + g, table[b, j] * Hkv + g
+                for hn, pn, sz in (("host_k", "k_pool", "k"), ("host_v", "v_pool", "k"),
+                                   ("host_k_scales", "k_scales", "s"), ("host_v_scales", "v_scales", "s")):
+                    if hn not in c.host:
+                        continue
+                    n_el = per_tile[sz]
+                    src_t = p.inp[pn].view(-1)[t * n_el:(t + 1) * n_el].cpu()
+                    c.host[hn].view(-1)[(u * MB + j) * n_el:(u * MB + j + 1) * n_el] = src_t
+                    c.o_host[hn].reshape(-1)[(u * MB + j) * n_el:(u * MB + j + 1) * n_el] = \
+                        c.o[pn].reshape(-1)[t * n_el:(t + 1) * n_el]
+    hs = HotBufferStep(L, k, ns, env.dev)
+    live = kvs.HotLive(p.inp["k_pool"], p.inp["v_pool"], p.inp["k_scales"], p.inp["v_scales"],
+                       p.inp["block_table"], p.inp["seq_lens"])
+    pt = np.full((units, MB), -1, np.int32)
+    owner = np.full((units, ns), -1, np.int32)
+    stamp = np.full((units, ns), -1, np.int64)
+    host = [c.host.get(n) for n in ("host_k", "host_v", "host_k_scales", "host_v_scales")]
+    print(f"[hot-append {name}] lens {lens0} -> +{steps}, k {k}, slots {ns}", flush=True)
+    for t in range(steps):
+        tok = c.new_token()
+        c.set_lens(c.lens + 1)
+        lens = c.lens.astype(np.int32)
+        kvs.kvs_append_token(L, c.args(tok), p.inp["seq_lens"], c.summ)
+        c.oracle_append(tok, lens)
+        c.check(f"step {t}")
+        sel, _ = p.gpu_select(c.summ, k, with_bounds=False)
+        osel = orc.select(p.OL, orc.bounds(p.OL, p.h["q"], c.o_summ, lens), lens, k)
+        assert np.array_equal(sel.cpu().numpy(), osel), f"step {t}: selection differs"
+        hs.swap_in(t, sel, *host, live=live)
+        misses, counts = [], []
+        for u in range(units):
+            m, cnt = orc.hot_step(MB, ns, t, u * ns, osel.reshape(units, -1)[u], pt[u], owner[u], stamp[u])
+            misses.append(m)
+            counts.append(cnt)
+        assert np.array_equal(hs.page_table.cpu().numpy().reshape(units, -1), pt), f"step {t}: page table"
+        assert np.array_equal(hs.slot_owner.cpu().numpy().reshape(units, -1), owner), f"step {t}: owners"
+        assert np.array_equal(hs.slot_stamp.cpu().numpy().reshape(units, -1), stamp), f"step {t}: stamps"
+        assert np.array_equal(hs.miss_list.cpu().numpy().reshape(units, -1), np.stack(misses)), f"step {t}"
+        assert np.array_equal(hs.miss_count.cpu().numpy().reshape(-1), np.array(counts)), f"step {t}"
+        no_device_errors(env)
+        # slot contents: the newest block from the paged cache, the others from the host tier
+        hot = {"k": hs.hot_k, "v": hs.hot_v, "ks": hs.hot_ks, "vs": hs.hot_vs}
+        pools = {"k": p.inp["k_pool"], "v": p.inp["v_pool"], "ks": p.inp["k_scales"], "vs": p.inp["v_scales"]}
+        hosts = {"k": host[0], "v": host[1], "ks": host[2], "vs": host[3]}
+        for key in ("k", "v", "ks", "vs"):
+            if hot[key] is None:
+                continue
+            n_el = hot[key].numel() // (units * ns)
+            hv = hot[key].cpu().reshape(units * ns, n_el)
+            pv = pools[key].cpu().reshape(-1, n_el)
+            hh = hosts[key].reshape(units * MB, n_el)
+            for u in range(units):
+                b, g = divmod(u, Hkv)
+                newest = (int(lens[b]) - 1) // S
+                for s in range(ns):
+                    j = int(owner[u, s])
+                    if j < 0:
+                        continue
+                    want = pv[table[b, j] * Hkv + g] if j == newest else hh[u * MB + j]
+                    got = hv[u * ns + s]
+                    if got.dtype == torch.bfloat16:  # compare bit patterns
+                        got, want = got.view(torch.int16), want.view(torch.int16)
+                    assert torch.equal(got, want), f"step {t}: slot {s} of unit {u} (block {j}, {key})"
+        out = hs.attend(p.inp["q"], sel, p.inp["seq_lens"])
+        no_device_errors(env)
+        ref = orc.sparse_attn(p.OL, p.h["q"], c.o["k_pool"], c.o["v_pool"], c.o["k_scales"], c.o["v_scales"],
+                              table, lens, osel, p.sm_scale)
+        check_attn(out, ref)
