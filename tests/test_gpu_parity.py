@@ -934,3 +934,30 @@ def test_fp32_summary_scores_adversarial(env, case, G):
         nb = (int(lens[b]) + S - 1) // S
         assert np.array_equal(ga[b, :, :nb], bb[b, :, :nb] + oW[b, :, :nb]), f"{case} G={G}: accumulated scores"
     assert kvs.kvs_device_errors(clear=True) == 0
+
+
+@pytest.mark.parametrize("B", [64, 128])
+def test_matrix_core_selection_multi_tile(env, B):
+    """The matrix-core selection at sizes where each scoring wavefront takes
+    two (B = 64) or four (B = 128) 16-block tiles, with a ragged last chunk
+    (520 blocks per row) and ragged lengths: selections bit-exact against
+    the oracle's exact scores.  Summaries are written directly (bf16,
+    min <= max), so no pool is needed at this size."""
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    Hkv, G, D, S, MB, k = 4, 8, 128, 64, 520, 32
+    rng = np.random.default_rng(50 + B)
+    q = torch.tensor(rng.standard_normal((B, Hkv * G, D)), dtype=torch.float32).to(torch.bfloat16)
+    x = torch.tensor(rng.standard_normal((B, Hkv, MB, 2, D)), dtype=torch.float32).to(torch.bfloat16)
+    summ = torch.stack([torch.minimum(x[:, :, :, 0], x[:, :, :, 1]), torch.maximum(x[:, :, :, 0], x[:, :, :, 1])],
+                       dim=3)
+    lens = rng.integers(1, MB * S + 1, size=B).astype(np.int32)
+    lens[:4] = [MB * S, MB * S - 63, 64 * 40 + 1, 1]
+    L = kvs.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_BF16, kvs.KVS_BF16)
+    assert kvs.kvs_select_uses_matrix_cores(L, k) == 1
+    OL = orc.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_BF16)
+    sel = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=env.dev)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    kvs.kvs_select_topk(L, q.to(env.dev), summ.to(env.dev), torch.tensor(lens).to(env.dev), k, sel, None, ws)
+    no_device_errors(env)
+    oW = orc.bounds(OL, q.double().numpy(), summ.double().numpy(), lens)
+    assert np.array_equal(sel.cpu().numpy(), orc.select(OL, oW, lens, k))
