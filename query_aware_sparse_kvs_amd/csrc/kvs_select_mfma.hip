@@ -87,11 +87,10 @@ __device__ __forceinline__ int scan_512(int v, int* tmp, int* total) {
 }
 
 // ---------------------------------------------------------------------------
-// scores32_kernel: grid (MB/(64*TPW) chunks, Hkv, B), 256 threads; each
-// wavefront scores TPW tiles of 16 blocks, all their loads issued first
+// scores32_kernel: grid (MB/64 chunks, Hkv, B), 256 threads
 // ---------------------------------------------------------------------------
-template <int D, int TPW>
-__global__ __launch_bounds__(256, TPW > 1 ? 2 : 4) void scores32_kernel(SelMfmaArgs a) {
+template <int D>
+__global__ __launch_bounds__(256, 4) void scores32_kernel(SelMfmaArgs a) {
   constexpr int HC = D / 32;  // 32-channel chunks per summary half
   constexpr int KC = 2 * HC;  // chunks of the [max | min] row
   const int g = blockIdx.y, b = blockIdx.z;
@@ -107,22 +106,18 @@ __global__ __launch_bounds__(256, TPW > 1 ? 2 : 4) void scores32_kernel(SelMfmaA
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j4 = lane >> 4;
   const int G = a.G, MB = a.MB;
-  const int jt0 = (blockIdx.x * 4 + wave) * 16 * TPW;  // this wavefront's first block
-  if (jt0 >= MB) return;  // uniform over the wavefront; no barrier below
+  const int jt = (blockIdx.x * 4 + wave) * 16;  // this wavefront's 16 blocks
+  if (jt >= MB) return;  // uniform over the wavefront; no barrier below
   const uint16_t* summ = static_cast<const uint16_t*>(a.summ) + ((long long)b * a.Hkv + g) * MB * 2 * D;
   const uint16_t* qrow0 = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G) * D;
-  // A operands (summary rows, max half first) of every tile before anything
-  // else: rows past the array read the last row instead (never stored), so
-  // the loads carry no branch
-  u32x4 ar[TPW][KC];
+  // A operand (summary rows, max half first) before anything else
+  u32x4 ar[KC];
+  const int j = jt + r;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int j = min(jt0 + 16 * t + r, MB - 1);
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int off = kc < HC ? D + kc * 32 : (kc - HC) * 32;
-      ar[t][kc] = *reinterpret_cast<const u32x4*>(summ + (long long)j * 2 * D + off + 8 * j4);
-    }
+  for (int kc = 0; kc < KC; ++kc) {
+    ar[kc] = u32x4{0u, 0u, 0u, 0u};
+    const int off = kc < HC ? D + kc * 32 : (kc - HC) * 32;
+    if (j < MB) ar[kc] = *reinterpret_cast<const u32x4*>(summ + (long long)j * 2 * D + off + 8 * j4);
   }
   u32x4 qs[KC];  // B operand: [q+ | q-] of head r
 #pragma unroll
@@ -133,33 +128,29 @@ __global__ __launch_bounds__(256, TPW > 1 ? 2 : 4) void scores32_kernel(SelMfmaA
     split_sign(v, qs[cs], neg, negabs);
     qs[HC + cs] = neg;
   }
+  f32x4_t u = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, ab = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) {
+    u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[kc]), as_bf(qs[kc]), u, 0, 0, 0);
+    ab = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[kc] & 0x7FFF7FFFu), as_bf(qs[kc] & 0x7FFF7FFFu), ab, 0, 0,
+                                                 0);
+  }
+  // lane (r, j4) holds blocks jt + 4*j4 + e of head r: max over the heads
   float* w32 = a.w32 + ((long long)b * a.Hkv + g) * MB;
   float* amag = a.amag + ((long long)b * a.Hkv + g) * MB;
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int jt = jt0 + 16 * t;
-    f32x4_t u = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, ab = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = 0; e < 4; ++e) {
+    float v = r < G ? u[e] : -__builtin_inff();
+    float m = r < G ? ab[e] : 0.0f;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[t][kc]), as_bf(qs[kc]), u, 0, 0, 0);
-      ab = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf(ar[t][kc] & 0x7FFF7FFFu), as_bf(qs[kc] & 0x7FFF7FFFu), ab,
-                                                   0, 0, 0);
+    for (int off = 1; off < 16; off <<= 1) {
+      v = fmaxf(v, __shfl_xor(v, off));
+      m = fmaxf(m, __shfl_xor(m, off));
     }
-    // lane (r, j4) holds blocks jt + 4*j4 + e of head r: max over the heads
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float v = r < G ? u[e] : -__builtin_inff();
-      float m = r < G ? ab[e] : 0.0f;
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) {
-        v = fmaxf(v, __shfl_xor(v, off));
-        m = fmaxf(m, __shfl_xor(m, off));
-      }
-      const int jj = jt + 4 * j4 + e;
-      if (r == 0 && jj < MB) {
-        w32[jj] = v;
-        amag[jj] = m;
-      }
+    const int jj = jt + 4 * j4 + e;
+    if (r == 0 && jj < MB) {
+      w32[jj] = v;
+      amag[jj] = m;
     }
   }
 }
@@ -459,27 +450,13 @@ bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G) {
 
 hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  // tiles per wavefront: as many as still leave about four workgroups per
-  // compute unit, so that more of each wavefront's loads are in flight
-  const long long chunks64 = (long long)a.B * a.Hkv * ((a.MB + 63) / 64);
-  const int tpw = chunks64 >= 4 * 4 * 256 ? 4 : (chunks64 >= 2 * 4 * 256 ? 2 : 1);
-  const dim3 g1((unsigned)((a.MB + 64 * tpw - 1) / (64 * tpw) + (a.append ? 1 : 0)), (unsigned)a.Hkv, (unsigned)a.B);
+  const dim3 g1((unsigned)((a.MB + 63) / 64 + (a.append ? 1 : 0)), (unsigned)a.Hkv, (unsigned)a.B);
   const dim3 g2((unsigned)a.Hkv, (unsigned)a.B);
   if (a.D == 64) {
-    if (tpw == 4)
-      hipLaunchKernelGGL((scores32_kernel<64, 4>), g1, dim3(256), 0, s, a);
-    else if (tpw == 2)
-      hipLaunchKernelGGL((scores32_kernel<64, 2>), g1, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((scores32_kernel<64, 1>), g1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(scores32_kernel<64>, g1, dim3(256), 0, s, a);
     hipLaunchKernelGGL(refine_kernel<64>, g2, dim3(kFT), 0, s, a);
   } else {
-    if (tpw == 4)
-      hipLaunchKernelGGL((scores32_kernel<128, 4>), g1, dim3(256), 0, s, a);
-    else if (tpw == 2)
-      hipLaunchKernelGGL((scores32_kernel<128, 2>), g1, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((scores32_kernel<128, 1>), g1, dim3(256), 0, s, a);
+    hipLaunchKernelGGL(scores32_kernel<128>, g1, dim3(256), 0, s, a);
     hipLaunchKernelGGL(refine_kernel<128>, g2, dim3(kFT), 0, s, a);
   }
   return hipGetLastError();

@@ -937,11 +937,11 @@ def test_fp32_summary_scores_adversarial(env, case, G):
 
 
 @pytest.mark.parametrize("B", [64, 128])
-def test_matrix_core_selection_multi_tile(env, B):
-    """The matrix-core selection at sizes where each scoring wavefront takes
-    two (B = 64) or four (B = 128) 16-block tiles, with a ragged last chunk
-    (520 blocks per row) and ragged lengths: selections bit-exact against
-    the oracle's exact scores.  Summaries are written directly (bf16,
+def test_matrix_core_selection_large_ragged(env, B):
+    """The matrix-core selection on large layouts (64 and 128 sequences,
+    133 120 and 266 240 blocks) with a ragged last 64-block chunk (520
+    blocks per row) and ragged lengths: selections bit-exact against the
+    oracle's exact scores.  Summaries are written directly (bf16,
     min <= max), so no pool is needed at this size."""
     torch, kvs, orc = env.torch, env.kvs, env.orc
     Hkv, G, D, S, MB, k = 4, 8, 128, 64, 520, 32
