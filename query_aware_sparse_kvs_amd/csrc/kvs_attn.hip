@@ -512,13 +512,16 @@ __device__ __forceinline__ void fp8x8_to_f32(u32x2 w, float* out) {
   fp8x4_to_f32(w.x, out);
   fp8x4_to_f32(w.y, out + 4);
 }
-// Eight floats that are bf16 values (low 16 bits zero) -> bf16x8.
-__device__ __forceinline__ bf16x8_t pack_bf16_exact(const float* f) {
-  u32x4 w;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (__float_as_uint(f[2 * i + 1]) & 0xFFFF0000u) | (__float_as_uint(f[2 * i]) >> 16);
-  return __builtin_bit_cast(bf16x8_t, w);
+// Eight E4M3FN codes -> bf16x8, exactly (every E4M3 value, subnormals
+// included, is a bf16 value): gfx950's packed conversion with a unit scale,
+// two codes per instruction.
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(u32x2 w) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+  const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+  const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+  const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+  return bf16x8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 // Eight floats -> hi = bf16(x), lo = bf16(x - hi): about 16 significant bits.
 __device__ __forceinline__ void split_bf16(const float* f, bf16x8_t& hi, bf16x8_t& lo) {
@@ -697,9 +700,7 @@ __device__ __forceinline__ void page_scores8g(const PageK8G<D, S>& K, const bf16
       f32x4_t sc = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int cs = 0; cs < CS; ++cs) {
-        float x[8];
-        fp8x8_to_f32(K.k[h][tg][cs], x);
-        const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pack_bf16_exact(x), qf[cs],
+        const f32x4_t part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(K.k[h][tg][cs]), qf[cs],
                                                                      f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
         // scales of this lane's 4 output tokens h*32 + 8*j4 + 4*tg + e
         const f32x4_t ks4 = *reinterpret_cast<const f32x4_t*>(ksl + kgu[cs] * S + h * 32 + 8 * j4 + 4 * tg);
@@ -730,6 +731,8 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
   for (int h = 0; h < NSUB; ++h) {
     const int nt = ntok - h * 32;
     const int t0 = 8 * j4;
+    // a sub-tile whose 32 slots all hold tokens needs no masks (uniform)
+    const bool full = nt >= 32;
     uint32_t keep[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w)
@@ -742,20 +745,28 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
         const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(vg);
         const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(vg + 4);
         float pp[8];
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pp[e] = t0 + e < nt ? pf[h][e] * s0[e] : 0.0f;
-          pp[4 + e] = t0 + 4 + e < nt ? pf[h][4 + e] * s1[e] : 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            pp[e] = pf[h][e] * s0[e];
+            pp[4 + e] = pf[h][4 + e] * s1[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pp[e] = t0 + e < nt ? pf[h][e] * s0[e] : 0.0f;
+            pp[4 + e] = t0 + 4 + e < nt ? pf[h][4 + e] * s1[e] : 0.0f;
+          }
         }
         split_bf16(pp, phi, plo);
       }
-      float x[8];
-      fp8x8_to_f32(V.v[h][ct], x);
-      bf16x8_t a = pack_bf16_exact(x);
-      u32x4 aw = __builtin_bit_cast(u32x4, a);
+      bf16x8_t a = fp8x8_to_bf16(V.v[h][ct]);
+      if (!full) {  // positions past the sequence may hold anything
+        u32x4 aw = __builtin_bit_cast(u32x4, a);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) aw[w] &= keep[w];  // positions past the sequence may hold anything
-      a = __builtin_bit_cast(bf16x8_t, aw);
+        for (int w = 0; w < 4; ++w) aw[w] &= keep[w];
+        a = __builtin_bit_cast(bf16x8_t, aw);
+      }
       o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, o[ct], 0, 0, 0);
       o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, o[ct], 0, 0, 0);
     }
