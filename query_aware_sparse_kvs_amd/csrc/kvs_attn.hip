@@ -97,20 +97,23 @@ __device__ __forceinline__ int tile_entry(const AttnArgs& a, const int32_t* srow
   return entry;
 }
 
+// The work index of workgroup w of n.  The dispatcher hands workgroups to
+// the eight XCDs in turn (workgroup w, counted x-fastest, runs on XCD w % 8),
+// and each XCD has its own L2; this numbering puts consecutive work indices
+// on one XCD.  It is a permutation of 0..n-1 for any n (a tail of fewer than
+// eight workgroups keeps its own numbers).
+__device__ __forceinline__ int xcd_order(int w, int n) {
+  const int per = n >> 3;  // workgroups per XCD in the whole rounds
+  return w < 8 * per ? (w & 7) * per + (w >> 3) : w;
+}
+
 // The (split, KV head, sequence) a workgroup of a (nsplit, Hkv, B) grid
-// works on.  The dispatcher hands workgroups to the eight XCDs in turn
-// (workgroup w, counted x-fastest, runs on XCD w % 8), and each XCD has its
-// own L2.  Numbering the work so that consecutive ids sit on one XCD keeps a
-// unit's splits together: they share its scores, its table row and its
-// query in one L2 instead of fetching them into eight.  The map is a
-// permutation of the grid for any size (a tail of fewer than eight
-// workgroups keeps its own numbers).
+// works on, numbered by xcd_order: a unit's splits sit together on one XCD
+// and share its scores, its table row and its query in one L2 instead of
+// fetching them into eight.
 __device__ __forceinline__ void xcd_unit(int& split, int& g, int& b) {
   const int nx = gridDim.x, ny = gridDim.y;
-  const int n = nx * ny * gridDim.z;
-  const int w = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
-  const int per = n >> 3;  // workgroups per XCD in the whole rounds
-  const int m = w < 8 * per ? (w & 7) * per + (w >> 3) : w;
+  const int m = xcd_order(blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z), nx * ny * gridDim.z);
   split = m % nx;
   const int u = m / nx;
   g = u % ny;
@@ -1194,7 +1197,9 @@ constexpr int kMergeBatch = 8;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnArgs a) {
   constexpr int C4 = D / 4;  // float4 chunks per head
-  const long long t = (long long)blockIdx.x * kMergeThreads + threadIdx.x;
+  // numbered like the attention's workgroups (xcd_unit), so that a unit's
+  // heads tend to be merged on the XCD whose L2 took its split partials
+  const long long t = (long long)xcd_order(blockIdx.x, gridDim.x) * kMergeThreads + threadIdx.x;
   const long long nrows = (long long)a.B * a.Hq;
   if (t >= nrows * C4) return;
   const long long row = t / C4;
