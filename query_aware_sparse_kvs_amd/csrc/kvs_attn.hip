@@ -98,10 +98,11 @@ __device__ __forceinline__ int tile_entry(const AttnArgs& a, const int32_t* srow
 }
 
 // The work index of workgroup w of n.  The dispatcher hands workgroups to
-// the eight XCDs in turn (workgroup w, counted x-fastest, runs on XCD w % 8),
-// and each XCD has its own L2; this numbering puts consecutive work indices
-// on one XCD.  It is a permutation of 0..n-1 for any n (a tail of fewer than
-// eight workgroups keeps its own numbers).
+// the eight XCDs in turn (workgroup w, counted x-fastest, runs on XCD
+// (w + s) % 8, s fixed for the launch: 0 launched alone, another value in a
+// graph), and each XCD has its own L2; this numbering puts consecutive work
+// indices on one XCD.  It is a permutation of 0..n-1 for any n (a tail of
+// fewer than eight workgroups keeps its own numbers).
 __device__ __forceinline__ int xcd_order(int w, int n) {
   const int per = n >> 3;  // workgroups per XCD in the whole rounds
   return w < 8 * per ? (w & 7) * per + (w >> 3) : w;

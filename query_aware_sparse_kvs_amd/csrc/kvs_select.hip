@@ -199,36 +199,57 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
       __syncthreads();
     }
     if (wave >= G) continue;
-#pragma unroll 1
-    for (int c0 = half * (D / 2); c0 < half * (D / 2) + D / 2; c0 += VEC) {
-      const u32x4 vmn = *reinterpret_cast<const u32x4*>(pmn + c0 * EB);
-      u32x4 vmx = vmn;
-      if constexpr (SK != K_MEAN) vmx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
+    // VEC-channel steps; each step's LDS reads (the lane's min and max
+    // words, the heads' masks and fp64 query values) are issued one step
+    // ahead of its arithmetic, and the heads' chains are interleaved channel
+    // by channel, each still summed in ascending c
+    constexpr int NSTEP = (D / 2) / VEC;
+    struct Step {
+      u32x4 mn, mx, m[HPW];
+      double q[HPW][VEC];
+    };
+    auto load = [&](int st, Step& t) {
+      const int c0 = half * (D / 2) + st * VEC;
+      t.mn = *reinterpret_cast<const u32x4*>(pmn + c0 * EB);
+      t.mx = t.mn;
+      if constexpr (SK != K_MEAN) t.mx = *reinterpret_cast<const u32x4*>(pmx + c0 * EB);
 #pragma unroll
       for (int i = 0; i < HPW; ++i) {
-        const int h = wave + NWB * i;
-        if (h >= G) break;
-        if constexpr (SK == K_MEAN) {  // score q.mean: the row is the mean itself
+        const int h = min(wave + NWB * i, G - 1);  // (heads past G: never used)
+        if constexpr (SK != K_MEAN) t.m[i] = *reinterpret_cast<const u32x4*>(&qm[h][c0 * EB / 4]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i] = __builtin_fma(qd[h][c0 + e], (double)__uint_as_float(vmn[e]), acc[i]);
-          continue;
-        }
-        const u32x4 m = *reinterpret_cast<const u32x4*>(&qm[h][c0 * EB / 4]);
-        const u32x4 x = (vmx & m) | (vmn & ~m);
-        float xf[VEC];
+        for (int e = 0; e < VEC; ++e) t.q[i][e] = qd[h][c0 + e];
+      }
+    };
+    Step cur, nxt;
+    load(0, cur);
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + 1 < NSTEP) load(st + 1, nxt);
+      __builtin_amdgcn_sched_barrier(0);  // the next step's reads go out before this step's arithmetic
+      float xf[HPW][VEC];
+#pragma unroll
+      for (int i = 0; i < HPW; ++i) {
+        // score q.mean: the row is the mean itself; else the word-wise choice of max or min
+        const u32x4 x = SK == K_MEAN ? cur.mn : (cur.mx & cur.m[i]) | (cur.mn & ~cur.m[i]);
         if constexpr (EB == 2) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            xf[2 * e] = bf16_lo(x[e]);
-            xf[2 * e + 1] = bf16_hi(x[e]);
+            xf[i][2 * e] = bf16_lo(x[e]);
+            xf[i][2 * e + 1] = bf16_hi(x[e]);
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xf[e] = __uint_as_float(x[e]);
+          for (int e = 0; e < 4; ++e) xf[i][e] = __uint_as_float(x[e]);
         }
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[i] = __builtin_fma(qd[h][c0 + e], (double)xf[e], acc[i]);
       }
+#pragma unroll
+      for (int e = 0; e < VEC; ++e)
+#pragma unroll
+        for (int i = 0; i < HPW; ++i)
+          if (wave + NWB * i < G) acc[i] = __builtin_fma(cur.q[i][e], (double)xf[i][e], acc[i]);
+      __builtin_amdgcn_sched_barrier(0);
+      if (st + 1 < NSTEP) cur = nxt;
     }
   }
   __syncthreads();  // the staged rows are no longer needed: reuse them for the group max
