@@ -255,7 +255,7 @@ hipError_t launch_append(const AppendArgs& a, int kv_kind, hipStream_t s);
 hipError_t launch_bounds(const BoundArgs& a, int q_kind, int summ_kind, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, hipStream_t s);
 bool select_mfma_supported(int q_kind, int summ_kind, int D, int MB, int G);
-hipError_t launch_select_mfma(const SelMfmaArgs& a, hipStream_t s);
+hipError_t launch_select_mfma(const SelMfmaArgs& a, int summ_kind, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s);
 // whether launch_attn can run this shape in self-selecting mode
 bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k);

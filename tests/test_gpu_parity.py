@@ -405,6 +405,52 @@ def test_matrix_core_selection_matches_oracle(env, kind):
         assert np.array_equal(f_sel.cpu().numpy(), o_sel), f"selection differs at k={k}"
 
 
+def test_matrix_core_selection_fp32_summaries(env):
+    """fp32 summaries (as fp8 K has them) on the matrix cores: 32 x 4 x 2048
+    blocks, above the size from which kvs_select_topk without bounds_out
+    takes that route.  Each summary is split into two bf16 parts and the
+    blocks near the threshold are ranked with the exact fp64 chain; the
+    selections must equal the plain definition's for ordinary units and for
+    units built to break the estimate: scores that overflow fp32, summaries
+    below the normal range, all-zero rows (every block tied), blocks of very
+    different scale, subnormal query values, and ragged lengths.  Summaries
+    are written directly (min <= max)."""
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    B, Hkv, G, D, S, MB = 32, 4, 8, 128, 64, 2048
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((B, Hkv * G, D))
+    x = rng.standard_normal((B, Hkv, MB, 2, D))
+    # unit (b, g) patterns
+    x[1, 0] *= 2.0 ** 100
+    q[1, 0:G] *= 2.0 ** 100                                        # fp32 overflow of the products
+    x[2, 1] *= 2.0 ** -135                                          # subnormal summaries
+    x[3, 2] = 0.0                                                   # every block tied at 0
+    x[4, 3] *= 2.0 ** rng.integers(-40, 40, size=(MB, 1, 1))        # mixed scales
+    q[5, 0:G, :4] = 2.0 ** -130                                     # subnormal query values
+    x[6, 0] = np.round(x[6, 0] * 2) / 2                             # many exact ties
+    q[6, 0:G] = np.sign(q[6, 0:G])
+    x = x.astype(np.float32)
+    summ = np.stack([np.minimum(x[:, :, :, 0], x[:, :, :, 1]), np.maximum(x[:, :, :, 0], x[:, :, :, 1])], axis=3)
+    qt = torch.tensor(q, dtype=torch.float64).to(torch.bfloat16)
+    lens = rng.integers(1, MB * S + 1, size=B).astype(np.int32)
+    lens[:8] = MB * S
+    lens[8:12] = [MB * S - 63, 64 * 40 + 1, 1, 64 * 65]
+    L = kvs.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_BF16, kvs.KVS_FP8_E4M3, 32)
+    assert kvs.kvs_select_uses_matrix_cores(L, 64) == 1
+    OL = orc.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_FP8_E4M3, 32)
+    oW = orc.bounds(OL, qt.double().numpy(), summ.astype(np.float64), lens)
+    g_q, g_summ, g_lens = qt.to(env.dev), torch.tensor(summ).to(env.dev), torch.tensor(lens).to(env.dev)
+    for k in (2, 5, 64, 130):
+        sel = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=env.dev)
+        ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+        kvs.kvs_select_topk(L, g_q, g_summ, g_lens, k, sel, None, ws)
+        no_device_errors(env)
+        o_sel = orc.select(OL, oW, lens, k)
+        g_sel = sel.cpu().numpy()
+        bad = [(b, g) for b in range(B) for g in range(Hkv) if not np.array_equal(g_sel[b, g], o_sel[b, g])]
+        assert not bad, f"k={k}: selection differs for units {bad[:8]}"
+
+
 def test_attention_padding_empty_and_partial(env):
     torch = env.torch
     w = env.synth.scaled(env.synth.WORKLOADS["llama8b"], B=4, L=1000, layers=1)
