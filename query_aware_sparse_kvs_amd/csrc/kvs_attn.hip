@@ -357,60 +357,63 @@ __device__ __forceinline__ const int32_t* self_select(const AttnArgs& a, int b, 
 
 // The end of an MFMA-kernel workgroup: merges the NW wavefronts' running
 // (max, sum, acc) in LDS; lane (r, j4) holds channels ct*16 + 4*j4 + e of
-// head r.  One split: the normalised output row is written; otherwise the
-// split partial.
+// head r.  Every wavefront stages its accumulator, then wavefront w merges
+// channel tiles w*CT/NW .. (w+1)*CT/NW-1 of every head (the wavefronts'
+// terms still added in order 0..NW-1).  One split: the normalised output
+// row is written; otherwise the split partial.
 template <int D, int NW>
 __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, int split, int wave, int r, int j4,
                                                float m_run, float l_run, const f32x4_t* o, float (*mg_m)[16],
                                                float (*mg_l)[16], float (*mg_o)[16][D + 4]) {
   constexpr int CT = D / 16;
+  constexpr int CPW = CT / NW;  // channel tiles merged per wavefront
+  static_assert(CT % NW == 0, "whole channel tiles per wavefront");
   const int G = a.G;
   if (j4 == 0) {
     mg_m[wave][r] = m_run;
     mg_l[wave][r] = l_run;
   }
-  if (wave > 0) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) mg_o[wave - 1][r][ct * 16 + 4 * j4 + e] = o[ct][e];
-  }
+  for (int ct = 0; ct < CT; ++ct)
+    *reinterpret_cast<f32x4_t*>(&mg_o[wave][r][ct * 16 + 4 * j4]) = o[ct];
   __syncthreads();
-  if (wave == 0 && r < G) {
-    float M = mg_m[0][r];
+  if (r >= G) return;
+  float M = mg_m[0][r];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) M = fmaxf(M, mg_m[w][r]);
-    float scw[NW], L = 0.0f;
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, mg_m[w][r]);
+  float scw[NW], L = 0.0f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = mg_m[w][r];
-      scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
-      L += mg_l[w][r] * scw[w];
+  for (int w = 0; w < NW; ++w) {
+    const float mw = mg_m[w][r];
+    scw[w] = mw == -__builtin_inff() ? 0.0f : exp2f(mw - M);
+    L += mg_l[w][r] * scw[w];
+  }
+  // one split: normalise and write the output row; else store the partial
+  const bool direct = a.nsplit == 1;
+  const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
+  const long long hrow = (long long)b * a.Hq + (long long)g * G + r;
+  const long long pi = hrow * a.nsplit + split;
+  if (!direct && wave == 0 && j4 == 0) {
+    a.part_m[pi] = M;
+    a.part_l[pi] = L;
+  }
+  float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
+#pragma unroll
+  for (int t = 0; t < CPW; ++t) {
+    const int ct = wave * CPW + t;
+    f32x4_t v[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v[w] = *reinterpret_cast<const f32x4_t*>(&mg_o[w][r][ct * 16 + 4 * j4]);
+    float4 res;
+    float* pv = reinterpret_cast<float*>(&res);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float x = v[0][e] * scw[0];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) x += v[w][e] * scw[w];
+      pv[e] = x * inv;
     }
-    // one split: normalise and write the output row; else store the partial
-    const bool direct = a.nsplit == 1;
-    const float inv = direct ? (L > 0.0f ? 1.0f / L : 0.0f) : 1.0f;
-    const long long hrow = (long long)b * a.Hq + (long long)g * G + r;
-    const long long pi = hrow * a.nsplit + split;
-    if (!direct && j4 == 0) {
-      a.part_m[pi] = M;
-      a.part_l[pi] = L;
-    }
-    float* dst = direct ? a.out + hrow * D : a.part_acc + pi * D;
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      float4 v;
-      float* pv = reinterpret_cast<float*>(&v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int c = ct * 16 + 4 * j4 + e;
-        float x = o[ct][e] * scw[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) x += mg_o[w - 1][r][c] * scw[w];
-        pv[e] = x * inv;
-      }
-      *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = v;
-    }
+    *reinterpret_cast<float4*>(dst + ct * 16 + 4 * j4) = res;
   }
 }
 
@@ -420,7 +423,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
   constexpr int NSUB = S / 32;  // 32-token sub-tiles per page
   __shared__ float mg_m[NW][16], mg_l[NW][16];
-  __shared__ float mg_o[NW - 1][16][D + 4];
+  __shared__ float mg_o[NW][16][D + 4];
   __shared__ long long wl_tile[NW][64];
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
@@ -785,7 +788,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   constexpr int CT = D / 16;
   constexpr int NSUB = S / 32;
   __shared__ float mg_m[NW][16], mg_l[NW][16];
-  __shared__ float mg_o[NW - 1][16][D + 4];
+  __shared__ float mg_o[NW][16][D + 4];
   __shared__ long long wl_tile[NW][64];
   __shared__ int wl_ntok[NW][64];
   __shared__ int trow[kTabMax];
