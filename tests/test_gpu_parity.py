@@ -982,6 +982,54 @@ def test_fp32_summary_scores_adversarial(env, case, G):
     assert kvs.kvs_device_errors(clear=True) == 0
 
 
+BF16_SUM_CASES = ["normal", "q-spread", "x-spread", "rounding", "zeros", "heavy"]
+
+
+@pytest.mark.parametrize("case", BF16_SUM_CASES)
+def test_bf16_scores_adversarial(env, case):
+    """bf16 query and summaries: the exact scores must equal the oracle's
+    ascending fp64 sum bit for bit on ordinary data and where that sum
+    rounds: queries or summaries spread over 2^+-20, query channels
+    alternating 2^20 and 2^-20 (a rounding at nearly every step), exact
+    zeros, and heavy rows; selections equal."""
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    rng = np.random.default_rng(300 + BF16_SUM_CASES.index(case))
+    B, Hkv, G, D, S, MB = 4, 4, 8, 128, 64, 300
+    q = rng.standard_normal((B, Hkv * G, D))
+    x = rng.standard_normal((B, Hkv, MB, 2, D))
+    if case == "q-spread":
+        q *= 2.0 ** rng.integers(-20, 21, size=q.shape)
+    elif case == "x-spread":
+        x *= 2.0 ** rng.integers(-20, 21, size=(B, Hkv, MB, 1, 1))
+    elif case == "rounding":
+        q[..., 0::2] *= 2.0 ** 20
+        q[..., 1::2] *= 2.0 ** -20
+    elif case == "zeros":
+        q[:, :, ::3] = 0.0
+        x[..., ::5] = 0.0
+    elif case == "heavy":
+        x[:, :, ::7] *= 4.0 * np.sqrt(D)
+    qt = torch.tensor(q, dtype=torch.float64).to(torch.bfloat16)
+    xt = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16)
+    summ = torch.stack([torch.minimum(xt[:, :, :, 0], xt[:, :, :, 1]), torch.maximum(xt[:, :, :, 0], xt[:, :, :, 1])],
+                       dim=3)
+    lens = np.array([MB * S, MB * S - 100 * S - 3, 64 * 70 + 1, MB * S - 1], dtype=np.int32)
+    k = 24
+    L = kvs.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_BF16, kvs.KVS_BF16)
+    OL = orc.Layout(B, Hkv * G, Hkv, D, S, MB, B * MB, kvs.KVS_BF16)
+    sel = torch.full((B, Hkv, k), -7, dtype=torch.int32, device=env.dev)
+    W = torch.empty((B, Hkv, MB), dtype=torch.float64, device=env.dev)
+    ws = torch.empty(kvs.kvs_select_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    kvs.kvs_select_topk(L, qt.to(env.dev), summ.to(env.dev), torch.tensor(lens).to(env.dev), k, sel, W, ws)
+    no_device_errors(env)
+    oW = orc.bounds(OL, qt.double().numpy(), summ.double().numpy(), lens)
+    gW = W.cpu().numpy()
+    for b in range(B):
+        nb = (int(lens[b]) + S - 1) // S
+        assert np.array_equal(gW[b, :, :nb], oW[b, :, :nb]), f"{case}: scores differ (sequence {b})"
+    assert np.array_equal(sel.cpu().numpy(), orc.select(OL, oW, lens, k)), f"{case}: selection differs"
+
+
 @pytest.mark.parametrize("B", [64, 128])
 def test_matrix_core_selection_large_ragged(env, B):
     """The matrix-core selection on large layouts (64 and 128 sequences,
