@@ -192,7 +192,8 @@ kvs_status kvs_build_summaries_ex(const kvs_layout* layout, int32_t summary_kind
  *  workspace    >= kvs_select_workspace_size(layout, k) bytes
  * Two implementations give identical selections.  By default every block's W
  * is computed in exact fp64 and a second kernel selects.  When bounds_out is
- * NULL, q and the summaries are bf16, MB <= 2048 and B*Hkv*MB >= 65536, the
+ * NULL, q is bf16, MB <= 2048 and B*Hkv*MB >= 65536 (bf16 summaries) or
+ * >= 262144 (fp32 summaries, each value split into two bf16 parts), the
  * blocks are instead scored on the matrix cores in fp32 together with a
  * rigorous bound on that rounding, and only the blocks whose fp32 score lies
  * within the bound of the top-k threshold get their W recomputed in exact
