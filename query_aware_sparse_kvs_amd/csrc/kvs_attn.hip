@@ -5,7 +5,9 @@
 //
 // Work split (both kernels): a (sequence, KV head) unit's k selected blocks
 // are cut into `nsplit` runs of `bps` entries; one 256-thread workgroup
-// (4 wavefronts) handles one run, each wavefront one block (tile) at a time.
+// (4 wavefronts) handles one run, each wavefront one tile at a time (the
+// MFMA kernels' tiles are 32-token halves of 64-token blocks, or whole
+// 32-token blocks; the VALU kernel's tiles are whole blocks).
 // The four wavefronts' running (max, sum, acc) are merged in LDS and written
 // as a split partial (or, with a single split, as the output row);
 // merge_kernel then merges the splits of every query head:
@@ -15,7 +17,7 @@
 // than a device-scope release per workgroup.)
 // Scores are kept in base 2: the query is scaled by sm_scale*log2(e).
 //
-// attn_mfma_kernel (bf16, S in {32, 64}): both products run on
+// attn_mfma_kernel (bf16, blocks of 32 or 64 tokens): both products run on
 // v_mfma_f32_16x16x32_bf16 with the G query heads padded to 16 columns.
 //   scores  S^T = K Q^T: the A operand is 16 token rows x 32 channels of K,
 //           loaded straight from the token-major tile with 16-byte loads;
@@ -28,12 +30,11 @@
 //           from the score accumulators in registers.  P is split into
 //           hi = bf16(p) and lo = bf16(p - hi), two MFMAs, so the product
 //           keeps ~16 bits of P.  No LDS traffic inside the tile loop.
-//   A wavefront resolves its pages (selection -> table) for all of them at
+//   A wavefront resolves its tiles (selection -> table) for all of them at
 //   once into LDS, then streams them through a two-stage software pipeline:
-//   the next page's K is requested as soon as the current page's scores are
+//   the next tile's K is requested as soon as the current tile's scores are
 //   computed, its V as soon as the current value product is, so about one
-//   page (32 KiB of K and V at S = 64, d = 128) stays in flight per
-//   wavefront.
+//   tile (16 KiB of K and V at d = 128) stays in flight per wavefront.
 // attn_valu_kernel (fp32, fp8, and bf16 with S = 16): lane = token for the
 //   scores (64/S lanes split a token's channels), lane = channel pair for the
 //   values, probabilities broadcast through LDS; every K/V load of a tile is
@@ -50,6 +51,11 @@ namespace {
 
 constexpr int kGMax = 16;
 constexpr int kAttnWaves = 4;  // wavefronts per workgroup of the MFMA kernels
+// tokens per tile of the MFMA kernels: a 64-token cache block is streamed as
+// its two 32-token halves (the K rows and the V runs of a half are
+// contiguous in the block's tiles), which keeps more of a wavefront's work
+// behind its loads than whole 64-token pages
+constexpr int kAttnTile = 32;
 constexpr int kComputeUnits = 256;  // MI355X
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -261,17 +267,26 @@ __device__ __forceinline__ void page_values(PageV<D, S>& V, int ntok, int j4, co
   }
 }
 
-// The selection slots a lane resolves in chunk t0 of its wavefront's list:
-// slot i = i0 + nw*(t0 + lane) (nw = wavefronts per workgroup) and the slot
-// before it, or -1 where there is none.
-__device__ __forceinline__ void fetch_slots(const int32_t* srow, int i0, int i1, int nw, int t0, int& j, int& jp) {
+// A wavefront's work list is over tiles of the selection: position i holds
+// tile `i % sub` of selection slot i / sub (sub = tiles per cache block, 1
+// or 2).  The position a lane resolves in chunk t0 of its wavefront's list
+// is i = i0 + nw*(t0 + lane); it yields that slot's block j (-2 where there
+// is no position), the block of the slot before it (jp; kFirstSlot for slot
+// 0) and the tile's half of the block.
+constexpr int kFirstSlot = -3;
+
+__device__ __forceinline__ void fetch_slots(const int32_t* srow, int i0, int i1, int nw, int sub, int t0, int& j,
+                                            int& jp, int& half) {
   const int lane = threadIdx.x & 63;
   const int i = i0 + nw * (t0 + lane);
-  j = -2;  // no slot
+  j = -2;  // no position
   jp = -1;
+  half = 0;
   if (i < i1) {
-    j = srow[i];
-    jp = i > 0 ? srow[i - 1] : -1;
+    const int slot = sub == 2 ? i >> 1 : i;
+    half = i - slot * sub;
+    j = srow[slot];
+    jp = slot > 0 ? srow[slot - 1] : kFirstSlot;
   }
 }
 
@@ -296,20 +311,22 @@ __device__ __forceinline__ void stage_table_row(const AttnArgs& a, int b, int g,
   }
 }
 
-// Resolves the chunk's slots (one per lane, from fetch_slots) into LDS: pool
-// tile index and valid token count (0 = nothing to do).  The table entry
-// comes from the staged row `trow` when there is one, else from memory.
-__device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow, int j, int jp, bool first_slot,
-                                              int b, int g, int nb, int len, int S, long long* wl_tile,
+// Resolves the chunk's positions (one per lane, from fetch_slots) into LDS:
+// the index of the T-token tile in the pool (the cache's S-token blocks seen
+// as sub = S/T consecutive tiles) and its valid token count (0 = nothing to
+// do).  The table entry comes from the staged row `trow` when there is one,
+// else from memory.
+__device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow, int j, int jp, int half, int b,
+                                              int g, int nb, int len, int T, int sub, long long* wl_tile,
                                               int* wl_ntok) {
   const int lane = threadIdx.x & 63;
-  long long tile = a.hot ? 0 : g;  // tile (0, g): always in bounds
+  long long tile = a.hot ? 0 : (long long)g * sub;  // the first tile of block (0, g): always in bounds
   int ntok = 0;
   if (j != -2) {
     bool ok = j >= 0;
     if (j < -1) raise_flag(a.err, 0x4u);
     if (ok) {
-      if (j >= nb || (!first_slot && (jp >= j || jp < 0))) raise_flag(a.err, 0x4u);
+      if (j >= nb || (jp != kFirstSlot && (jp >= j || jp < 0))) raise_flag(a.err, 0x4u);
       ok = j < nb;
     }
     if (ok) {
@@ -318,8 +335,8 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow
       if (entry < 0 || entry >= a.P) {
         raise_flag(a.err, 0x2u);
       } else {
-        tile = a.hot ? (long long)entry : (long long)entry * a.Hkv + g;
-        ntok = min(S, len - j * S);
+        tile = (a.hot ? (long long)entry : (long long)entry * a.Hkv + g) * sub + half;
+        ntok = max(0, min(T, len - j * a.S - half * T));
       }
     }
   }
@@ -417,11 +434,13 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
   }
 }
 
+// S: tokens per tile (kAttnTile); the cache's blocks hold a.S = S or 2S
+// tokens, and a block of 2S tokens is streamed as its two tiles.
 template <int D, int S, int NW, int SELF>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CS = D / 32;  // k-steps of the score product
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
-  constexpr int NSUB = S / 32;  // 32-token sub-tiles per page
+  constexpr int NSUB = S / 32;  // 32-token sub-tiles per tile
   __shared__ float mg_m[NW][16], mg_l[NW][16];
   __shared__ float mg_o[NW][16][D + 4];
   __shared__ long long wl_tile[NW][64];
@@ -449,7 +468,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     }
   }
   const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
-  const int nb = (len + S - 1) / S;
+  const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
+  const int sub = a.S / S;                // tiles per block: 1 or 2
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4_t o[CT];
@@ -457,8 +477,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;  // self-selecting: replaced below
-  const int i0 = split * a.bps + wave;           // this wavefront's pages: i0, i0+NW, ...
-  const int i1 = min(split * a.bps + a.bps, a.k);
+  // this split's selection slots, as tile positions; the wavefront's tiles
+  // are positions i0, i0+NW, ...
+  const int i0 = split * a.bps * sub + wave;
+  const int i1 = min(split * a.bps + a.bps, a.k) * sub;
   const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
@@ -471,21 +493,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   // caches keep (no HBM traffic)
   // the first chunk's slots and the table row are fetched together, so the
   // table lookups need no further round trip
-  int j0, jp0;
+  int j0, jp0, h0;
   const bool staged = a.MB <= kTabMax;
   if constexpr (SELF > 0) {
     srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
-    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
   } else {
-    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
     if (staged) stage_table_row<64 * NW>(a, b, g, trow);
     __syncthreads();
   }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
-    int j = j0, jp = jp0;
-    if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
-    resolve_tiles(a, staged ? trow : nullptr, j, jp, t0 == 0 && lane == 0 && i0 == 0, b, g, nb, len, S,
-                  wl_tile[wave], wl_ntok[wave]);
+    int j = j0, jp = jp0, hf = h0;
+    if (t0 > 0) fetch_slots(srow, i0, i1, NW, sub, t0, j, jp, hf);
+    resolve_tiles(a, staged ? trow : nullptr, j, jp, hf, b, g, nb, len, S, sub, wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
     PageK<D, S> K;
     PageV<D, S> V;
@@ -496,7 +517,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
     }
     for (int tt = 0; tt < nt; ++tt) {
       const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
-      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : g));
+      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : (long long)g * sub));
       bf16x8_t ph[NSUB], pl[NSUB];
       page_scores<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, ph, pl);
       load_page_k<D, S>(kpool + tnext * S * D, r, j4, K);
@@ -781,7 +802,8 @@ __device__ __forceinline__ void page_values8(const PageV8<D, S>& V, int ntok, in
 }
 
 // PG: quantisation groups of 32 channels or more (page_scores8g), else the
-// hi/lo score product (page_scores8).
+// hi/lo score product (page_scores8).  S: tokens per tile, as in
+// attn_mfma_kernel.
 template <int D, int S, int NW, int SELF, int PG>
 __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a) {
   constexpr int CS = D / 32;
@@ -823,7 +845,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
     }
   }
   const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
-  const int nb = (len + S - 1) / S;
+  const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
+  const int sub = a.S / S;                // tiles per block: 1 or 2
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4_t o[CT];
@@ -831,8 +854,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
-  const int i0 = split * a.bps + wave;
-  const int i1 = min(split * a.bps + a.bps, a.k);
+  const int i0 = split * a.bps * sub + wave;  // tile positions, as in the bf16 kernel
+  const int i1 = min(split * a.bps + a.bps, a.k) * sub;
   const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
@@ -840,21 +863,20 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
   float* kw = ksl[PG ? wave : 0];
 
   // the same two-stage page pipeline as the bf16 kernel
-  int j0, jp0;
+  int j0, jp0, h0;
   const bool staged = a.MB <= kTabMax;
   if constexpr (SELF > 0) {
     srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
-    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
   } else {
-    fetch_slots(srow, i0, i1, NW, 0, j0, jp0);
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
     if (staged) stage_table_row<64 * NW>(a, b, g, trow);
     __syncthreads();
   }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {
-    int j = j0, jp = jp0;
-    if (t0 > 0) fetch_slots(srow, i0, i1, NW, t0, j, jp);
-    resolve_tiles(a, staged ? trow : nullptr, j, jp, t0 == 0 && lane == 0 && i0 == 0, b, g, nb, len, S,
-                  wl_tile[wave], wl_ntok[wave]);
+    int j = j0, jp = jp0, hf = h0;
+    if (t0 > 0) fetch_slots(srow, i0, i1, NW, sub, t0, j, jp, hf);
+    resolve_tiles(a, staged ? trow : nullptr, j, jp, hf, b, g, nb, len, S, sub, wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
     typename std::conditional<PG != 0, PageK8G<D, S>, PageK8<D, S>>::type K;
     PageV8<D, S> V;
@@ -868,7 +890,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
     }
     for (int tt = 0; tt < nt; ++tt) {
       const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
-      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : g));
+      const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : (long long)g * sub));
       float pf[NSUB][8];
       if constexpr (PG) {
         // this page's K scales -> LDS as [group][S]
@@ -1278,10 +1300,7 @@ hipError_t launch_valu(const AttnArgs& a, hipStream_t st) {
 
 template <int D, int SELF, int PG>
 void launch_mfma8_g(const AttnArgs& a, const dim3& grid, hipStream_t st) {
-  if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 32, kAttnWaves, SELF, PG>), grid, dim3(64 * kAttnWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma8_kernel<D, 64, kAttnWaves, SELF, PG>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  hipLaunchKernelGGL((attn_mfma8_kernel<D, kAttnTile, kAttnWaves, SELF, PG>), grid, dim3(64 * kAttnWaves), 0, st, a);
 }
 template <int D, int SELF>
 void launch_mfma8_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
@@ -1305,10 +1324,7 @@ hipError_t launch_mfma8(const AttnArgs& a, hipStream_t st) {
 
 template <int D, int SELF>
 void launch_mfma_s(const AttnArgs& a, const dim3& grid, hipStream_t st) {
-  if (a.S == 32)
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 32, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma_kernel<D, 64, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
+  hipLaunchKernelGGL((attn_mfma_kernel<D, kAttnTile, kAttnWaves, SELF>), grid, dim3(64 * kAttnWaves), 0, st, a);
 }
 
 template <int D>
