@@ -110,7 +110,7 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
   // the query first: loads complete in issue order, so the query must not
   // queue behind the chunk
   constexpr int QPT = (G * D + NT - 1) / NT;
-  float qv[QPT];
+  uint32_t qv[QPT];  // raw bits: converted only after the chunk's loads are out
 #pragma unroll
   for (int y = 0; y < QPT; ++y) {
     // unconditional loads (index clamped) keep the load counter exact
@@ -118,9 +118,9 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     const int h = i / D, c = i % D;
     const long long qi = ((long long)b * a.Hq + (long long)g * G + h) * D + c;
     if constexpr (QK == K_F32)
-      qv[y] = static_cast<const float*>(a.q)[qi];
+      qv[y] = static_cast<const uint32_t*>(a.q)[qi];
     else
-      qv[y] = __uint_as_float((uint32_t) static_cast<const uint16_t*>(a.q)[qi] << 16);
+      qv[y] = static_cast<const uint16_t*>(a.q)[qi];
   }
   __builtin_amdgcn_sched_barrier(0);  // the query loads stay ahead of the chunk's
   // stage the chunk's summaries in two channel halves (channels [0, D/2),
@@ -141,27 +141,42 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     raw[x] = *reinterpret_cast<const u32x4*>(src + (long long)blk * ROWB + off);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // each unit's first workgroup also appends the decode token (a workgroup
+  // of its own would leave some compute units with two scoring workgroups;
+  // mean tables are rebuilt instead).  Its loads go out behind the chunk's,
+  // its block's page and stored summary once the length is in, and its
+  // stores after the scores, so the append never holds up the chunk.  Every
+  // workgroup issues the same loads (the others read a spare address), so
+  // the waits for the chunk stay exact.
+  const bool appender = SK != K_MEAN && a.append == 2 && blockIdx.x == 0;  // uniform
+  const int tkind = SK == K_BF16 ? (int)K_BF16 : (a.app_kv == K_FP8 ? (int)K_FP8 : (int)K_F32);  // K storage
+  const int32_t* spare = a.seq_lens;
+  TokenIn tin{0u, 0u, 1.0f, 0};
+  if constexpr (SK == K_BF16)
+    tin = load_token_in<K_BF16, D, true>(a.tok, b, g, appender, spare);
+  else if constexpr (SK == K_F32)
+    tin = load_token_in_word<D>(a.tok, b, g, appender, tkind == K_FP8, spare);
   // the query as fp64, and per head the words' choice of max (mask bits set) or min
 #pragma unroll
   for (int y = 0; y < QPT; ++y) {
     const int i = y * NT + tid;
-    if (i < G * D) qd[i / D][i % D] = (double)qv[y];
+    if (i < G * D) qd[i / D][i % D] = (double)__uint_as_float(QK == K_F32 ? qv[y] : qv[y] << 16);
   }
-  // the decode token is appended by the unit's first workgroup while its
-  // chunk loads are in flight (a workgroup of its own would leave some
-  // compute units with two scoring workgroups)
-  if (SK != K_MEAN && a.append == 2 && blockIdx.x == 0) {  // (mean tables are rebuilt instead)
-    if constexpr (SK == K_BF16)
-      append_token_unit<K_BF16, D, NT>(a.tok, b, g);
-    else if (a.app_kv == K_FP8)
-      append_token_unit<K_FP8, D, NT>(a.tok, b, g);
-    else
-      append_token_unit<K_F32, D, NT>(a.tok, b, g);
-  }
+  const int tok_len = len;
   const int cap = a.MB * a.S;
   if (len < 0 || len > cap) {
     if (tid == 0 && blockIdx.x == 0 && g == 0) raise_flag(a.err, 0x1u);
     len = len < 0 ? 0 : cap;
+  }
+  // the token's block (an invalid length is flagged and appends nothing; an
+  // empty sequence appends nothing)
+  const bool tok_ok = appender && tok_len >= 1 && tok_len <= a.tok.MB * a.tok.S;
+  if (appender && (tok_len < 0 || tok_len > a.tok.MB * a.tok.S) && tid == 0 && g == 0) raise_flag(a.tok.err, 0x1u);
+  TokenBlock tblk{0, 0u, 0u};
+  if constexpr (SK == K_BF16) {
+    tblk = load_token_block<K_BF16, D, true, true>(a.tok, b, g, tok_len, tok_ok, spare);
+  } else if constexpr (SK == K_F32) {  // fp8 and fp32 K both keep fp32 summaries
+    tblk = load_token_block<K_F32, D, true, true>(a.tok, b, g, tok_len, tok_ok, spare);
   }
   const int nb = (len + a.S - 1) / a.S;
   // one half of the chunk -> its LDS rows
@@ -275,6 +290,14 @@ __global__ __launch_bounds__((64 * bound_waves<G, SK>()), (16 / bound_waves<G, S
     if (a.ema && valid) w = smooth_score(w, a.ema_state + wi, a.ema_alpha, a.ema_beta);
     if (a.accumulate && valid) w = a.W[wi] + w;  // the earlier layers' sum first
     a.W[wi] = w;
+  }
+  if (tok_ok) {  // the token's stores (and the seal of a block it fills)
+    if (tkind == K_BF16)
+      store_token<K_BF16, D, NT>(a.tok, b, g, tok_len, tin, tblk);
+    else if (tkind == K_FP8)
+      store_token<K_FP8, D, NT>(a.tok, b, g, tok_len, tin, tblk);
+    else
+      store_token<K_F32, D, NT>(a.tok, b, g, tok_len, tin, tblk);
   }
 }
 
