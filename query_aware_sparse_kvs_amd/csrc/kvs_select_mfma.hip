@@ -141,26 +141,29 @@ __global__ __launch_bounds__(256, SK == K_BF16 ? 4 : 2) void scores32_kernel(Sel
   constexpr int NV = EB / 2;                // 16-byte vectors per 8 elements
   const char* summ = static_cast<const char*>(a.summ) + ((long long)b * a.Hkv + g) * MB * 2 * D * EB;
   const uint16_t* qrow0 = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G) * D;
-  // A operand (summary rows, max half first) before anything else
+  // A operand (summary rows, max half first) before anything else.  Every
+  // load is unconditional, so they all go out in one batch: a row past MB
+  // reads row MB-1 and a head past G reads head G-1 instead; the products
+  // of those rows and columns are never stored.
   u32x4 ar[KC][NV];
-  const int j = jt + r;
+  const int j = min(jt + r, MB - 1);
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) {
     const int off = kc < HC ? D + kc * 32 : (kc - HC) * 32;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      ar[kc][v] = u32x4{0u, 0u, 0u, 0u};
-      if (j < MB)
-        ar[kc][v] = *reinterpret_cast<const u32x4*>(summ + ((long long)j * 2 * D + off + 8 * j4) * EB + 16 * v);
-    }
+    for (int v = 0; v < NV; ++v)
+      ar[kc][v] = *reinterpret_cast<const u32x4*>(summ + ((long long)j * 2 * D + off + 8 * j4) * EB + 16 * v);
   }
+  u32x4 qv[HC];
+  const int rq = min(r, G - 1);
+#pragma unroll
+  for (int cs = 0; cs < HC; ++cs) qv[cs] = *reinterpret_cast<const u32x4*>(qrow0 + (long long)rq * D + cs * 32 + 8 * j4);
+  __builtin_amdgcn_sched_barrier(0);  // every load out before any product
   u32x4 qs[KC];  // B operand: [q+ | q-] of head r
 #pragma unroll
   for (int cs = 0; cs < HC; ++cs) {
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if (r < G) v = *reinterpret_cast<const u32x4*>(qrow0 + (long long)r * D + cs * 32 + 8 * j4);
     u32x4 neg, negabs;
-    split_sign(v, qs[cs], neg, negabs);
+    split_sign(qv[cs], qs[cs], neg, negabs);
     qs[HC + cs] = neg;
   }
   f32x4_t u = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, ab = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
