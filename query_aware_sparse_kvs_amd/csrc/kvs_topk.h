@@ -22,8 +22,8 @@
 //
 // Cross-lane steps avoid LDS round trips: minima and maxima go through DPP
 // row moves and readlane, prefix sums of small counts through one ballot and
-// popcount per bit; only the per-wavefront totals meet in LDS, behind one
-// workgroup barrier each.
+// popcount per bit, and the bucket counts' prefix through a DPP scan; only
+// the per-wavefront totals meet in LDS, behind one workgroup barrier each.
 #pragma once
 
 #include "kvs_internal.h"
@@ -110,6 +110,40 @@ __device__ __forceinline__ int block_prefix_small_256(int v, int* tmp, int* tota
 }
 
 constexpr int bits_for(int n) { return n <= 1 ? 1 : 1 + bits_for(n / 2); }  // bits of values 0..n
+
+// Inclusive prefix sum over the 64 lanes: DPP row shifts by 1, 2, 4 and 8
+// within each 16-lane row (lanes shifted in from outside the row add 0),
+// then lane 15's sum broadcast into row 1 and row 3, and lane 31's into rows
+// 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return x;
+}
+
+// Exclusive prefix over the 256 threads of any v >= 0, and the total, with
+// six DPP steps per wavefront and one workgroup barrier (the wide counts of
+// the bucket scan, where one ballot per bit would take 14 steps); `tmp` as
+// for block_prefix_small_256.
+__device__ __forceinline__ int block_prefix_256(int v, int* tmp, int* total) {
+  const int wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(v);
+  if ((threadIdx.x & 63) == 63) tmp[wave] = incl;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int t = tmp[w];
+    if (w < wave) before += t;
+    all += t;
+  }
+  *total = all;
+  return before + incl - v;
+}
 
 // min and max of the active scores and their count, over the 256 threads
 // (one workgroup barrier)
@@ -230,7 +264,7 @@ __device__ __forceinline__ void select_unit(const double (&wv)[PT], int MB, int 
       s += (int)cnt[q];
     }
     int tot;
-    int above = block_prefix_small_256<bits_for(256 * 32)>(s, sh.scan_h, &tot);
+    int above = block_prefix_256(s, sh.scan_h, &tot);
     if (above < need && need <= above + s) {  // exactly one thread
 #pragma unroll
       for (int q = 0; q < BPT; ++q) {
