@@ -295,15 +295,19 @@ __device__ __forceinline__ void fetch_slots(const int32_t* srow, int i0, int i1,
 // entries; the caller synchronises the workgroup before reading it.
 constexpr int kTabMax = 2048;
 
+// In two halves, so that a kernel can issue the loads before it waits for
+// anything else (the sequence length, say) and store them to LDS later.
 template <int NT>
-__device__ __forceinline__ void stage_table_row(const AttnArgs& a, int b, int g, int* trow) {
+__device__ __forceinline__ void load_table_row(const AttnArgs& a, int b, int g, int (&v)[kTabMax / NT]) {
   const int32_t* row = a.hot ? a.table + ((long long)b * a.Hkv + g) * a.MB : a.table + (long long)b * a.MB;
-  int v[kTabMax / NT];
 #pragma unroll
   for (int x = 0; x < kTabMax / NT; ++x) {
     const int e = x * NT + (int)threadIdx.x;
     v[x] = e < a.MB ? row[e] : 0;
   }
+}
+template <int NT>
+__device__ __forceinline__ void store_table_row(const AttnArgs& a, const int (&v)[kTabMax / NT], int* trow) {
 #pragma unroll
   for (int x = 0; x < kTabMax / NT; ++x) {
     const int e = x * NT + (int)threadIdx.x;
@@ -350,22 +354,36 @@ __device__ __forceinline__ void resolve_tiles(const AttnArgs& a, const int* trow
 // Self-selecting mode: the workgroup picks its unit's blocks itself, from
 // the scores, with the selection of kvs_topk.h (the same one topk_kernel
 // runs), instead of reading a selection another launch wrote; the table
-// row's loads go out beside the scores'.  Returns the selection row (in
-// LDS) after a workgroup barrier; the first split's workgroup also writes
-// it to sel_out.
+// row's loads go out beside the scores', both before the kernel waits for
+// the sequence length.  self_select_finish returns the selection row (in
+// LDS) after a workgroup barrier; the first split's workgroup also writes it
+// to sel_out.
 constexpr int kSelfSelMax = 2048;  // largest MB and k of the mode
 
 // SELF: score ids per thread (0 = reads a selection): 2 up to 512 blocks,
 // 8 up to kSelfSelMax
 template <int NW, int SELF>
-__device__ __forceinline__ const int32_t* self_select(const AttnArgs& a, int b, int g, int split, int nb,
-                                                      bool staged, int* trow, int32_t* lsel, TopkLds& tk) {
+struct SelfSelLoads {
+  double wv[SELF > 0 ? SELF : 1];  // the unit's scores, as load_unit_scores lays them out
+  int tv[kTabMax / (64 * NW)];     // the table row, as load_table_row lays it out
+};
+
+template <int NW, int SELF>
+__device__ __forceinline__ void self_select_load(const AttnArgs& a, int b, int g, bool staged,
+                                                 SelfSelLoads<NW, SELF>& ld) {
   static_assert(NW * 64 == 256, "the selection runs on 256 threads");
   const long long unit = (long long)b * a.Hkv + g;
-  double wv[SELF];
-  load_unit_scores<SELF>(a.W + unit * a.MB, a.MB, wv);
-  if (staged) stage_table_row<64 * NW>(a, b, g, trow);
-  select_unit<SELF>(wv, a.MB, nb, a.k, a.recent, lsel, tk);
+  load_unit_scores<SELF>(a.W + unit * a.MB, a.MB, ld.wv);
+  if (staged) load_table_row<64 * NW>(a, b, g, ld.tv);
+}
+
+template <int NW, int SELF>
+__device__ __forceinline__ const int32_t* self_select_finish(const AttnArgs& a, int b, int g, int split, int nb,
+                                                             bool staged, const SelfSelLoads<NW, SELF>& ld,
+                                                             int* trow, int32_t* lsel, TopkLds& tk) {
+  const long long unit = (long long)b * a.Hkv + g;
+  if (staged) store_table_row<64 * NW>(a, ld.tv, trow);
+  select_unit<SELF>(ld.wv, a.MB, nb, a.k, a.recent, lsel, tk);
   __syncthreads();
   if (split == 0)
     for (int i = threadIdx.x; i < a.k; i += 64 * NW) a.sel_out[unit * a.k + i] = lsel[i];
@@ -467,40 +485,48 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       qf[cs] = as_bf16x8(v);
     }
   }
-  const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
-  const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
-  const int sub = a.S / S;                // tiles per block: 1 or 2
-
-  float m_run = -__builtin_inff(), l_run = 0.0f;
-  f32x4_t o[CT];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
+  const int sub = a.S / S;  // tiles per block: 1 or 2
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;  // self-selecting: replaced below
   // this split's selection slots, as tile positions; the wavefront's tiles
   // are positions i0, i0+NW, ...
   const int i0 = split * a.bps * sub + wave;
   const int i1 = min(split * a.bps + a.bps, a.k) * sub;
   const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
+  // the loads that need no sequence length go out before it is awaited:
+  // the unit's scores (self-selecting) or the first chunk's selection
+  // slots, and the table row
+  const bool staged = a.MB <= kTabMax;
+  SelfSelLoads<NW, SELF> sl;
+  int j0 = -2, jp0 = -1, h0 = 0;
+  if constexpr (SELF > 0) {
+    self_select_load<NW, SELF>(a, b, g, staged, sl);
+  } else {
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
+    if (staged) load_table_row<64 * NW>(a, b, g, sl.tv);
+  }
+  const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
+  const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
+
+  float m_run = -__builtin_inff(), l_run = 0.0f;
+  f32x4_t o[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k_pool);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v_pool);
 
-  // a software pipeline over the wavefront's pages: K of the next page is
-  // requested as soon as this page's scores are done, V as soon as its
+  // a software pipeline over the wavefront's tiles: K of the next tile is
+  // requested as soon as this tile's scores are done, V as soon as its
   // value product is.  Every iteration issues the same loads, so the waits
   // stay exact; after the last page the request goes to the pool's first
   // tile of this KV head, which every workgroup of the head shares and the
   // caches keep (no HBM traffic)
   // the first chunk's slots and the table row are fetched together, so the
   // table lookups need no further round trip
-  int j0, jp0, h0;
-  const bool staged = a.MB <= kTabMax;
   if constexpr (SELF > 0) {
-    srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
+    srow = self_select_finish<NW, SELF>(a, b, g, split, nb, staged, sl, trow, lsel, tk);
     fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
   } else {
-    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
-    if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+    if (staged) store_table_row<64 * NW>(a, sl.tv, trow);
     __syncthreads();
   }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
@@ -844,33 +870,39 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
       qf[cs] = as_bf16x8(v);
     }
   }
+  const int sub = a.S / S;  // tiles per block: 1 or 2
+  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
+  const int i0 = split * a.bps * sub + wave;  // tile positions, as in the bf16 kernel
+  const int i1 = min(split * a.bps + a.bps, a.k) * sub;
+  const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
+  // the loads that need no sequence length first, as in the bf16 kernel
+  const bool staged = a.MB <= kTabMax;
+  SelfSelLoads<NW, SELF> sl;
+  int j0 = -2, jp0 = -1, h0 = 0;
+  if constexpr (SELF > 0) {
+    self_select_load<NW, SELF>(a, b, g, staged, sl);
+  } else {
+    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
+    if (staged) load_table_row<64 * NW>(a, b, g, sl.tv);
+  }
   const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
   const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
-  const int sub = a.S / S;                // tiles per block: 1 or 2
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4_t o[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) o[ct] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-  const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
-  const int i0 = split * a.bps * sub + wave;  // tile positions, as in the bf16 kernel
-  const int i1 = min(split * a.bps + a.bps, a.k) * sub;
-  const int ntiles = i0 < i1 ? (i1 - i0 + NW - 1) / NW : 0;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
   float* vw = vsl[wave];
   float* kw = ksl[PG ? wave : 0];
 
   // the same two-stage page pipeline as the bf16 kernel
-  int j0, jp0, h0;
-  const bool staged = a.MB <= kTabMax;
   if constexpr (SELF > 0) {
-    srow = self_select<NW, SELF>(a, b, g, split, nb, staged, trow, lsel, tk);
+    srow = self_select_finish<NW, SELF>(a, b, g, split, nb, staged, sl, trow, lsel, tk);
     fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
   } else {
-    fetch_slots(srow, i0, i1, NW, sub, 0, j0, jp0, h0);
-    if (staged) stage_table_row<64 * NW>(a, b, g, trow);
+    if (staged) store_table_row<64 * NW>(a, sl.tv, trow);
     __syncthreads();
   }
   for (int t0 = 0; t0 < ntiles; t0 += 64) {
