@@ -366,6 +366,48 @@ def test_score_blocks_then_select_attn(env, case):
 
 
 @pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_fused_append_error_paths_leave_the_cache_alone(env, kind):
+    """kvs_score_blocks with the token append, where sequence 0's length is
+    past the table (flagged KVS_DEVERR_SEQLEN) and sequence 1's newest block
+    maps to a page past the pool (flagged KVS_DEVERR_TABLE): neither gets the
+    token, while sequence 2 is appended (K/V, summary, scales) exactly as the
+    oracle appends it and its scores are exact.  Every workgroup issues the
+    same token loads whether or not it appends, so this also runs the
+    kernel's spare-address path for all of them."""
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    base = "llama8b" if kind == "bf16" else "longfp8"
+    w = env.synth.scaled(env.synth.WORKLOADS[base], B=3, L=64 * 20, k=8, layers=1)
+    c = Cache(env, w, [64 * 20 - 9, 64 * 13 + 7, 64 * 11 + 30], seed=23, host_tier=False)
+    p, L = c.p, c.p.L
+    lens = c.lens + 1
+    c.set_lens(lens)
+    bad_lens = lens.copy()
+    bad_lens[0] = L.max_blocks * L.block_size + 5
+    p.inp["seq_lens"].copy_(torch.as_tensor(bad_lens, dtype=torch.int32))
+    j1 = int(lens[1] - 1) // L.block_size
+    tbl = p.inp["block_table"].clone()
+    p.inp["block_table"][1, j1] = L.num_pages + 1000
+    tok = c.new_token()
+    scores = torch.empty((L.num_seqs, L.num_kv_heads, L.max_blocks), dtype=torch.float64, device=env.dev)
+    kvs.kvs_score_blocks(L, p.inp["q"], c.summ, p.inp["seq_lens"], kvs.SelectOpts(), c.args(tok), scores, None)
+    torch.cuda.synchronize()
+    flags = kvs.kvs_device_errors(clear=True)
+    assert flags & kvs.KVS_DEVERR_SEQLEN and flags & kvs.KVS_DEVERR_TABLE, f"flags {flags:#x}"
+    p.inp["block_table"].copy_(tbl)
+    p.inp["seq_lens"].copy_(torch.as_tensor(lens, dtype=torch.int32))
+    # the oracle appends to sequence 2 only (a length of 0 appends nothing)
+    c.oracle_append(tok, np.asarray([0, 0, lens[2]], np.int32))
+    c.check("error paths")
+    p.h["q"] = p.inp["q"].double().cpu().numpy()
+    o_W = orc.bounds(p.OL, p.h["q"], c.o_summ, p.h["lens"])
+    nb2 = p.nbs[2]
+    gs = scores.cpu().numpy()
+    assert np.array_equal(gs[2, :, :nb2 - 1], o_W[2, :, :nb2 - 1]), "sequence 2's scores differ"
+    no_device_errors(env)
+    print(f"[fused append errors {kind}] flags {flags:#x}; sequence 2 appended, 0 and 1 untouched")
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
 def test_prefetch_pipeline_matches_oracle_and_sequential_hot_steps(env, kind):
     """Layers' swap-ins issued ahead (page-table steps two layers ahead on
     the compute stream, copies one layer ahead on a second stream while
