@@ -75,7 +75,7 @@
 extern "C" {
 #endif
 
-#define KVS_ABI_VERSION 5
+#define KVS_ABI_VERSION 6
 
 typedef enum kvs_status {
   KVS_OK = 0,
@@ -285,6 +285,35 @@ typedef struct kvs_append_args {
 
 kvs_status kvs_append_token(const kvs_layout* layout, const kvs_append_args* append,
                             const int32_t* seq_lens, void* summaries, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kvs_append_sparse_decode_attn -- kvs_append_token followed by
+ * kvs_sparse_decode_attn (paged table) over a given selection, as one call
+ *
+ * Page "KV 稀疏化", §7 "HiSparse" (the newest KV written to the device
+ * cache) and §5 "Quest" (attention over the selected blocks only), for a
+ * layer that attends over a selection made elsewhere ("SparDA…" §3.1 and
+ * §4.1: deeper layers reuse the mask of the predictor layers).  Results are
+ * those of the two calls in a row: the cache, summaries and host tier as
+ * kvs_append_token leaves them, out as kvs_sparse_decode_attn returns it on
+ * the updated cache.  With bf16 q and K/V, blocks of 32 or 64 tokens and
+ * head dim 64 or 128 both run in one launch: the attention takes the new
+ * token's K and V from the append arguments (so it does not wait for the
+ * write), and one workgroup per (sequence, KV head) writes the token after
+ * its attention work; other layouts run the append launch first.
+ *
+ *  append       as for kvs_append_token; its block_table, k_pool, v_pool,
+ *               k_scales and v_scales are also the attention's
+ *  summaries, seq_lens  as for kvs_append_token (lengths with the token)
+ *  q, sel, k, sm_scale, out, workspace  as for kvs_sparse_decode_attn
+ * Errors: as kvs_append_token and kvs_sparse_decode_attn.  Device flags:
+ * theirs (a sequence whose length or token page is out of range gets no
+ * token, and its attention is that of kvs_sparse_decode_attn).
+ * ---------------------------------------------------------------------- */
+kvs_status kvs_append_sparse_decode_attn(const kvs_layout* layout, const kvs_append_args* append,
+                                         void* summaries, const void* q, const int32_t* seq_lens,
+                                         const int32_t* sel, int32_t k, float sm_scale, float* out,
+                                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * kvs_select_topk_ex -- kvs_select_topk with the selection options of

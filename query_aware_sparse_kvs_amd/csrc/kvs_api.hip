@@ -584,7 +584,7 @@ kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, con
                      const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
                      const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
                      size_t workspace_bytes, void* stream, const double* scores, int32_t recent,
-                     bool noalloc = false);
+                     bool noalloc = false, const kvs::AppendArgs* tok = nullptr);
 }  // namespace
 
 extern "C" {
@@ -596,6 +596,19 @@ kvs_status kvs_sparse_decode_attn(const kvs_layout* L, int32_t table_kind, const
                                   void* workspace, size_t workspace_bytes, void* stream) {
   return attn_impl(L, table_kind, q, k_pool, v_pool, k_scales, v_scales, table, seq_lens, sel, k, sm_scale, out,
                    workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kvs_status kvs_append_sparse_decode_attn(const kvs_layout* L, const kvs_append_args* append, void* summaries,
+                                         const void* q, const int32_t* seq_lens, const int32_t* sel, int32_t k,
+                                         float sm_scale, float* out, void* workspace, size_t workspace_bytes,
+                                         void* stream) {
+  kvs_status st = check_layout(L, true);
+  if (st != KVS_OK) return st;
+  kvs::AppendArgs t{};
+  if ((st = make_append(L, append, seq_lens, summaries, &t)) != KVS_OK) return st;
+  return attn_impl(L, KVS_TABLE_PAGED, q, append->k_pool, append->v_pool, append->k_scales, append->v_scales,
+                   append->block_table, seq_lens, sel, k, sm_scale, out, workspace, workspace_bytes, stream, nullptr,
+                   0, false, &t);
 }
 
 kvs_status kvs_sparse_decode_attn_noalloc(const kvs_layout* L, int32_t table_kind, const void* q,
@@ -638,7 +651,7 @@ kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, con
                      const float* k_scales, const float* v_scales, const int32_t* table, const int32_t* seq_lens,
                      const int32_t* sel, int32_t k, float sm_scale, float* out, void* workspace,
                      size_t workspace_bytes, void* stream, const double* scores, int32_t recent,
-                     bool noalloc) {
+                     bool noalloc, const kvs::AppendArgs* tok) {
   // noalloc: the split partials go to the library's scratch array instead
   // of a caller's workspace (workspace and workspace_bytes are ignored)
   kvs_status st = check_layout(L, true);
@@ -722,6 +735,15 @@ kvs_status attn_impl(const kvs_layout* L, int32_t table_kind, const void* q, con
       hipError_t e = kvs::launch_topk(ta, s);
       if (e != hipSuccess) return hip_status(e, "top-k launch");
     }
+  }
+  if (tok) {  // the token append first: in the same launch where the kernel allows, else its own
+    kvs::AppendArgs t = *tok;
+    t.err = err;
+    if (kvs::attn_tok_supported(kind_of(L->q_dtype), kind_of(L->kv_dtype), L->block_size, L->head_dim, a.hot))
+      return hip_status(kvs::launch_attn_tok(a, t, kind_of(L->q_dtype), kind_of(L->kv_dtype), s),
+                        "append + attention launch");
+    hipError_t e = kvs::launch_append(t, kind_of(L->kv_dtype), s);
+    if (e != hipSuccess) return hip_status(e, "append launch");
   }
   return hip_status(kvs::launch_attn(a, kind_of(L->q_dtype), kind_of(L->kv_dtype), s), "attention launch");
 }

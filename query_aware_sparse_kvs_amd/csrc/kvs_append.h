@@ -153,11 +153,15 @@ __device__ __forceinline__ TokenBlock load_token_block(const AppendArgs& a, int 
 }
 
 // Every thread of the NT-thread workgroup calls it (D <= NT), with len in
-// [1, MB*S]; all exits are uniform over the workgroup.
-template <int KVK, int D, int NT>
+// [1, MB*S]; all exits are uniform over the workgroup.  COHERENT_SEAL: the
+// workgroup may have read the block's tiles before (through its L1, which
+// does not see its own later stores), so the seal reads them back from the
+// device-coherent level after a device-scope fence.
+template <int KVK, int D, int NT, bool COHERENT_SEAL = false>
 __device__ __forceinline__ void store_token(const AppendArgs& a, int b, int g, int len, const TokenIn& in,
                                             const TokenBlock& blk) {
   static_assert(D <= NT, "one thread per channel");
+  static_assert(!COHERENT_SEAL || KVK != K_FP8, "the coherent seal copies the K/V tiles only");
   using E = typename ElemT<KVK>::T;
   constexpr int EB = elem_bytes<KVK>();
   const int tid = threadIdx.x;
@@ -228,11 +232,27 @@ __device__ __forceinline__ void store_token(const AppendArgs& a, int b, int g, i
   u32x4* dk = reinterpret_cast<u32x4*>(static_cast<char*>(a.host_k) + host_tile * tile_bytes);
   u32x4* dv = reinterpret_cast<u32x4*>(static_cast<char*>(a.host_v) + host_tile * tile_bytes);
   const int nvec = (int)(tile_bytes / 16);
-  for (int i = tid; i < nvec; i += NT) {
-    const u32x4 x = sk[i];
-    const u32x4 y = sv[i];
-    dk[i] = x;
-    dv[i] = y;
+  if constexpr (COHERENT_SEAL) {
+    __threadfence();
+    for (int i = tid; i < nvec; i += NT) {
+      u32x4 x, y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(sk + i) + e, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+        y[e] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(sv + i) + e, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+      }
+      dk[i] = x;
+      dv[i] = y;
+    }
+  } else {
+    for (int i = tid; i < nvec; i += NT) {
+      const u32x4 x = sk[i];
+      const u32x4 y = sv[i];
+      dk[i] = x;
+      dv[i] = y;
+    }
   }
   if constexpr (KVK == K_FP8) {
     const long long ns = (long long)S * groups;

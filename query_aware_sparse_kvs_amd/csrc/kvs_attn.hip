@@ -43,6 +43,7 @@
 // selected block.
 #include <type_traits>
 
+#include "kvs_append.h"
 #include "kvs_internal.h"
 #include "kvs_topk.h"
 
@@ -454,8 +455,15 @@ __device__ __forceinline__ void wg_merge_write(const AttnArgs& a, int b, int g, 
 
 // S: tokens per tile (kAttnTile); the cache's blocks hold a.S = S or 2S
 // tokens, and a block of 2S tokens is streamed as its two tiles.
-template <int D, int S, int NW, int SELF>
-__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
+// The bf16 kernel's body.  TOK: the decode token is appended in the same
+// launch (attn_mfma_tok_kernel, given selection, paged table): for the one
+// tile that holds token len-1 its K row and V column come from the append
+// arguments, whatever the pool still holds there, and each unit's first
+// split workgroup writes the token into the cache (with its block's summary
+// and the seal of a block it fills) after its own attention work.
+template <int D, int S, int NW, int SELF, int TOK>
+__device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, const AppendArgs* ta) {
+  static_assert(!TOK || (SELF == 0 && S == 32), "the token path streams 32-token tiles of a given selection");
   constexpr int CS = D / 32;  // k-steps of the score product
   constexpr int CT = D / 16;  // 16-channel tiles of the value product
   constexpr int NSUB = S / 32;  // 32-token sub-tiles per tile
@@ -466,6 +474,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   __shared__ int trow[kTabMax];
   __shared__ int32_t lsel[SELF > 0 ? kSelfSelMax : 1];
   __shared__ TopkLds tk;
+  __shared__ int wl_tok[TOK ? NW : 1][TOK ? 64 : 1];  // the token's row in the tile, or -1
 
   int split, g, b;
   xcd_unit(split, g, b);
@@ -484,6 +493,21 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       if (r < G) v = *reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4);
       qf[cs] = as_bf16x8(v);
     }
+  }
+  // the token's K (this lane's 8 channels of every k-step) and V (channel
+  // ct*16 + r of every channel tile), and the first split's append inputs
+  u32x4 kn[TOK ? CS : 1];
+  uint32_t vn[TOK ? CT : 1];
+  TokenIn tin{0u, 0u, 1.0f, 0};
+  if constexpr (TOK) {
+    const long long unit = (long long)b * a.Hkv + g;
+    const uint16_t* kb = static_cast<const uint16_t*>(ta->k_new) + unit * D;
+    const uint16_t* vb = static_cast<const uint16_t*>(ta->v_new) + unit * D;
+#pragma unroll
+    for (int cs = 0; cs < CS; ++cs) kn[cs] = *reinterpret_cast<const u32x4*>(kb + cs * 32 + 8 * j4);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) vn[ct] = vb[ct * 16 + r];
+    tin = load_token_in<K_BF16, D, true>(*ta, b, g, split == 0, a.seq_lens);
   }
   const int sub = a.S / S;  // tiles per block: 1 or 2
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;  // self-selecting: replaced below
@@ -506,6 +530,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   }
   const int len = clamp_len(a, b, tid == 0 && split == 0 && g == 0);
   const int nb = (len + a.S - 1) / a.S;  // blocks of the cache (a.S = S or 2S tokens)
+  // the token: position len-1 (none for an empty sequence; a length past
+  // the table was flagged and clamped, and appends nothing)
+  const int raw_len = TOK ? ld_uniform(a.seq_lens + b) : 0;
+  const bool tok_ok = TOK && raw_len >= 1 && raw_len <= a.MB * a.S;
+  const int tok_t = tok_ok ? raw_len - 1 : -1;
+  const int tok_j = tok_ok ? tok_t / a.S : -3, tok_half = tok_ok ? (tok_t % a.S) / S : 0;
+  const int tok_row = tok_ok ? tok_t % S : -1;
+  TokenBlock tblk{0, 0u, 0u};
+  if constexpr (TOK) tblk = load_token_block<K_BF16, D, true, true>(*ta, b, g, raw_len, tok_ok && split == 0, a.seq_lens);
 
   float m_run = -__builtin_inff(), l_run = 0.0f;
   f32x4_t o[CT];
@@ -532,6 +565,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
   for (int t0 = 0; t0 < ntiles; t0 += 64) {  // chunks of 64 tiles
     int j = j0, jp = jp0, hf = h0;
     if (t0 > 0) fetch_slots(srow, i0, i1, NW, sub, t0, j, jp, hf);
+    if constexpr (TOK) wl_tok[wave][lane] = j == tok_j && hf == tok_half ? tok_row : -1;  // (ordered by resolve)
     resolve_tiles(a, staged ? trow : nullptr, j, jp, hf, b, g, nb, len, S, sub, wl_tile[wave], wl_ntok[wave]);
     const int nt = min(64, ntiles - t0);
     PageK<D, S> K;
@@ -545,14 +579,47 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) 
       const int ntok = __builtin_amdgcn_readfirstlane(wl_ntok[wave][tt]);
       const long long tnext = uniform64(tt + 1 < nt ? wl_tile[wave][tt + 1] : (a.hot ? 0 : (long long)g * sub));
       bf16x8_t ph[NSUB], pl[NSUB];
+      int trw = -1;
+      if constexpr (TOK) trw = __builtin_amdgcn_readfirstlane(wl_tok[wave][tt]);
+      if (TOK && trw >= 0) {  // uniform: this tile holds the token; its K row from the arguments
+#pragma unroll
+        for (int tg = 0; tg < 2; ++tg)
+          if (8 * (r >> 2) + 4 * tg + (r & 3) == trw)
+#pragma unroll
+            for (int cs = 0; cs < CS; ++cs) K.r[0][tg][cs] = kn[cs];
+      }
       page_scores<D, S>(K, qf, a.q_scale, ntok, j4, m_run, l_run, o, ph, pl);
       load_page_k<D, S>(kpool + tnext * S * D, r, j4, K);
+      if (TOK && trw >= 0 && (trw >> 3) == j4) {  // and its V column: element trw % 8 of this lane's run
+        const int w = (trw & 7) >> 1;
+        const bool hi = trw & 1;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+          V.r[0][ct][w] = hi ? (V.r[0][ct][w] & 0x0000FFFFu) | (vn[ct] << 16) : (V.r[0][ct][w] & 0xFFFF0000u) | vn[ct];
+      }
       page_values<D, S>(V, ntok, j4, ph, pl, o);
       load_page_v<D, S>(vpool + tnext * D * S, r, j4, V);
     }
   }
 
   wg_merge_write<D, NW>(a, b, g, split, wave, r, j4, m_run, l_run, o, mg_m, mg_l, mg_o);
+  if constexpr (TOK) {
+    // the unit's first split writes the token (this workgroup may have read
+    // the token's tile: the seal reads it back past the L1)
+    if (split == 0 && tok_ok) store_token<K_BF16, D, 64 * NW, true>(*ta, b, g, raw_len, tin, tblk);
+  }
+}
+
+template <int D, int S, int NW, int SELF>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_kernel(AttnArgs a) {
+  attn_mfma_body<D, S, NW, SELF, 0>(a, nullptr);
+}
+
+// attention over a given selection with the decode token appended in the
+// same launch (bf16 K/V, paged table)
+template <int D, int S, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma_tok_kernel(AttnArgs a, AppendArgs t) {
+  attn_mfma_body<D, S, NW, 0, 1>(a, &t);
 }
 
 // ---------------------------------------------------------------------------
@@ -1392,6 +1459,30 @@ bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k) {
   // selection prologue
   return q_kind == K_BF16 && (kv_kind == K_BF16 || kv_kind == K_FP8) && S >= 32 && MB <= kSelfSelMax &&
          k <= kSelfSelMax;
+}
+
+bool attn_tok_supported(int q_kind, int kv_kind, int S, int D, int hot) {
+  return q_kind == K_BF16 && kv_kind == K_BF16 && S >= 32 && (D == 64 || D == 128) && !hot;
+}
+
+hipError_t launch_attn_tok(const AttnArgs& a, const AppendArgs& t, int q_kind, int kv_kind, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  if (a.nsplit < 1 || a.nsplit > kMaxSplits || a.W || !attn_tok_supported(q_kind, kv_kind, a.S, a.D, a.hot))
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)a.nsplit, (unsigned)a.Hkv, (unsigned)a.B);
+  if (a.D == 64)
+    hipLaunchKernelGGL((attn_mfma_tok_kernel<64, kAttnTile, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a, t);
+  else
+    hipLaunchKernelGGL((attn_mfma_tok_kernel<128, kAttnTile, kAttnWaves>), grid, dim3(64 * kAttnWaves), 0, st, a, t);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.nsplit == 1) return e;
+  const long long threads = (long long)a.B * a.Hq * (a.D / 4);
+  const dim3 mgrid((unsigned)((threads + kMergeThreads - 1) / kMergeThreads));
+  if (a.D == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, mgrid, dim3(kMergeThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(merge_kernel<128>, mgrid, dim3(kMergeThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t st) {

@@ -259,6 +259,10 @@ hipError_t launch_select_mfma(const SelMfmaArgs& a, int summ_kind, hipStream_t s
 hipError_t launch_attn(const AttnArgs& a, int q_kind, int kv_kind, hipStream_t s);
 // whether launch_attn can run this shape in self-selecting mode
 bool attn_self_select_supported(int q_kind, int kv_kind, int S, int MB, int k);
+// attention over a given selection with the decode token appended in the
+// same launch (bf16 K/V, blocks of 32 or 64 tokens, paged table)
+bool attn_tok_supported(int q_kind, int kv_kind, int S, int D, int hot);
+hipError_t launch_attn_tok(const AttnArgs& a, const AppendArgs& t, int q_kind, int kv_kind, hipStream_t s);
 // hot-buffer phases: the page-table step (hits, miss list, LRU victims) and
 // the copy of the listed misses from the host tier
 constexpr int kHotLookup = 1, kHotCopy = 2;

@@ -152,6 +152,8 @@ def _load():
         "kvs_sparse_decode_attn": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, sz, P]),
         "kvs_sparse_decode_attn_noalloc": (i32, [LP, i32, P, P, P, P, P, P, P, P, i32, ctypes.c_float, P, P]),
         "kvs_append_token": (i32, [LP, ctypes.POINTER(_CAppendArgs), P, P, P]),
+        "kvs_append_sparse_decode_attn": (i32, [LP, ctypes.POINTER(_CAppendArgs), P, P, P, P, i32, ctypes.c_float,
+                                                P, P, sz, P]),
         "kvs_score_blocks": (i32, [LP, P, P, P, ctypes.POINTER(_CSelectOpts), ctypes.POINTER(_CAppendArgs),
                                    P, P, P]),
         "kvs_select_attn": (i32, [LP, P, P, P, P, P, P, P, P, i32, i32, P, ctypes.c_float, P, P, sz, P]),
@@ -178,7 +180,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("kvs_build_summaries", "kvs_select_topk", "kvs_select_topk_append", "kvs_sparse_decode_attn",
             "kvs_sparse_decode_attn_noalloc", "kvs_hot_lookup_swapin", "kvs_hot_lookup", "kvs_hot_swapin",
-            "kvs_append_token", "kvs_select_topk_ex", "kvs_score_blocks", "kvs_select_attn",
+            "kvs_append_token", "kvs_append_sparse_decode_attn", "kvs_select_topk_ex", "kvs_score_blocks",
+            "kvs_select_attn",
             "kvs_build_summaries_ex", "kvs_select_uses_matrix_cores",
             "kvs_select_workspace_size", "kvs_attn_workspace_size", "kvs_attn_num_splits",
             "kvs_device_errors", "kvs_status_string", "kvs_last_error", "kvs_abi_version")
@@ -346,6 +349,22 @@ def kvs_append_token(layout: Layout, append: AppendArgs, seq_lens, summaries, st
         _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
         _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
         _stream(stream)), "kvs_append_token")
+
+
+def kvs_append_sparse_decode_attn(layout: Layout, append: AppendArgs, summaries, q, seq_lens, sel, k: int,
+                                  sm_scale: float, out, workspace, stream=None) -> None:
+    L = layout
+    ca = _append_struct(L, append)
+    _check(_lib.kvs_append_sparse_decode_attn(
+        ctypes.byref(L.c()), ctypes.byref(ca),
+        _ptr(summaries, "summaries", L.summary_dtype, L.num_seqs * L.num_kv_heads * L.max_blocks * 2 * L.head_dim),
+        _ptr(q, "q", _TORCH_OF[L.q_dtype], L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(seq_lens, "seq_lens", torch.int32, L.num_seqs),
+        _ptr(sel, "sel", torch.int32, L.num_seqs * L.num_kv_heads * k),
+        k, float(sm_scale),
+        _ptr(out, "out", torch.float32, L.num_seqs * L.num_q_heads * L.head_dim),
+        _ptr(workspace, "workspace", torch.uint8), workspace.numel() if workspace is not None else 0,
+        _stream(stream)), "kvs_append_sparse_decode_attn")
 
 
 def kvs_select_topk_ex(layout: Layout, q, summaries, seq_lens, k: int, opts: SelectOpts | None,

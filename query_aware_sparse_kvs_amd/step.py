@@ -286,10 +286,10 @@ class CrossLayerDecode:
     scores to the fused score (kvs_score_blocks with accumulate for l > 0,
     so the fused score is the sum over layers 0..l, added in layer order)
     and attends over the top-k of that sum (kvs_select_attn).  Every deeper
-    layer appends its token (kvs_append_token: its K/V written, its
-    summary kept current) and attends over the last predictor layer's
-    selection (kvs_sparse_decode_attn): it reads no summaries and scores
-    nothing.  Block ids are logical positions, so each layer gathers its own
+    layer appends its token (its K/V written, its summary kept current) and
+    attends over the last predictor layer's selection, in one call
+    (kvs_append_sparse_decode_attn: one launch for bf16 K/V): it reads no
+    summaries and scores nothing.  Block ids are logical positions, so each layer gathers its own
     pages through its own block table.  All layers share seq_lens."""
 
     def __init__(self, layout: kvs.Layout, k: int, num_layers: int, predictor_layers: int, device="cuda"):
@@ -317,10 +317,8 @@ class CrossLayerDecode:
                                 seq_lens, self.fused, k, 1, self.sel, self.sm_scale, self.out[l], self.attn_ws,
                                 stream)
         else:
-            kvs.kvs_append_token(L, tok, seq_lens, summaries, stream)
-            kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, q, tok.k_pool, tok.v_pool, tok.k_scales,
-                                       tok.v_scales, tok.block_table, seq_lens, self.sel, k, self.sm_scale,
-                                       self.out[l], self.attn_ws, stream)
+            kvs.kvs_append_sparse_decode_attn(L, tok, summaries, q, seq_lens, self.sel, k, self.sm_scale,
+                                              self.out[l], self.attn_ws, stream)
         return self.out[l]
 
     def run(self, qs, toks, seq_lens, summaries, stream=None) -> torch.Tensor:

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(kvs):
 
 
 def test_abi_version_and_status_strings(kvs):
-    assert kvs.kvs_abi_version() == 5
+    assert kvs.kvs_abi_version() == 6
     for st in range(5):
         assert kvs.kvs_status_string(st).startswith("KVS_")
     assert "unknown" in kvs.kvs_status_string(99)

@@ -158,6 +158,79 @@ def test_append_token_steps_match_oracle(env, case):
     assert sealed > 0
 
 
+FUSED_CASES = [
+    # (name, workload, overrides, first lengths, steps, k); k 2 gives one split
+    ("bf16-s64-d128", "llama8b", {"B": 3, "L": 64 * 8, "layers": 1}, [64 * 3 - 5, 64 * 5 + 3, 1], 70, 6),
+    ("bf16-s64-one-split", "llama8b", {"B": 2, "L": 64 * 6, "layers": 1}, [64 * 2 - 2, 64 + 40], 68, 2),
+    ("bf16-s32-d64", "llama8b", {"B": 2, "L": 32 * 10, "S": 32, "D": 64, "Hq": 16, "layers": 1}, [40, 32 * 3], 36,
+     5),
+    ("fp8-two-launches", "longfp8", {"B": 2, "L": 64 * 5}, [64 * 2 - 3, 64], 67, 4),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_append_attn_in_one_call_matches_two_calls_and_oracle(env, case):
+    """kvs_append_sparse_decode_attn over many decode steps (blocks filled and
+    sealed on the way) against kvs_append_token + kvs_sparse_decode_attn on
+    a second copy of the cache: outputs, pools, summaries and host tiers
+    bit-identical at every step; and against the oracle (cache bit-exact,
+    attention within the bars).  bf16 runs as one launch (the token's tile
+    takes its K row and V column from the arguments, the unit's first split
+    workgroup writes it after its attention); fp8 takes the two launches."""
+    from test_gpu_parity import check_attn
+    name, base, over, lens0, steps, k = case
+    torch, kvs, orc = env.torch, env.kvs, env.orc
+    w = env.synth.scaled(env.synth.WORKLOADS[base], **over, k=k)
+    c1 = Cache(env, w, lens0, seed=31)
+    c2 = Cache(env, w, lens0, seed=31)
+    L = c1.p.L
+    print(f"[append+attn {name}] B={w.B} D={w.D} S={w.S} k={k} splits={kvs.kvs_attn_num_splits(L, k)} "
+          f"steps={steps} {w.kv_dtype}", flush=True)
+    ws1 = torch.zeros(kvs.kvs_attn_workspace_size(L, k), dtype=torch.uint8, device=env.dev)
+    ws2 = torch.zeros_like(ws1)
+    lens = np.asarray(lens0, np.int64)
+    worst = 0.0
+    for step in range(steps):
+        lens = lens + 1
+        c1.set_lens(lens)
+        c2.set_lens(lens)
+        tok = c1.new_token()
+        c2.new_token()  # keeps the two generators in step
+        sel_np = env.synth.random_selection(w, lens, k, seed=step)
+        sel = torch.from_numpy(sel_np).to(env.dev)
+        o1 = torch.full((L.num_seqs, L.num_q_heads, L.head_dim), float("nan"), device=env.dev)
+        o2 = torch.full_like(o1, float("nan"))
+        p1, p2 = c1.p, c2.p
+        kvs.kvs_append_sparse_decode_attn(L, c1.args(tok), c1.summ, p1.inp["q"], p1.inp["seq_lens"], sel, k,
+                                          p1.sm_scale, o1, ws1)
+        kvs.kvs_append_token(L, c2.args(tok), p2.inp["seq_lens"], c2.summ)
+        kvs.kvs_sparse_decode_attn(L, kvs.KVS_TABLE_PAGED, p2.inp["q"], p2.inp["k_pool"], p2.inp["v_pool"],
+                                   p2.inp["k_scales"], p2.inp["v_scales"], p2.inp["block_table"],
+                                   p2.inp["seq_lens"], sel, k, p2.sm_scale, o2, ws2)
+        torch.cuda.synchronize()
+        no_device_errors(env)
+        def same(x, y):  # bit for bit (unbuilt summaries hold NaN)
+            return torch.equal(x.contiguous().view(torch.uint8), y.contiguous().view(torch.uint8))
+        assert same(o1, o2), f"step {step}: outputs differ"
+        for n in ("k_pool", "v_pool", "k_scales", "v_scales"):
+            if p1.inp[n] is not None:
+                assert same(p1.inp[n], p2.inp[n]), f"step {step}: {n} differs"
+        assert same(c1.summ, c2.summ), f"step {step}: summaries differ"
+        for n in c1.host:
+            assert same(c1.host[n], c2.host[n]), f"step {step}: {n} differs"
+        c1.oracle_append(tok, lens.astype(np.int32))
+        if step % 11 == 10 or step == steps - 1:
+            c1.check(f"step {step}")
+            o_out = orc.sparse_attn(p1.OL, p1.inp["q"].double().cpu().numpy(), c1.o["k_pool"], c1.o["v_pool"],
+                                    c1.o["k_scales"], c1.o["v_scales"], p1.h["table"], p1.h["lens"], sel_np,
+                                    p1.sm_scale)
+            err, _ = check_attn(o1, o_out)
+            worst = max(worst, err)
+    sealed = sum(int(n) // w.S - int(m) // w.S for n, m in zip(lens, lens0))
+    print(f"[append+attn {name}] {steps} steps, {sealed} blocks sealed, attention max|err| {worst:.2e}")
+    assert sealed > 0
+
+
 def _drift_q(env, q, rng):
     """Next step's query: a bf16 random walk that keeps most of the last one."""
     torch = env.torch
