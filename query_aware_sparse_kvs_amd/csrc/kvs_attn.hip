@@ -486,13 +486,13 @@ __device__ __forceinline__ void attn_mfma_body(const AttnArgs& a, const AppendAr
   // B operand of the score product: Q^T, column r = query head g*G + r
   bf16x8_t qf[CS];
   {
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + r) * D;
+    // columns past the group repeat its last head (their results are never
+    // written): the loads are unconditional, so no wait for them is placed
+    // before the loads that follow
+    const int rq = min(r, G - 1);
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + rq) * D;
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < G) v = *reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4);
-      qf[cs] = as_bf16x8(v);
-    }
+    for (int cs = 0; cs < CS; ++cs) qf[cs] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4));
   }
   // the token's K (this lane's 8 channels of every k-step) and V (channel
   // ct*16 + r of every channel tile), and the first split's append inputs
@@ -929,13 +929,10 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void attn_mfma8_kernel(AttnArgs a)
 
   bf16x8_t qf[CS];  // B operand of the score product: Q^T, column r = query head g*G + r
   {
-    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + r) * D;
+    const int rq = min(r, G - 1);  // (columns past the group repeat its last head, as in the bf16 kernel)
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + ((long long)b * a.Hq + (long long)g * G + rq) * D;
 #pragma unroll
-    for (int cs = 0; cs < CS; ++cs) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (r < G) v = *reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4);
-      qf[cs] = as_bf16x8(v);
-    }
+    for (int cs = 0; cs < CS; ++cs) qf[cs] = as_bf16x8(*reinterpret_cast<const uint4*>(qb + cs * 32 + 8 * j4));
   }
   const int sub = a.S / S;  // tiles per block: 1 or 2
   const int32_t* srow = a.sel + ((long long)b * a.Hkv + g) * a.k;
